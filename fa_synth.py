@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for exact attention, shared by tests and bench.
+
+This module holds no attention arithmetic: it only draws Gaussian tensors from
+a seeded CPU generator, scales them by a standard deviation and rounds them to
+the storage dtype (round-to-nearest-even, torch's ``.to``).  Both the fp64
+oracle and the HIP path read the very same rounded tensors, so input rounding
+never enters a parity error.
+
+The workloads follow the problem statement the pages share: Q, K, V of shape
+[B, H, N, d] with a scale on QK^T and an optional causal mask.  The pages
+measure on synthetic data with no stated distribution; i.i.d. Gaussians are
+the plainest reading.  Draw order is fixed: Q, K, V, then dO.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    seed: int
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    passes: tuple = field(default=("fwd",))
+    naive: bool = False
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B} H={self.H} N={self.N} d={self.d} {self.dtype} "
+                f"{'causal' if self.causal else 'non-causal'} scale={self.scale:.6g} seed={self.seed}")
+
+
+def _c2(n: int) -> Workload:
+    return Workload(f"noncausal_fwd_sweep_N{n}_B4_H8_d64_f16", 4, 8, n, 64, "f16", False, 1 / 8,
+                    1002 + n, naive=True)
+
+
+# Single head, non-causal, fp32 (the size the T4 lesson sweeps start from).
+SINGLE_HEAD_F32 = Workload("single_head_fwd_N512_d64_f32", 1, 1, 512, 64, "f32", False, 1 / 8, 1001)
+# Non-causal fp16 sweep with the naive baseline beside it.
+NONCAUSAL_SWEEP = tuple(_c2(n) for n in (512, 1024, 2048, 4096))
+# Causal prefill, wide heads.
+CAUSAL_PREFILL = Workload("causal_prefill_fwd_B2_H32_N8192_d128_bf16", 2, 32, 8192, 128, "bf16", True,
+                          1 / math.sqrt(128), 1003)
+# Long causal sequence with wide logits, naive baseline beside it.
+LONG_CAUSAL = Workload("long_causal_fwd_B1_H16_N16384_d64_bf16", 1, 16, 16384, 64, "bf16", True, 1 / 8,
+                       1004, sigma_qk=2.0, naive=True)
+# Causal training step: forward and backward.
+TRAIN_STEP = Workload("causal_train_step_B4_H16_N4096_d128_bf16", 4, 16, 4096, 128, "bf16", True,
+                      1 / math.sqrt(128), 1005, passes=("fwd", "bwd"))
+
+ALL_WORKLOADS = (SINGLE_HEAD_F32,) + NONCAUSAL_SWEEP + (CAUSAL_PREFILL, LONG_CAUSAL, TRAIN_STEP)
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, sigma_qk: float = 1.0,
+                sigma_v: float = 1.0, with_dout: bool = False):
+    """Q, K, V (and dO) as CPU tensors of ``dtype`` and shape [B,H,N,d].
+
+    Q and K are N(0, sigma_qk^2), V and dO are N(0, sigma_v^2) and N(0, 1).
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (B, H, N, d)
+
+    def draw(sigma):
+        t = torch.randn(*shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            t = t * sigma
+        return t.to(DTYPES[dtype])
+
+    q = draw(sigma_qk)
+    k = draw(sigma_qk)
+    v = draw(sigma_v)
+    if not with_dout:
+        return q, k, v
+    return q, k, v, draw(1.0)
+
+
+def workload_inputs(w: Workload, with_dout: bool | None = None):
+    if with_dout is None:
+        with_dout = "bwd" in w.passes
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.sigma_qk, w.sigma_v, with_dout)
+
+
+def to_f64(t):
+    """Exact upcast of a (rounded) CPU tensor to a float64 NumPy array."""
+    return t.to(torch.float64).numpy()

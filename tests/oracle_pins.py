@@ -1,0 +1,246 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes the implementation under test as an argument and raises
+AssertionError when it disagrees with something *other* than itself: a closed
+form, an invariant, calculus (finite differences), brute-force sums, or an
+independent library routine (torch's float64 scaled_dot_product_attention and
+autograd, scipy's logsumexp).  ``tests/test_oracle.py`` runs them on the
+oracle; ``tests/test_oracle_mutants.py`` runs them on copies of the oracle
+with planted mistakes and requires that every mistake fails at least one pin.
+
+Page tags: [essay] "Flash Attention: IO-awareness principle" (hrletsgo.me);
+[triton] "Triton 06: Flash Attention v2" (wonbeomjang.kr); [review] "Paper
+review: FlashAttention ... with IO-Awareness" (osehyeon.github.io).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+RNG = np.random.default_rng
+
+
+def rand(shape, seed, sigma=1.0):
+    return RNG(seed).standard_normal(shape) * sigma
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------------------
+# forward pins
+# ----------------------------------------------------------------------------
+
+def pin_rows_are_distributions(fwd):
+    """With V = I (d = N) the output is P itself: every row sums to 1, is
+    non-negative, and is zero above the diagonal when causal ([review] the
+    softmax definition under 'Tiling')."""
+    for causal in (False, True):
+        for n in (1, 5, 12):
+            q = rand((1, 2, n, n), 1 + n)
+            k = rand((1, 2, n, n), 2 + n)
+            v = np.broadcast_to(np.eye(n), (1, 2, n, n)).copy()
+            o, _ = fwd(q, k, v, 0.7, causal)
+            _close(o.sum(-1), 1.0, 1e-12, "row sums")
+            assert np.all(o >= 0), "negative probability"
+            if causal:
+                _close(np.triu(o[0, 0], 1), 0.0, 0.0, "future keys")
+                _close(np.triu(o[0, 1], 1), 0.0, 0.0, "future keys")
+
+
+def pin_constant_v(fwd):
+    """Every V row equal to c gives O_i = c (a convex combination of equal rows)."""
+    for causal in (False, True):
+        q = rand((2, 2, 9, 4), 11)
+        k = rand((2, 2, 9, 4), 12)
+        c = np.array([0.5, -1.25, 3.0, 7.0])
+        v = np.broadcast_to(c, (2, 2, 9, 4)).copy()
+        o, _ = fwd(q, k, v, 0.9, causal)
+        _close(o, np.broadcast_to(c, o.shape), 1e-12, "constant V")
+
+
+def pin_zero_q(fwd):
+    """Q = 0 makes every logit 0: O_i is the plain mean of the allowed V rows
+    and LSE_i = ln(#allowed keys), for any scale."""
+    n, d = 13, 5
+    v = rand((1, 3, n, d), 21)
+    k = rand((1, 3, n, d), 22)
+    q = np.zeros((1, 3, n, d))
+    o, lse = fwd(q, k, v, 2.5, False)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), 1e-12, "Q=0 mean")
+    _close(lse, math.log(n), 1e-12, "Q=0 LSE")
+    o, lse = fwd(q, k, v, 2.5, True)
+    pref = np.cumsum(v, axis=2) / np.arange(1, n + 1)[None, None, :, None]
+    _close(o, pref, 1e-12, "Q=0 causal prefix mean")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, n + 1)), lse.shape), 1e-12, "Q=0 causal LSE")
+
+
+def pin_single_key(fwd):
+    """N = 1: O = V and LSE = scale * q.k.  Causal row 0 sees only key 0:
+    O_0 = V_0 and LSE_0 = scale * q_0.k_0."""
+    q, k, v = rand((2, 1, 1, 6), 31), rand((2, 1, 1, 6), 32), rand((2, 1, 1, 6), 33)
+    o, lse = fwd(q, k, v, 0.3, False)
+    _close(o, v, 1e-12, "N=1 O")
+    _close(lse, 0.3 * np.sum(q * k, -1), 1e-12, "N=1 LSE")
+    q, k, v = rand((1, 2, 7, 6), 34), rand((1, 2, 7, 6), 35), rand((1, 2, 7, 6), 36)
+    o, lse = fwd(q, k, v, 0.3, True)
+    _close(o[:, :, 0], v[:, :, 0], 1e-12, "causal row 0 O")
+    _close(lse[:, :, 0], 0.3 * np.sum(q[:, :, 0] * k[:, :, 0], -1), 1e-12, "causal row 0 LSE")
+
+
+def pin_shift_invariance(fwd):
+    """Adding u to every key adds scale*q_i.u to every logit of row i: softmax
+    is unchanged, LSE_i grows by scale*q_i.u."""
+    for causal in (False, True):
+        q, k, v = rand((1, 2, 10, 4), 41), rand((1, 2, 10, 4), 42), rand((1, 2, 10, 4), 43)
+        u = np.array([0.3, -2.0, 1.1, 0.05])
+        o1, l1 = fwd(q, k, v, 0.8, causal)
+        o2, l2 = fwd(q, k + u, v, 0.8, causal)
+        _close(o2, o1, 1e-10, "shift O")
+        _close(l2 - l1, 0.8 * (q @ u), 1e-10, "shift LSE")
+
+
+def pin_key_permutation(fwd):
+    """Non-causal attention is a function of the *set* of (k_j, v_j) pairs."""
+    q, k, v = rand((2, 1, 11, 3), 51), rand((2, 1, 11, 3), 52), rand((2, 1, 11, 3), 53)
+    perm = RNG(54).permutation(11)
+    o1, l1 = fwd(q, k, v, 1.3, False)
+    o2, l2 = fwd(q, k[:, :, perm], v[:, :, perm], 1.3, False)
+    _close(o2, o1, 1e-12, "perm O")
+    _close(l2, l1, 1e-12, "perm LSE")
+
+
+def pin_huge_logits(fwd):
+    """Logits ~1e3 stay finite (max subtraction), and when one key dominates
+    every row by a margin of hundreds, O_i equals that key's V row."""
+    n, d = 8, 4
+    q = rand((1, 1, n, d), 61)
+    k = rand((1, 1, n, d), 62)
+    v = rand((1, 1, n, d), 63)
+    o, lse = fwd(q, k, v, 40.0, False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "huge logits overflowed"
+    # a construction with one dominant key for every row
+    q = np.ones((1, 1, n, d))
+    k = np.zeros((1, 1, n, d))
+    k[0, 0, 3] = 10.0
+    o, lse = fwd(q, k, v, 25.0, False)  # logit 1000 vs 0
+    _close(o[0, 0], np.broadcast_to(v[0, 0, 3], (n, d)), 1e-12, "dominant key")
+    _close(lse, 1000.0, 1e-12, "dominant LSE")
+
+
+def pin_bruteforce_fwd(fwd, brute):
+    """Vectorised result equals explicit-loop sums on tiny inputs."""
+    for causal in (False, True):
+        for n in (1, 3, 7):
+            q, k, v = rand((2, 2, n, 3), 71 + n), rand((2, 2, n, 3), 72 + n), rand((2, 2, n, 3), 73 + n)
+            o1, l1 = fwd(q, k, v, 0.6, causal)
+            o2, l2 = brute(q, k, v, 0.6, causal)
+            _close(o1, o2, 1e-12, "brute O")
+            _close(l1, l2, 1e-12, "brute LSE")
+
+
+def pin_torch_sdpa(fwd):
+    """Independent library: torch's float64 CPU scaled_dot_product_attention
+    (is_causal is the lower-triangular, diagonal-kept mask) and scipy's
+    logsumexp of the scaled, masked logits."""
+    for causal in (False, True):
+        for n, d in ((1, 8), (33, 16), (70, 8)):
+            q, k, v = rand((2, 3, n, d), 81), rand((2, 3, n, d), 82), rand((2, 3, n, d), 83)
+            o, lse = fwd(q, k, v, 0.25, causal)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.25)
+            _close(o, ref.numpy(), 1e-12, "SDPA O")
+            s = 0.25 * np.einsum("bhid,bhjd->bhij", q, k)
+            if causal:
+                s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+            _close(lse, logsumexp(s, axis=-1), 1e-12, "logsumexp LSE")
+
+
+def pin_rows_helper(fwd, rows_fn):
+    """The per-row helper equals the full forward at sampled rows."""
+    for causal in (False, True):
+        q, k, v = rand((2, 2, 40, 8), 91), rand((2, 2, 40, 8), 92), rand((2, 2, 40, 8), 93)
+        o, lse = fwd(q, k, v, 0.4, causal)
+        rows = [(0, 0, 0), (1, 1, 39), (0, 1, 17), (1, 0, 5)]
+        ro, rl = rows_fn(q, k, v, 0.4, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            _close(ro[n], o[b, h, i], 1e-12, "row helper O")
+            _close(rl[n], lse[b, h, i], 1e-12, "row helper LSE")
+
+
+# ----------------------------------------------------------------------------
+# backward pins
+# ----------------------------------------------------------------------------
+
+def pin_finite_differences(fwd, bwd):
+    """Central differences of L = sum(dO * O) (h = 1e-6) match the analytic
+    dQ, dK, dV to 1e-6 relative, at N <= 16, d <= 8."""
+    for causal in (False, True):
+        n, d = 6, 3
+        q, k, v, g = (rand((1, 1, n, d), s) for s in (101, 102, 103, 104))
+        dq, dk, dv, _ = bwd(q, k, v, g, 0.9, causal)
+        h = 1e-6
+        for name, x, dx in (("Q", q, dq), ("K", k, dk), ("V", v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = float(np.sum(g * fwd(q, k, v, 0.9, causal)[0]))
+                x[idx] = old - h
+                lm = float(np.sum(g * fwd(q, k, v, 0.9, causal)[0]))
+                x[idx] = old
+                fd[idx] = (lp - lm) / (2 * h)
+            scale = max(1.0, float(np.max(np.abs(dx))))
+            _close(fd / scale, dx / scale, 1e-6, f"finite differences d{name}")
+
+
+def pin_delta_identity(fwd, bwd):
+    """The Jacobian-form Delta_i = sum_k P_ik dP_ik equals rowsum(dO_i * O_i),
+    the preprocessing step of [triton] 'Backward' (because O = P V)."""
+    for causal in (False, True):
+        q, k, v, g = (rand((2, 2, 21, 5), s) for s in (111, 112, 113, 114))
+        o, _ = fwd(q, k, v, 0.7, causal)
+        _, _, _, delta = bwd(q, k, v, g, 0.7, causal)
+        _close(delta, np.sum(g * o, -1), 1e-10, "Delta identity")
+
+
+def pin_gradient_sums(bwd):
+    """sum_j dS_ij = 0 for every row gives sum_j dK_j = 0; sum_j P_ij = 1 gives
+    sum_j dV_j = sum_i dO_i."""
+    for causal in (False, True):
+        q, k, v, g = (rand((2, 2, 19, 4), s) for s in (121, 122, 123, 124))
+        _, dk, dv, _ = bwd(q, k, v, g, 1.1, causal)
+        _close(dk.sum(axis=2), 0.0, 1e-9, "sum dK")
+        _close(dv.sum(axis=2), g.sum(axis=2), 1e-9, "sum dV")
+
+
+def pin_torch_autograd(bwd):
+    """Independent library: torch float64 autograd through SDPA."""
+    for causal in (False, True):
+        n, d = 37, 8
+        q, k, v, g = (rand((2, 2, n, d), s) for s in (131, 132, 133, 134))
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.35)
+        out.backward(torch.from_numpy(g))
+        dq, dk, dv, _ = bwd(q, k, v, g, 0.35, causal)
+        _close(dq, tq.grad.numpy(), 1e-11, "autograd dQ")
+        _close(dk, tk.grad.numpy(), 1e-11, "autograd dK")
+        _close(dv, tv.grad.numpy(), 1e-11, "autograd dV")
+
+
+def pin_bruteforce_bwd(bwd, brute):
+    for causal in (False, True):
+        q, k, v, g = (rand((1, 2, 5, 3), s) for s in (141, 142, 143, 144))
+        a = bwd(q, k, v, g, 0.8, causal)[:3]
+        b = brute(q, k, v, g, 0.8, causal)
+        for x, y, nm in zip(a, b, ("dQ", "dK", "dV")):
+            _close(x, y, 1e-12, f"brute {nm}")
+
+
+FWD_PINS = (pin_rows_are_distributions, pin_constant_v, pin_zero_q, pin_single_key,
+            pin_shift_invariance, pin_key_permutation, pin_huge_logits, pin_torch_sdpa)

@@ -1,0 +1,165 @@
+"""The fp64 oracle against its pins (CPU only).
+
+Page tags: [triton] "Triton 06: Flash Attention v2" (wonbeomjang.kr);
+[review] "Paper review: FlashAttention ... with IO-Awareness"
+(osehyeon.github.io); [essay] "Flash Attention: IO-awareness principle"
+(hrletsgo.me).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+from tests import oracle_pins as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("pin", P.FWD_PINS, ids=lambda f: f.__name__)
+def test_forward_pins(pin):
+    pin(oracle.attn_fwd)
+
+
+def test_forward_matches_bruteforce():
+    P.pin_bruteforce_fwd(oracle.attn_fwd, oracle.attn_fwd_bruteforce)
+
+
+def test_row_helper():
+    P.pin_rows_helper(oracle.attn_fwd, oracle.attn_fwd_rows)
+
+
+def test_row_chunking_is_invisible(monkeypatch):
+    """Row chunks of the oracle (a memory bound only) do not change results."""
+    q, k, v, g = (P.rand((1, 2, 45, 4), s) for s in (1, 2, 3, 4))
+    ref = oracle.attn_fwd(q, k, v, 0.5, True)
+    refb = oracle.attn_bwd(q, k, v, g, 0.5, True)
+    monkeypatch.setattr(A, "ROW_CHUNK", 7)
+    got = oracle.attn_fwd(q, k, v, 0.5, True)
+    gotb = oracle.attn_bwd(q, k, v, g, 0.5, True)
+    for a, b in zip(ref + refb, got + gotb):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_finite_differences():
+    P.pin_finite_differences(oracle.attn_fwd, oracle.attn_bwd)
+
+
+def test_delta_identity():
+    P.pin_delta_identity(oracle.attn_fwd, oracle.attn_bwd)
+
+
+def test_gradient_sums():
+    P.pin_gradient_sums(oracle.attn_bwd)
+
+
+def test_torch_autograd():
+    P.pin_torch_autograd(oracle.attn_bwd)
+
+
+def test_backward_matches_bruteforce():
+    P.pin_bruteforce_bwd(oracle.attn_bwd, oracle.attn_bwd_bruteforce)
+
+
+# ---------------------------------------------------------------------------
+# tiled models of the algorithm: equal to the definition (decomposition
+# identity of [review] 'Tiling'; online update of [essay] 'Tiling')
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 33])
+def test_online_models_equal_definition(n, causal):
+    q, k, v = (P.rand((1, 2, n, 4), 200 + n + s) for s in range(3))
+    o, lse = oracle.attn_fwd(q, k, v, 0.45, causal)
+    for bm in (1, 2, 5, 8):
+        for bn in (1, 2, 5, 8):
+            o1, l1 = oracle.online_fa1(q, k, v, 0.45, causal, bm, bn)
+            o2, l2 = oracle.online_fa2(q, k, v, 0.45, causal, bm, bn)
+            np.testing.assert_allclose(o1, o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l1, lse, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l2, lse, rtol=0, atol=1e-12)
+
+
+def test_online_fa2_stage_plan_and_trace():
+    """Causal FA2 visits stage-1 blocks, then the diagonal block(s), and never a
+    block entirely in the future; l starts at 1 yet ends as the true sum."""
+    n, bm, bn = 40, 8, 4
+    q, k, v = (P.rand((1, 1, n, 3), 300 + s) for s in range(3))
+    tr = []
+    oracle.online_fa2(q, k, v, 1.0, True, bm, bn, trace=tr)
+    for i in range(-(-n // bm)):
+        visited = [(j, st) for (ii, j, st, _, _) in tr if ii == i]
+        assert [j for j, _ in visited] == list(range(len(visited)))
+        for j, st in visited:
+            assert j * bn <= min(n, (i + 1) * bm) - 1  # no future block
+            assert st == (1 if (j + 1) * bn <= i * bm else 2)
+    # non-causal runs every block as stage 3
+    tr = []
+    oracle.online_fa2(q, k, v, 1.0, False, bm, bn, trace=tr)
+    assert {st for (_, _, st, _, _) in tr} == {3}
+    assert len(tr) == (-(-n // bm)) * (-(-n // bn))
+
+
+def test_online_fa1_trace_running_max():
+    """FA1's running max m_i never decreases and ends at the row max."""
+    n = 12
+    q, k, v = (P.rand((1, 1, n, 3), 400 + s) for s in range(3))
+    tr = []
+    oracle.online_fa1(q, k, v, 1.0, False, 4, 3, trace=tr)
+    for i in range(3):
+        ms = [m for (ii, _, m, _) in tr if ii == i]
+        for a, b in zip(ms, ms[1:]):
+            assert np.all(b >= a)
+    s = q[0, 0] @ k[0, 0].T
+    final = np.concatenate([m for (ii, j, m, _) in tr if j == 3])
+    np.testing.assert_allclose(final, s.max(1), rtol=0, atol=1e-12)
+
+
+def test_fa1_block_sizes():
+    """B_c = ceil(M/4d), B_r = min(B_c, d) ([review] Algorithm 1, step 1)."""
+    assert oracle.fa1_block_sizes(1000, 16) == (16, 16)     # ceil(1000/64) = 16
+    assert oracle.fa1_block_sizes(81920, 128) == (128, 160)  # 160 KB of bf16 at d=128
+    assert oracle.fa1_block_sizes(81920, 64) == (64, 320)
+    assert oracle.fa1_block_sizes(100, 64) == (1, 1)
+
+
+def test_causal_stages_golden():
+    """The worked example of [triton] 'Improvement 3'."""
+    g = json.load(open(os.path.join(GOLDEN, "triton_fa2_causal_stages.json")))
+    c0, c1 = g["cases"]
+    (a1, b1), (a2, b2) = oracle.causal_stage_ranges(c0["start_m"], c0["block_m"], c0["block_n"], c0["seq"])
+    assert list(range(a1, b1)) == c0["stage1"]
+    assert list(range(a2, b2)) == c0["stage2"]
+    assert b2 == c0["first_skipped"]
+    (a1, b1), (a2, b2) = oracle.causal_stage_ranges(c1["start_m"], c1["block_m"], c1["block_n"], c1["seq"])
+    assert b1 - a1 == c1["stage1_count"] and b2 - a2 == c1["stage2_count"]
+    assert (b2 - a2) / (b2 - a1) == pytest.approx(1 / 64)
+
+
+def test_causal_stages_cover_exactly_the_allowed_keys():
+    """Stage 1 blocks hold only allowed keys for every row of the block;
+    stage 2 blocks straddle; every allowed key is in a visited block."""
+    for n in (1, 7, 64, 100, 513):
+        for bm in (16, 64, 128, 256):
+            for bn in (16, 32, 64, 128):
+                for i in range(-(-n // bm)):
+                    (a1, b1), (a2, b2) = oracle.causal_stage_ranges(i, bm, bn, n)
+                    first, last = i * bm, min(n, (i + 1) * bm) - 1
+                    for j in range(a1, b1):
+                        assert (j + 1) * bn - 1 <= first
+                    for j in range(a2, b2):
+                        assert j * bn <= last
+                    assert b2 * bn > last  # last row's own key is visited
+                    assert (b2 * bn) >= last + 1
+
+
+def test_nonfinite_guard_in_fa1():
+    """Rows with no allowed key in a causal block contribute nothing (the
+    exp of -inf minus -inf is taken as 0, never NaN)."""
+    q, k, v = (P.rand((1, 1, 9, 2), 500 + s) for s in range(3))
+    o, lse = oracle.online_fa1(q, k, v, 1.0, True, 9, 2)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))

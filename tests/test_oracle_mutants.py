@@ -1,0 +1,117 @@
+"""Planted mistakes in copies of the oracle must each fail a pin (CPU only).
+
+The mutants below are the oracle's forward/backward with one plausible slip
+each: a dropped scale, a mask that points the wrong way or drops the
+diagonal, a transposed or swapped operand, a wrong log base, no max
+subtraction, a dropped term of the softmax Jacobian, a missing scale in one
+gradient.  If a mutant passed every pin, the pins would not be strong enough
+to trust the oracle; this test fails in that case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+
+def _fwd_variant(q, k, v, scale, causal, mut):
+    B, H, N, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            s = (1.0 if mut == "no_scale" else scale) * (q[b, h] @ k[b, h].T)
+            if causal:
+                i = np.arange(N)[:, None]
+                j = np.arange(N)[None, :]
+                bad = {"mask_reversed": j < i, "mask_no_diag": j >= i}.get(mut, j > i)
+                s = np.where(bad, -np.inf, s)
+            m = 0.0 if mut == "no_max_sub" else s.max(1, keepdims=True)
+            with np.errstate(over="ignore", invalid="ignore"):
+                f = np.exp(s - m)
+                l = f.sum(1, keepdims=True)
+                p = f / l
+            if mut == "p_transposed":
+                p = p.T
+            o[b, h] = p @ (k[b, h] if mut == "uses_k_not_v" else v[b, h])
+            with np.errstate(divide="ignore", invalid="ignore"):
+                ll = (m + np.log(l))[:, 0]
+            lse[b, h] = ll / np.log(2) if mut == "lse_base2" else ll
+    return o, lse
+
+
+FWD_MUTANTS = ["no_scale", "mask_reversed", "mask_no_diag", "no_max_sub", "p_transposed",
+               "uses_k_not_v", "lse_base2"]
+
+
+def _bwd_variant(q, k, v, g, scale, causal, mut):
+    B, H, N, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    delta = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            dp = g[b, h] @ v[b, h].T
+            dl = (p * dp).sum(1)
+            ds = p * dp if mut == "no_delta_term" else p * (dp - dl[:, None])
+            dq[b, h] = scale * ds @ k[b, h]
+            dk[b, h] = (1.0 if mut == "dk_no_scale" else scale) * ds.T @ q[b, h]
+            dv[b, h] = (p @ g[b, h]) if mut == "dv_no_transpose" else p.T @ g[b, h]
+            if mut == "dq_uses_q":
+                dq[b, h] = scale * ds @ q[b, h]
+            delta[b, h] = dl
+    return dq, dk, dv, delta
+
+
+BWD_MUTANTS = ["no_delta_term", "dk_no_scale", "dv_no_transpose", "dq_uses_q"]
+
+
+def _fails_some(pins):
+    failed = []
+    for name, run in pins:
+        try:
+            run()
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_variants_pass():
+    fwd = lambda q, k, v, s, c: _fwd_variant(q, k, v, s, c, None)  # noqa: E731
+    bwd = lambda q, k, v, g, s, c: _bwd_variant(q, k, v, g, s, c, None)  # noqa: E731
+    for pin in P.FWD_PINS:
+        pin(fwd)
+    P.pin_finite_differences(oracle.attn_fwd, bwd)
+    P.pin_gradient_sums(bwd)
+    P.pin_torch_autograd(bwd)
+
+
+@pytest.mark.parametrize("mut", FWD_MUTANTS)
+def test_forward_mutant_is_caught(mut):
+    fwd = lambda q, k, v, s, c: _fwd_variant(q, k, v, s, c, mut)  # noqa: E731
+    pins = [(p.__name__, (lambda p=p: p(fwd))) for p in P.FWD_PINS]
+    pins.append(("bruteforce", lambda: P.pin_bruteforce_fwd(fwd, oracle.attn_fwd_bruteforce)))
+    assert _fails_some(pins), f"mutant {mut} passed every forward pin"
+
+
+@pytest.mark.parametrize("mut", BWD_MUTANTS)
+def test_backward_mutant_is_caught(mut):
+    bwd = lambda q, k, v, g, s, c: _bwd_variant(q, k, v, g, s, c, mut)  # noqa: E731
+    pins = [
+        ("fd", lambda: P.pin_finite_differences(oracle.attn_fwd, bwd)),
+        ("sums", lambda: P.pin_gradient_sums(bwd)),
+        ("autograd", lambda: P.pin_torch_autograd(bwd)),
+    ]
+    assert _fails_some(pins), f"mutant {mut} passed every backward pin"
+
+
+def test_fd_alone_catches_every_backward_mutant():
+    """Calculus alone (no library) already rejects each backward mutant."""
+    for mut in BWD_MUTANTS:
+        bwd = lambda q, k, v, g, s, c, mut=mut: _bwd_variant(q, k, v, g, s, c, mut)  # noqa: E731
+        with pytest.raises(AssertionError):
+            P.pin_finite_differences(oracle.attn_fwd, bwd)
