@@ -25,8 +25,10 @@ ROW_CHUNK = 512
 
 
 def _check(q, k, v):
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError(f"q, k, v must share one [B,H,N,d] shape, got {q.shape} {k.shape} {v.shape}")
+    """q and k are [B,H,N,d]; v is [B,H,N,d_v] with any d_v (Algorithm 0
+    only needs V to have one row per key)."""
+    if q.ndim != 4 or q.shape != k.shape or v.ndim != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"need q, k [B,H,N,d] and v [B,H,N,d_v], got {q.shape} {k.shape} {v.shape}")
     for t in (q, k, v):
         if t.dtype != np.float64:
             raise TypeError("the oracle computes in float64; upcast the inputs first")
@@ -51,7 +53,7 @@ def attn_fwd(q, k, v, scale: float, causal: bool):
     """
     _check(q, k, v)
     B, H, N, d = q.shape
-    out = np.empty_like(q)
+    out = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
@@ -76,8 +78,7 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, rows):
     Returns (O rows [len, d], LSE [len]).
     """
     rows = list(rows)
-    d = q.shape[-1]
-    o = np.empty((len(rows), d), dtype=np.float64)
+    o = np.empty((len(rows), v.shape[-1]), dtype=np.float64)
     lse = np.empty(len(rows), dtype=np.float64)
     for n, (b, h, i) in enumerate(rows):
         n_keys = i + 1 if causal else q.shape[2]

@@ -1,0 +1,172 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/fa.h declares, and rejects bad arguments before any HIP call (no
+compute call is made here)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_exact_03_amd import _lib
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
+
+
+def test_binding_signatures_cover_header():
+    from io_aware_exact_03_amd import _lib
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+FA_OK, FA_ERR_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN = 0, 1, 2, 3
+A = 4096  # a 16-byte aligned fake address; never dereferenced on rejected calls
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=8, d=64, scale=1.0, causal=0, dtype=2):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), FA_ERR_ARG), (dict(k=None), FA_ERR_ARG), (dict(v=None), FA_ERR_ARG),
+    (dict(o=None), FA_ERR_ARG), (dict(lse=None), FA_ERR_ARG),
+    (dict(N=0), FA_ERR_ARG), (dict(B=0), FA_ERR_ARG), (dict(H=-1), FA_ERR_ARG),
+    (dict(causal=2), FA_ERR_ARG), (dict(scale=float("nan")), FA_ERR_ARG), (dict(scale=float("inf")), FA_ERR_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED), (dict(d=256), FA_ERR_UNSUPPORTED), (dict(dtype=7), FA_ERR_UNSUPPORTED),
+    (dict(q=A + 8), FA_ERR_ALIGN), (dict(lse=A + 4), FA_ERR_ALIGN), (dict(o=A + 2), FA_ERR_ALIGN),
+    (dict(B=1 << 20, H=1 << 20, N=1 << 20), FA_ERR_ARG),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_bwd_rejects(lib):
+    args = [A] * 10
+    base = dict(B=1, H=1, N=8, d=64, scale=1.0, causal=0, dtype=2)
+
+    def call(ptrs, **kw):
+        p = dict(base, **kw)
+        return lib.fa_bwd(*ptrs, p["B"], p["H"], p["N"], p["d"], p["scale"], p["causal"], p["dtype"], None)
+    for i in range(10):
+        ptrs = list(args)
+        ptrs[i] = None
+        assert call(ptrs) == FA_ERR_ARG
+        ptrs[i] = A + 4
+        assert call(ptrs) == FA_ERR_ALIGN
+    assert call(args, d=32) == FA_ERR_UNSUPPORTED
+    assert call(args, N=-3) == FA_ERR_ARG
+
+
+def test_naive_rejects(lib):
+    args = [A] * 7
+
+    def call(ptrs, N=8, d=64, dtype=1):
+        return lib.fa_naive_fwd(*ptrs, 1, 1, N, d, 0.5, 0, dtype, None)
+    for i in range(7):
+        ptrs = list(args)
+        ptrs[i] = None
+        assert call(ptrs) == FA_ERR_ARG
+        ptrs[i] = A + 2
+        assert call(ptrs) == FA_ERR_ALIGN
+    assert call(args, d=80) == FA_ERR_UNSUPPORTED
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_naive_workspace_bytes(4, 8, 4096, 1) == 4 * 8 * 4096 * 4096 * 2
+    assert lib.fa_naive_workspace_bytes(1, 16, 16384, 2) == 16 * 16384 * 16384 * 2  # fp16 S for bf16 inputs
+    assert lib.fa_naive_workspace_bytes(1, 1, 512, 0) == 512 * 512 * 4
+    assert lib.fa_naive_workspace_bytes(0, 1, 512, 0) == 0
+    assert lib.fa_naive_workspace_bytes(1, 1, 512, 9) == 0
+
+
+def test_strerror(lib):
+    for s in range(6):
+        assert isinstance(lib.fa_strerror(s), bytes)
+    assert lib.fa_last_hip_error() == 0
+
+
+def test_kernel_causal_plan_matches_page_example():
+    """The kernels' causal plan reproduces the worked example of 'Triton 06:
+    Flash Attention v2', Improvement 3."""
+    from io_aware_exact_03_amd import causal_stages
+    g = json.load(open(os.path.join(GOLDEN, "triton_fa2_causal_stages.json")))
+    c0, c1 = g["cases"]
+    r0 = c0["start_m"] * c0["block_m"]
+    s1, s2 = causal_stages(r0, r0 + c0["block_m"], c0["block_n"], c0["seq"])
+    assert list(range(0, s1)) == c0["stage1"] and list(range(s1, s2)) == c0["stage2"]
+    assert s2 == c0["first_skipped"]
+    r0 = c1["start_m"] * c1["block_m"]
+    s1, s2 = causal_stages(r0, r0 + c1["block_m"], c1["block_n"], c1["seq"])
+    assert s1 == c1["stage1_count"] and s2 - s1 == c1["stage2_count"]
+
+
+def test_kernel_causal_plan_is_exact():
+    """Unmasked blocks hold only keys visible to every row; masked blocks
+    hold at least one visible key; skipped blocks hold none."""
+    from io_aware_exact_03_amd import causal_stages
+    for n in (1, 5, 64, 100, 777):
+        for bm in (32, 64, 128, 256):
+            for bn in (32, 64, 128):
+                for r0 in range(0, n, bm):
+                    r1 = min(n, r0 + bm)
+                    s1, s2 = causal_stages(r0, r1, bn, n)
+                    for j in range(-(-n // bn)):
+                        first, last = j * bn, (j + 1) * bn - 1
+                        if j < s1:
+                            assert last <= r0
+                        elif j < s2:
+                            assert first <= r1 - 1
+                        else:
+                            assert first > r1 - 1
+
+
+def test_causal_plan_rejects(lib):
+    a, b = ctypes.c_int(), ctypes.c_int()
+    assert lib.fa_causal_stages(5, 5, 64, 10, ctypes.byref(a), ctypes.byref(b)) == FA_ERR_ARG
+    assert lib.fa_causal_stages(0, 11, 64, 10, ctypes.byref(a), ctypes.byref(b)) == FA_ERR_ARG
+    assert lib.fa_causal_stages(0, 10, 0, 10, ctypes.byref(a), ctypes.byref(b)) == FA_ERR_ARG
+    assert lib.fa_causal_stages(0, 10, 64, 10, None, ctypes.byref(b)) == FA_ERR_ARG
+
+
+def test_fwd_tile():
+    import torch
+    from io_aware_exact_03_amd import fwd_tile
+    for d in (64, 128):
+        for dt in (torch.float32, torch.float16, torch.bfloat16):
+            bm, bn, w = fwd_tile(d, dt)
+            assert bm % 32 == 0 and bn % 32 == 0 and w >= 1 and bm % bn == 0
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    """With the library absent the binding raises; nothing computes on the CPU."""
+    from io_aware_exact_03_amd import _lib
+    with pytest.raises(OSError):
+        _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_package_does_not_import_oracle():
+    """The product package never imports the oracle (no file mentions it)."""
+    pkg = os.path.join(ROOT, "io_aware_exact_03_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\bimport\s+oracle|from\s+oracle|oracle/", text), f
