@@ -1,0 +1,147 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * What the library computes.  For every batch b and head h, with Q, K, V the
+ * N x d slices of that (b, h):
+ *
+ *     S = scale * Q K^T            (N x N, never stored by fa_fwd / fa_bwd)
+ *     P = softmax(S) row-wise      (causal: S_ij = -inf for j > i)
+ *     O = P V                      (N x d)
+ *     LSE_i = ln sum_j exp(S_ij)   (natural log, over the allowed j)
+ *
+ * This is standard attention as defined by Algorithm 0 of "Paper review:
+ * FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * (osehyeon.github.io), with the 1/sqrt(d)-style scale of "Flash Attention:
+ * IO-awareness principle" (hrletsgo.me, section on standard attention's
+ * bottleneck) taken as an argument.  fa_fwd computes it the FlashAttention-2
+ * way ("Triton 06: Flash Attention v2", wonbeomjang.kr, Improvements 1-4):
+ * Q row-blocks outside, K/V blocks inside, S and P kept on chip.  fa_bwd
+ * recomputes P from LSE ("Backward" and the forward/backward flow summary on
+ * the same page).  fa_naive_fwd is the three-kernel path that writes S and P
+ * to memory ("Flash Attention -- five lessons converging into 80 lines",
+ * brianyu43.github.io, "Two implementations").
+ *
+ * Layout.  Q, K, V, O, dO are [B, H, N, d] contiguous row-major (d fastest)
+ * in the element type `dtype`.  LSE and Delta are float32 [B, H, N].  dQ, dK,
+ * dV are float32 [B, H, N, d].  Naive S and P workspaces are [B, H, N, N],
+ * float16 when dtype is 16-bit (f16 or bf16) and float32 when dtype is f32.
+ *
+ * Supported values.  d in {64, 128} (else FA_ERR_UNSUPPORTED); N >= 1 (any
+ * value; ragged tails are masked); B, H >= 1; causal in {0, 1}; scale finite
+ * (zero and negative allowed).  causal = 1 keeps key j for query i iff
+ * j <= i (square, top-left aligned, diagonal kept).
+ *
+ * Ownership.  The caller allocates and frees every buffer, workspaces
+ * included.  The library never allocates, frees or synchronises, and keeps
+ * no state between calls except a thread-local copy of the last HIP error.
+ * All device pointers are on the current HIP device.  `stream` is a
+ * hipStream_t (NULL = the default stream).  Calls enqueue work and return:
+ * results are ready when the stream is; a fault in a kernel shows at the
+ * caller's next synchronisation.
+ *
+ * Errors.  Every entry point returns an fa_status synchronously.  All
+ * argument checks run on the host before any HIP call, so a rejected call
+ * touches no device state: null pointer -> FA_ERR_ARG; shape or size
+ * overflowing int64 -> FA_ERR_ARG; a device pointer not 16-byte aligned ->
+ * FA_ERR_ALIGN; unsupported d or dtype (or f32 in fa_bwd's unsupported
+ * cases, none today) -> FA_ERR_UNSUPPORTED.  A launch failure reported by
+ * hipGetLastError() -> FA_ERR_HIP; fa_last_hip_error() then returns that
+ * hipError_t value for the calling thread.  No C++ exception crosses the ABI.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_ALIGN = 3,
+  FA_ERR_HIP = 4
+} fa_status;
+
+/*
+ * Fused forward.  Reads q, k, v; writes o (dtype, [B,H,N,d]) and lse
+ * (float32 [B,H,N], natural log).  One pass over K/V per query block with
+ * the online softmax: running max and sum per row, an un-scaled accumulator
+ * rescaled when the max grows, one divide at the end, exp2 with
+ * log2(e) folded into the scale, and a per-row LSE saved for fa_bwd
+ * ("Triton 06: Flash Attention v2", Improvements 1-3).  Causal runs the
+ * fully visible key blocks without a mask and masks only the diagonal
+ * blocks; key blocks wholly in the future are never read.
+ * q, k, v, o, lse: device pointers, 16-byte aligned, not aliased with each
+ * other.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Fused backward with recomputation ("Triton 06: Flash Attention v2",
+ * "Backward" and the flow summary; "Flash Attention: IO-awareness
+ * principle", "Recomputation").  Inputs q, k, v, o (the fa_fwd output),
+ * dout (dO), all dtype [B,H,N,d], and lse (float32 [B,H,N], natural log,
+ * as fa_fwd wrote it).  Three launches on `stream`, in order:
+ *   1. Delta_i = sum_c dO_ic * O_ic  -> delta_ws (float32 [B,H,N])
+ *   2. per K/V block: P recomputed from LSE; dV += P^T dO;
+ *      dS = P * (dO V^T - Delta); dK += scale * dS^T Q      -> dk, dv
+ *   3. per Q block:  dQ += scale * dS K                      -> dq
+ * dq, dk, dv are float32 [B,H,N,d] and are fully overwritten (no zeroing
+ * needed).  delta_ws is caller-owned scratch that holds Delta afterwards.
+ * dtype f16 and bf16 are supported; f32 too (same kernels in fp32).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, float* delta_ws, float* dq, float* dk, float* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Naive three-kernel forward ("Flash Attention -- five lessons converging
+ * into 80 lines", "Two implementations"; Algorithm 0 of the FlashAttention
+ * paper review): kernel 1 writes S = scale * Q K^T for all N x N into
+ * s_ws; kernel 2 reads S, applies the causal mask if asked, and writes the
+ * row softmax P into p_ws plus lse; kernel 3 reads P and V and writes o.
+ * s_ws and p_ws are caller-owned, fa_naive_workspace_bytes() bytes each.
+ * Kept to measure the N^2 memory traffic that fa_fwd avoids.
+ */
+int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* s_ws, void* p_ws, int B, int H, int N, int d, float scale,
+                 int causal, int dtype, void* stream);
+
+/* Bytes of ONE of the naive S, P workspaces: B*H*N*N elements of float16
+ * (dtype f16/bf16) or float32 (dtype f32).  0 for invalid arguments. */
+size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/* Static English text for an fa_status value (never NULL). */
+const char* fa_strerror(int status);
+
+/* hipError_t of the most recent FA_ERR_HIP on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+/*
+ * Host copy of the causal key-block plan the kernels use ("Triton 06: Flash
+ * Attention v2", Improvement 3).  For the query rows [row0, row_end) and key
+ * blocks of `bn` keys: blocks [0, *s1_end) lie at or left of row0 and run
+ * without a mask; blocks [*s1_end, *s2_end) straddle the diagonal and are
+ * masked; later blocks are skipped.  Requires 0 <= row0 < row_end <= n,
+ * bn >= 1; returns FA_ERR_ARG otherwise.  Pure host function (no HIP call).
+ */
+int fa_causal_stages(int row0, int row_end, int bn, int n, int* s1_end, int* s2_end);
+
+/*
+ * The forward's tile for (d, dtype): *bm query rows per workgroup,
+ * *bn keys per K/V block, *waves wavefronts of 64 lanes per workgroup.
+ * Pure host function; FA_ERR_UNSUPPORTED for unsupported d/dtype.
+ */
+int fa_fwd_tile(int d, int dtype, int* bm, int* bn, int* waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,131 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation on the
+// host (before any HIP call), kernel dispatch, error mapping.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+#include "fa_plan.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = (int)e;
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// Shape checks shared by every entry point.  Sizes must fit the kernels'
+// index arithmetic: int for row/column indices, 64-bit for element offsets.
+int check_shape(int B, int H, int N, int d, int dtype, int causal, float scale) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  if (bh > 0x7fffffffLL) return FA_ERR_ARG;
+  // bytes of one [B,H,N,d] tensor must fit in int64 (and then some)
+  const long double bytes = (long double)bh * N * d * elem_bytes(dtype);
+  if (bytes > (long double)(1LL << 62)) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_ARG: return "invalid argument (null pointer, bad size or flag, non-finite scale, or overflow)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FA_ERR_HIP: return "HIP launch error (see fa_last_hip_error)";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_causal_stages(int row0, int row_end, int bn, int n, int* s1_end, int* s2_end) {
+  if (!s1_end || !s2_end || bn < 1 || row0 < 0 || row_end <= row0 || row_end > n) return FA_ERR_ARG;
+  fa::causal_stages(row0, row_end, bn, s1_end, s2_end);
+  return FA_OK;
+}
+
+int fa_fwd_tile(int d, int dtype, int* bm, int* bn, int* waves) {
+  if (!bm || !bn || !waves) return FA_ERR_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const fa::FwdTile t = fa::fwd_tile(d, dtype == FA_F32);
+  *bm = t.bm;
+  *bn = t.bn;
+  *waves = t.waves;
+  return FA_OK;
+}
+
+size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;
+  const long double b = (long double)B * H * N * N * (dtype == FA_F32 ? 4 : 2);
+  if (b > (long double)(1LL << 62)) return 0;
+  return (size_t)B * H * (size_t)N * (size_t)N * (dtype == FA_F32 ? 4 : 2);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
+  const int st = check_shape(B, H, N, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
+  a.qk_scale = fabsf(scale) * fa::kLog2eHost;
+  a.neg = scale < 0.f;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_fwd(a));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+           int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta_ws || !dq || !dk || !dv) return FA_ERR_ARG;
+  const int st = check_shape(B, H, N, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, delta_ws, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.delta = delta_ws; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0; a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_bwd(a));
+}
+
+int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* s_ws, void* p_ws, int B,
+                 int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !s_ws || !p_ws) return FA_ERR_ARG;
+  const int st = check_shape(B, H, N, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  if (fa_naive_workspace_bytes(B, H, N, dtype) == 0) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, s_ws, p_ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  fa::NaiveArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.s = s_ws; a.p = p_ws;
+  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0; a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_naive(a));
+}
+
+}  // extern "C"

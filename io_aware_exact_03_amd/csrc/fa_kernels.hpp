@@ -1,0 +1,67 @@
+// fa_kernels.hpp -- internal launch interface between the C ABI (fa_api.hip)
+// and the kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;          // batch * heads
+  int N;
+  int d;           // 64 or 128
+  int dtype;       // 0 f32, 1 f16, 2 bf16
+  bool causal;
+  float qk_scale;  // |scale| * log2(e)
+  bool neg;        // scale < 0: the kernels negate Q on load
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int BH;
+  int N;
+  int d;
+  int dtype;
+  bool causal;
+  float scale;     // signed
+  hipStream_t stream;
+};
+
+struct NaiveArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* s;
+  void* p;
+  int BH;
+  int N;
+  int d;
+  int dtype;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_naive(const NaiveArgs& a);
+
+}  // namespace fa

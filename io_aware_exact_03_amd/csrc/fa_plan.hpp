@@ -1,0 +1,68 @@
+// fa_plan.hpp -- integer planning shared by the host ABI and the kernels:
+// causal key-block stages, workgroup-to-tile order, tile shapes.
+//
+// Pages cited: "Triton 06: Flash Attention v2" (wonbeomjang.kr),
+// Improvement 3 (causal mask split into an unmasked stage and a masked
+// diagonal stage); "Flash Attention: IO-awareness principle" (hrletsgo.me),
+// section "FA2/FA3" (query blocks in the outer loop, each workgroup finishes
+// its own output block with no cross-block synchronisation).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define FA_HD __host__ __device__ __forceinline__
+#else
+#define FA_HD inline
+#endif
+
+namespace fa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Key-block plan of the causal split for the query rows [row0, row_end):
+// blocks j < s1_end hold only keys <= row0 (their last key, (j+1)*bn - 1, is
+// at or left of the first row) and need no mask; blocks s1_end <= j < s2_end
+// straddle the diagonal and are masked; blocks from s2_end on lie wholly in
+// the future and are skipped.
+//
+// The page classifies block j as unmasked when its first key is left of
+// the block's first row, which is exact only when the query block size is a
+// multiple of bn; the comparison below is exact for any sizes.
+FA_HD void causal_stages(int row0, int row_end, int bn, int* s1_end, int* s2_end) {
+  // (j+1)*bn - 1 <= row0  <=>  j <= (row0 + 1)/bn - 1
+  *s1_end = (row0 + 1) / bn;
+  *s2_end = (row_end - 1) / bn + 1;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs (hardware id b runs on XCD
+// b % 8), and each XCD has its own L2.  Renumber so that every XCD gets one
+// contiguous range of logical tiles: tiles of one (batch, head) then share
+// an L2 and its K/V stream.  Bijective on [0, total) for any total.
+FA_HD int xcd_remap(int b, int total) {
+  constexpr int NX = 8;
+  const int xcd = b % NX, slot = b / NX;
+  const int q = total / NX, r = total % NX;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Logical tile -> (batch*head, query block).  Within one (batch, head) the
+// causal order runs from the last query block (most key blocks) to the
+// first, so long workgroups start early and the tail is short.
+FA_HD void tile_of(int logical, int n_qblk, bool causal, int* bh, int* qblk) {
+  *bh = logical / n_qblk;
+  const int j = logical % n_qblk;
+  *qblk = causal ? (n_qblk - 1 - j) : j;
+}
+
+// Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
+struct FwdTile {
+  int bm, bn, waves;
+};
+
+FA_HD FwdTile fwd_tile(int d, bool is_f32) {
+  if (is_f32) return FwdTile{128, 64, 4};
+  return d == 128 ? FwdTile{256, 64, 4} : FwdTile{256, 64, 4};
+}
+
+}  // namespace fa
