@@ -43,8 +43,8 @@
  * argument checks run on the host before any HIP call, so a rejected call
  * touches no device state: null pointer -> FA_ERR_ARG; shape or size
  * overflowing int64 -> FA_ERR_ARG; a device pointer not 16-byte aligned ->
- * FA_ERR_ALIGN; unsupported d or dtype (or f32 in fa_bwd's unsupported
- * cases, none today) -> FA_ERR_UNSUPPORTED.  A launch failure reported by
+ * FA_ERR_ALIGN; unsupported d or dtype (and f32 in fa_bwd) ->
+ * FA_ERR_UNSUPPORTED.  A launch failure reported by
  * hipGetLastError() -> FA_ERR_HIP; fa_last_hip_error() then returns that
  * hipError_t value for the calling thread.  No C++ exception crosses the ABI.
  */
@@ -94,7 +94,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   3. per Q block:  dQ += scale * dS K                      -> dq
  * dq, dk, dv are float32 [B,H,N,d] and are fully overwritten (no zeroing
  * needed).  delta_ws is caller-owned scratch that holds Delta afterwards.
- * dtype f16 and bf16 are supported; f32 too (same kernels in fp32).
+ * dtype f16 and bf16 are supported; f32 returns FA_ERR_UNSUPPORTED.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, float* delta_ws, float* dq, float* dk, float* dv,

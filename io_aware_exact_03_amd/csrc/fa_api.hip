@@ -101,6 +101,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (!q || !k || !v || !o || !dout || !lse || !delta_ws || !dq || !dk || !dv) return FA_ERR_ARG;
   const int st = check_shape(B, H, N, d, dtype, causal, scale);
   if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit MFMA only
   const void* ptrs[] = {q, k, v, o, dout, lse, delta_ws, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;

@@ -1,6 +1,481 @@
-// fa_bwd.hip -- placeholder until the backward kernels land.
+// fa_bwd.hip -- exact-attention backward with recomputation, for gfx950.
+//
+// Three launches on one stream ("Triton 06: Flash Attention v2",
+// wonbeomjang.kr, "Backward" and the forward/backward flow summary; "Flash
+// Attention: IO-awareness principle", hrletsgo.me, "Recomputation"):
+//   1. Delta_i = rowsum(dO_i * O_i)
+//   2. dK/dV: one workgroup per block of keys, looping over query blocks;
+//      P recomputed from the saved LSE, dV += P^T dO,
+//      dS = P * (dO V^T - Delta), dK += scale * dS^T Q
+//   3. dQ:    one workgroup per block of queries, looping over key blocks;
+//      dQ += scale * dS K
+// No N x N matrix is stored and no atomics are used: every output element
+// is written by exactly one workgroup, so results are deterministic.
+//
+// Layout choices on gfx950 (the pages show no code for these kernels):
+// * dK/dV computes S = Q K^T (queries x keys) so each lane owns one key:
+//   the fp32 accumulators of P and dS, packed to 16-bit, are directly the A
+//   operand of the dV and dK products, whose B operands (dO and Q with the
+//   queries as contraction index) come from transposed LDS copies whose
+//   query order matches the accumulator registers.
+// * dQ computes S^T (keys x queries) like the forward, so each lane owns one
+//   query; dS^T is the B operand of dQ^T = K^T dS^T with K^T in LDS.
+// * Per-query LSE and Delta are lane-local in dQ and read from LDS (four
+//   16-byte broadcast reads per 32 queries) in dK/dV.
+// * The next query/key block is loaded into registers while the current one
+//   computes; LDS is double-buffered with one barrier per block.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.hpp"
 #include "fa_kernels.hpp"
+#include "fa_plan.hpp"
+
 namespace fa {
-hipError_t launch_bwd(const BwdArgs&) { return hipErrorNotSupported; }
+namespace {
+
+constexpr float kPosInf = __builtin_huge_valf();
+
+// Position of row kappa of a 16-row group in a transposed LDS tile: bits 2
+// and 3 swapped, which puts the rows a lane half holds in accumulator
+// registers 0..7 at 8 consecutive positions (see the forward kernel).
+__device__ __forceinline__ int tpos(int kappa) {
+  return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
+}
+
+// Write KPT rows x 8 columns (16-bit, one uint4 per row) transposed into 8
+// rows of `dst` (row stride `stride` elements) at column `pos`.
+template <int KPT>
+__device__ __forceinline__ void store_transposed(uint16_t* dst, int stride, int pos, const uint4 (&x)[KPT]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(x);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int sh = (t & 1) ? 16 : 0;
+    uint16_t* p = dst + t * stride + pos;
+    if constexpr (KPT == 4) {
+      const uint32_t e0 = (w[0 + t / 2] >> sh) & 0xffffu, e1 = (w[4 + t / 2] >> sh) & 0xffffu;
+      const uint32_t e2 = (w[8 + t / 2] >> sh) & 0xffffu, e3 = (w[12 + t / 2] >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(p) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    } else {
+      const uint32_t e0 = (w[0 + t / 2] >> sh) & 0xffffu, e1 = (w[4 + t / 2] >> sh) & 0xffffu;
+      *reinterpret_cast<uint32_t*>(p) = e0 | (e1 << 16);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack8(T, const f32x16& v, int h) {
+  return make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
+                    pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
+}
+
+// ---------------------------------------------------------------------------
+// 1. Delta_i = sum_c dO_ic O_ic (fp32), D/8 lanes per row.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ og,
+                                                        const uint16_t* __restrict__ dog,
+                                                        float* __restrict__ delta, long long rows) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(og + row * D + 8 * c);
+    const uint4 b = *reinterpret_cast<const uint4*>(dog + row * D + 8 * c);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_fmaf(lo16(T{}, wa[i]), lo16(T{}, wb[i]), acc);
+      acc = __builtin_fmaf(hi16(T{}, wa[i]), hi16(T{}, wb[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV.  Workgroup = 4 waves x 32 keys; inner loop over 64-query blocks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KV {
+  static constexpr int NW = 4, NT = 256, KW = 32, BNK = NW * KW, BMQ = 64;
+  static constexpr int QROW = D + 8;      // row-major Q / dO stride (elements)
+  static constexpr int TROW = BMQ + 8;    // transposed Q^T / dO^T stride
+  static constexpr int DS = D / 16, DB = D / 32;
+  static constexpr int KPT = BMQ * D / 8 / NT;  // query rows per thread in staging
+  static_assert(KPT == 2 || KPT == 4, "staging packs 2 or 4 rows per thread");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
+    float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, float qk_scale, float dk_scale,
+    uint32_t qsign) {
+  using C = KV<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::BMQ * C::QROW];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::BMQ * C::QROW];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) float lse_lds[2][C::BMQ];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][C::BMQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
+  int bh, kblk;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), n_kblk, false, &bh, &kblk);  // ascending = heaviest first
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* qh = qg + head;
+  const uint16_t* doh = dog + head;
+  const float* lseh = lseg + (size_t)bh * N;
+  const float* dlh = deltag + (size_t)bh * N;
+
+  const int kw0 = kblk * C::BNK + wave * C::KW;  // first key of this wave
+  const int key = kw0 + n;                       // this lane's key
+  const bool wave_live = kw0 < N;
+
+  // K and V as B operands of S = Q K^T and dP = dO V^T: K[key][16 s + 8 g ..].
+  uint4 kf[C::DS], vf[C::DS];
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (key < N) {
+      a = *reinterpret_cast<const uint4*>(kg + head + (size_t)key * D + 16 * s + 8 * g);
+      b = *reinterpret_cast<const uint4*>(vg + head + (size_t)key * D + 16 * s + 8 * g);
+    }
+    kf[s] = a;
+    vf[s] = b;
+  }
+  f32x16 dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
+  const int i_lo = CAUSAL ? (kblk * C::BNK) / C::BMQ : 0;
+
+  // staging: thread owns KPT consecutive query rows x one 8-column chunk
+  const int sa = tid % (C::BMQ / C::KPT), sc = tid / (C::BMQ / C::KPT);
+  uint4 qs[C::KPT], dos[C::KPT];
+  float lse_s = 0.f, dl_s = 0.f;
+
+  auto load_block = [&](int i) {
+#pragma unroll
+    for (int e = 0; e < C::KPT; ++e) {
+      const int row = i * C::BMQ + C::KPT * sa + e;
+      uint4 a = make_uint4(0, 0, 0, 0), b = a;
+      if (row < N) {
+        a = *reinterpret_cast<const uint4*>(qh + (size_t)row * D + 8 * sc);
+        b = *reinterpret_cast<const uint4*>(doh + (size_t)row * D + 8 * sc);
+        a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
+      }
+      qs[e] = a;
+      dos[e] = b;
+    }
+    if (tid < C::BMQ) {
+      const int row = i * C::BMQ + tid;
+      // A query past the end gets LSE = +inf, so its recomputed P is 0.
+      lse_s = row < N ? lseh[row] * kLog2e : kPosInf;
+      dl_s = row < N ? dlh[row] : 0.f;
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < C::KPT; ++e) {
+      const int r = C::KPT * sa + e;
+      *reinterpret_cast<uint4*>(&q_lds[buf][r * C::QROW + 8 * sc]) = qs[e];
+      *reinterpret_cast<uint4*>(&do_lds[buf][r * C::QROW + 8 * sc]) = dos[e];
+    }
+    store_transposed<C::KPT>(&qt_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), qs);
+    store_transposed<C::KPT>(&dot_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), dos);
+    if (tid < C::BMQ) {
+      lse_lds[buf][tid] = lse_s;
+      dl_lds[buf][tid] = dl_s;
+    }
+  };
+
+  if (i_lo < n_qblk) {
+    load_block(i_lo);
+    store_block(i_lo & 1);
+  }
+  __syncthreads();
+
+  for (int i = i_lo; i < n_qblk; ++i) {
+    const int buf = i & 1;
+    const bool more = i + 1 < n_qblk;
+    if (more) load_block(i + 1);
+
+    const int q_first = i * C::BMQ;
+    const int q_last = min(q_first + C::BMQ, N) - 1;
+    const bool active = wave_live && (!CAUSAL || q_last >= kw0);
+    const bool need_mask = CAUSAL && q_first < kw0 + C::KW - 1;
+    if (active) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        s[qc] = f32x16{};
+        dp[qc] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < C::DS; ++st) {
+          const int off = (32 * qc + n) * C::QROW + 16 * st + 8 * g;
+          s[qc] = mma16(T{}, *reinterpret_cast<const uint4*>(&q_lds[buf][off]), kf[st], s[qc]);
+          dp[qc] = mma16(T{}, *reinterpret_cast<const uint4*>(&do_lds[buf][off]), vf[st], dp[qc]);
+        }
+      }
+      // P = exp2(S * qk_scale - LSE2), dS = P * (dP - Delta); register r of
+      // block qc is query q_first + 32 qc + 8 (r/4) + 4 g + r%4.
+      uint4 pp[4], dsp[4];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ql = 32 * qc + 8 * rq + 4 * g;
+          const float4 l4 = *reinterpret_cast<const float4*>(&lse_lds[buf][ql]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][ql]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            float p = fast_exp2(__builtin_fmaf(s[qc][r], qk_scale, -lv[e]));
+            if (need_mask) p = (key <= q_first + ql + e) ? p : 0.f;
+            s[qc][r] = p;
+            dp[qc][r] = p * (dp[qc][r] - dv4[e]);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          pp[2 * qc + h] = pack8(T{}, s[qc], h);
+          dsp[2 * qc + h] = pack8(T{}, dp[qc], h);
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q (contraction over the 64 queries).
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int off = (32 * db + n) * C::TROW + 16 * kk + 8 * g;
+          dv[db] = mma16(T{}, pp[kk], *reinterpret_cast<const uint4*>(&dot_lds[buf][off]), dv[db]);
+          dk[db] = mma16(T{}, dsp[kk], *reinterpret_cast<const uint4*>(&qt_lds[buf][off]), dk[db]);
+        }
+      }
+    }
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
+  float* dkh = dkg + head;
+  float* dvh = dvg + head;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = kw0 + 8 * (r / 4) + 4 * g + (r % 4);
+      if (kr < N) {
+        dkh[(size_t)kr * D + 32 * db + n] = dk[db][r] * dk_scale;
+        dvh[(size_t)kr * D + 32 * db + n] = dv[db][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ.  Workgroup = 4 waves x 32 queries; inner loop over 64-key blocks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct QG {
+  static constexpr int NW = 4, NT = 256, BM = NW * 32, BN = 64;
+  static constexpr int KROW = D + 8, TROW = BN + 8;
+  static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32;
+  static constexpr int KPT = BN * D / 8 / NT;
+  static_assert(KPT == 2 || KPT == 4, "staging packs 2 or 4 rows per thread");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
+    float* __restrict__ dqg, int N, int n_qblk, float qk_scale, float dq_scale, uint32_t qsign) {
+  using C = QG<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * C::KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::BN * C::KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][D * C::TROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
+  int bh, qblk;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* kh = kg + head;
+  const uint16_t* vh = vg + head;
+  const int q0 = qblk * C::BM;
+  const int qw0 = q0 + wave * 32;
+  const int query = qw0 + n;
+
+  uint4 qf[C::DS], dof[C::DS];
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (query < N) {
+      a = *reinterpret_cast<const uint4*>(qg + head + (size_t)query * D + 16 * s + 8 * g);
+      b = *reinterpret_cast<const uint4*>(dog + head + (size_t)query * D + 16 * s + 8 * g);
+      a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
+    }
+    qf[s] = a;
+    dof[s] = b;
+  }
+  const float lse2 = query < N ? lseg[(size_t)bh * N + query] * kLog2e : kPosInf;
+  const float dl = query < N ? deltag[(size_t)bh * N + query] : 0.f;
+
+  f32x16 dq[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dq[db] = f32x16{};
+
+  const int n_kv = (N + C::BN - 1) / C::BN;
+  int j_end = n_kv;
+  if (CAUSAL) j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / C::BN + 1);
+  int w_s1 = n_kv, w_s2 = n_kv;
+  const bool wave_live = qw0 < N;
+  if (CAUSAL && wave_live) causal_stages(qw0, min(qw0 + 32, N), C::BN, &w_s1, &w_s2);
+  const int full_blocks = N / C::BN;
+
+  const int sa = tid % (C::BN / C::KPT), sc = tid / (C::BN / C::KPT);
+  uint4 ks[C::KPT], vs[C::KPT];
+  auto load_block = [&](int j) {
+#pragma unroll
+    for (int e = 0; e < C::KPT; ++e) {
+      const int row = j * C::BN + C::KPT * sa + e;
+      uint4 a = make_uint4(0, 0, 0, 0), b = a;
+      if (row < N) {
+        a = *reinterpret_cast<const uint4*>(kh + (size_t)row * D + 8 * sc);
+        b = *reinterpret_cast<const uint4*>(vh + (size_t)row * D + 8 * sc);
+      }
+      ks[e] = a;
+      vs[e] = b;
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < C::KPT; ++e) {
+      const int r = C::KPT * sa + e;
+      *reinterpret_cast<uint4*>(&k_lds[buf][r * C::KROW + 8 * sc]) = ks[e];
+      *reinterpret_cast<uint4*>(&v_lds[buf][r * C::KROW + 8 * sc]) = vs[e];
+    }
+    store_transposed<C::KPT>(&kt_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), ks);
+  };
+
+  if (j_end > 0) {
+    load_block(0);
+    store_block(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < j_end; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < j_end;
+    if (more) load_block(j + 1);
+    const bool need_mask = (CAUSAL && j >= w_s1) || j >= full_blocks;
+    const bool active = wave_live && (!CAUSAL || j < w_s2);
+    if (active) {
+      f32x16 s[C::KB], dp[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < C::DS; ++st) {
+          const int off = (32 * kb + n) * C::KROW + 16 * st + 8 * g;
+          s[kb] = mma16(T{}, *reinterpret_cast<const uint4*>(&k_lds[buf][off]), qf[st], s[kb]);
+          dp[kb] = mma16(T{}, *reinterpret_cast<const uint4*>(&v_lds[buf][off]), dof[st], dp[kb]);
+        }
+      }
+      // Register r of key block kb is key j BN + 32 kb + 8(r/4) + 4g + r%4.
+      const int key_lim = CAUSAL ? min(query + 1, N) : N;
+      uint4 dsp[C::KB * 2];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[kb][r], qk_scale, -lse2));
+          if (need_mask) {
+            const int kr = j * C::BN + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
+            p = kr < key_lim ? p : 0.f;
+          }
+          dp[kb][r] = p * (dp[kb][r] - dl);
+        }
+        dsp[2 * kb] = pack8(T{}, dp[kb], 0);
+        dsp[2 * kb + 1] = pack8(T{}, dp[kb], 1);
+      }
+      // dQ^T += K^T dS^T (contraction over the 64 keys).
+#pragma unroll
+      for (int kk = 0; kk < C::KB * 2; ++kk) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int off = (32 * db + n) * C::TROW + 16 * kk + 8 * g;
+          dq[db] = mma16(T{}, *reinterpret_cast<const uint4*>(&kt_lds[buf][off]), dsp[kk], dq[db]);
+        }
+      }
+    }
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (query < N) {
+    float* row = dqg + head + (size_t)query * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x16& v = dq[db];
+        *reinterpret_cast<float4*>(row + 32 * db + 8 * rq + 4 * g) =
+            make_float4(v[4 * rq] * dq_scale, v[4 * rq + 1] * dq_scale, v[4 * rq + 2] * dq_scale,
+                        v[4 * rq + 3] * dq_scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+hipError_t run(const BwdArgs& a) {
+  const long long rows = (long long)a.BH * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  const long long g1 = (rows + RPB - 1) / RPB;
+  const int n_kblk = (a.N + KV<D>::BNK - 1) / KV<D>::BNK;
+  const int n_qblk = (a.N + QG<D>::BM - 1) / QG<D>::BM;
+  const long long g2 = (long long)n_kblk * a.BH, g3 = (long long)n_qblk * a.BH;
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float qk_scale = fabsf(a.scale) * kLog2eHost;
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  const auto* q = static_cast<const uint16_t*>(a.q);
+  const auto* k = static_cast<const uint16_t*>(a.k);
+  const auto* v = static_cast<const uint16_t*>(a.v);
+  const auto* o = static_cast<const uint16_t*>(a.o);
+  const auto* dout = static_cast<const uint16_t*>(a.dout);
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g1), dim3(256), 0, a.stream, o, dout, a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(256), 0, a.stream, q, k, v, dout,
+                     a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, fabsf(a.scale), qsign);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(256), 0, a.stream, q, k, v, dout,
+                     a.lse, a.delta, a.dq, a.N, n_qblk, qk_scale, a.scale, qsign);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? run<T, 64, true>(a) : run<T, 64, false>(a);
+  return a.causal ? run<T, 128, true>(a) : run<T, 128, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  if (a.dtype == 1) return dispatch<F16>(a);
+  if (a.dtype == 2) return dispatch<BF16>(a);
+  return hipErrorNotSupported;  // fp32 is rejected by the ABI before this point
+}
+
 }  // namespace fa
