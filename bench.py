@@ -1,0 +1,385 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X; prints ONE JSON line.
+
+A timed step is one training step of causal attention -- fa_fwd followed by
+fa_bwd (Delta, dK/dV, dQ) -- on the causal training-step workload
+(B=4, H=16, N=4096, d=128, bf16), inputs resident in HBM.  `value` is the
+credited attention TFLOP/s of that step: forward 4*B*H*N^2*d and backward
+10*B*H*N^2*d (five contractions), both halved for causal.
+
+The same run also times, as separate legs reported under "legs": the causal
+prefill forward (B2 H32 N8192 d128 bf16), the long causal forward and the
+naive three-kernel baseline (B1 H16 N16384 d64 bf16), the non-causal fp16
+sweep N=512..4096 (fused vs naive, with the byte models), and the fp32
+single-head forward.  `cpu_baseline` times the fp64 oracle on a sample of the
+step's heads on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s (bf16 fwd/bwd) at N=4k-16k; % of MFMA peak; HBM bytes"
+CSRC = os.path.join(ROOT, "io_aware_exact_03_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Cost model.  Flops: forward 4 N^2 d per head (two contractions), backward
+# 10 N^2 d (five distinct contractions), halved for causal.  Bytes: what each
+# path must move through HBM at least -- the fused path reads Q, K, V once
+# and writes O (plus the fp32 LSE); the naive path also writes S, reads S,
+# writes P and reads P ("Flash Attention -- five lessons converging into 80
+# lines", Lesson 1: 4 N^2 + 4 N d elements against 4 N d).
+# ---------------------------------------------------------------------------
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, H, N, d, causal):
+    f = 10.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def fused_fwd_bytes(B, H, N, d, e_in, lse=True):
+    """Q, K, V read + O written (e_in bytes each) [+ fp32 LSE written]."""
+    return B * H * (4 * N * d * e_in + (4 * N if lse else 0))
+
+
+def naive_fwd_bytes(B, H, N, d, e_in, e_ws, lse=True):
+    """The fused bytes plus S and P each written once and read once
+    (4 N^2 elements of the workspace type)."""
+    return B * H * 4 * N * N * e_ws + fused_fwd_bytes(B, H, N, d, e_in, lse)
+
+
+def sp_roundtrip_bytes(N, e_ws):
+    """The S + P round trips alone, per head: 4 N^2 elements."""
+    return 4 * N * N * e_ws
+
+
+def fused_bwd_bytes(B, H, N, d, e_in):
+    """The backward's compulsory traffic: Q, K, V, O, dO read once; LSE read
+    once; Delta written once and read once; dQ, dK, dV written in fp32."""
+    return B * H * (5 * N * d * e_in + 4 * N + 2 * 4 * N + 3 * 4 * N * d)
+
+
+def delta_bytes(w):
+    """The Delta preprocess reads O and dO and writes one fp32 per row."""
+    return w.B * w.H * w.N * (2 * w.d * 2 + 4)
+
+
+# Flops each kernel of the step executes as contractions (per launch):
+# forward S, PV; dK/dV pass S, dP, dV, dK; dQ pass S, dP, dQ.
+KERNEL_CONTRACTIONS = {"fa_fwd": 2, "bwd_delta": 0, "bwd_dkdv": 4, "bwd_dq": 3}
+
+
+def read_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_digest") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_reps(fn, reps: int, torch):
+    """Median and min milliseconds of fn() over reps, HIP events on the
+    current stream."""
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def cpu_baseline(w, q, k, v, do, target_s: float):
+    """The fp64 oracle (forward + backward) on a sample of the workload's
+    heads, one head per worker thread with single-threaded BLAS."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import fa_synth
+    import oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qq, kk, vv, gg = (fa_synth.to_f64(t[sl]) for t in (q, k, v, do))
+        oracle.attn_fwd(qq, kk, vv, w.scale, w.causal)
+        oracle.attn_bwd(qq, kk, vv, gg, w.scale, w.causal)
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        one(heads[0])
+        per_head = time.perf_counter() - t0
+        n = max(cores, min(len(heads), int(target_s * cores / max(per_head, 1e-3))))
+        n = min(len(heads), (n // cores) * cores or cores)
+        sample = heads[:n]
+        with cf.ThreadPoolExecutor(cores) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(one, sample))
+            wall = time.perf_counter() - t0
+    flops = (fwd_flops(1, 1, w.N, w.d, w.causal) + bwd_flops(1, 1, w.N, w.d, w.causal)) * len(sample)
+    return {
+        "value": flops / wall / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{len(sample)} of {len(heads)} heads of {w.name}, forward + backward, fp64 NumPy, one head "
+                   f"per thread with single-threaded BLAS; {wall:.1f} s wall; credited flops as on the GPU (the "
+                   f"oracle computes the full N x N before masking, twice the credited causal work)"),
+        "seconds": wall,
+        "heads": len(sample),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", type=int, default=1, help="also time the other workloads (1) or not (0)")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only (the attention kernels "
+              f"run per (batch, head) on a single MI355X; no multi-GPU path exists)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fa_synth
+    import io_aware_exact_03_amd as fa
+
+    fa._lib.load()
+    dev = torch.device("cuda:0")
+    digest = source_digest()
+
+    # ---------------- the timed step: causal training step ----------------
+    w = fa_synth.TRAIN_STEP
+    log(f"[bench] inputs {w.describe()}")
+    q, k, v, do = fa_synth.workload_inputs(w)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(qd)
+    f32 = dict(dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), **f32)
+    delta = torch.empty((w.B, w.H, w.N), **f32)
+    dq = torch.empty((w.B, w.H, w.N, w.d), **f32)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse)
+        for s in (1, 2, 3):
+            if ev is not None:
+                ev[s].record()
+            fa.bwd_stage(s, qd, kd, vd, o, dod, lse, w.scale, w.causal, delta, dq, dk, dv)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    names = ["fa_fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i, n in enumerate(names)}
+    step_flops = fwd_flops(w.B, w.H, w.N, w.d, w.causal) + bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kern_ms}")
+
+    # roofline of the dominant kernel of the step
+    dom = max(kern_ms, key=kern_ms.get)
+    unit_flops = 2.0 * w.B * w.H * w.N * w.N * w.d / (2 if w.causal else 1)  # one contraction
+    if KERNEL_CONTRACTIONS[dom] > 0:
+        achieved = KERNEL_CONTRACTIONS[dom] * unit_flops / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        byts = delta_bytes(w)
+        achieved = byts / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kern_ms[dom]
+    roof["traffic"] = read_traffic(dom, w.name, digest)
+
+    kernels = {}
+    for n_ in names:
+        c = KERNEL_CONTRACTIONS[n_]
+        entry = {"ms": kern_ms[n_]}
+        if c:
+            tf = c * unit_flops / (kern_ms[n_] * 1e-3) / 1e12
+            entry.update({"tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS})
+        else:
+            entry.update({"gbs": delta_bytes(w) / (kern_ms[n_] * 1e-3) / 1e9})
+        kernels[n_] = entry
+    fwd_tf = fwd_flops(w.B, w.H, w.N, w.d, w.causal) / (kern_ms["fa_fwd"] * 1e-3) / 1e12
+    bwd_ms = kern_ms["bwd_delta"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+    bwd_tf = bwd_flops(w.B, w.H, w.N, w.d, w.causal) / (bwd_ms * 1e-3) / 1e12
+    del o, lse, delta, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    legs = {}
+    if args.legs:
+        legs = run_legs(torch, fa, fa_synth, dev)
+
+    cpu = None
+    if args.cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle) ...")
+        cpu = cpu_baseline(w, q, k, v, do, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "seed": w.seed, "step": "fa_fwd + fa_bwd",
+                   "flops_per_step": step_flops},
+        "frac_mfma_peak": value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_tf,
+        "bwd_tflops": bwd_tf,
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "legs": legs,
+        "source_digest": digest,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_legs(torch, fa, fa_synth, dev):
+    legs = {}
+
+    # causal prefill forward and long causal forward (bf16)
+    for w in (fa_synth.CAUSAL_PREFILL, fa_synth.LONG_CAUSAL):
+        q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        ms, ms_min = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 20, torch)
+        tf = fwd_flops(w.B, w.H, w.N, w.d, w.causal) / (ms * 1e-3) / 1e12
+        alg_bytes = fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)
+        entry = {"fwd_ms": ms, "fwd_ms_min": ms_min, "fwd_tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS,
+                 "alg_bytes": alg_bytes}
+        if w.naive:
+            entry.update(naive_leg(torch, fa, w, q, k, v, dev, ms))
+        legs[w.name] = entry
+        log(f"[bench] {w.name}: {entry}")
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+    # non-causal fp16 sweep, fused vs naive, with the byte models
+    for w in fa_synth.NONCAUSAL_SWEEP:
+        q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        ms, _ = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 20, torch)
+        tf = fwd_flops(w.B, w.H, w.N, w.d, False) / (ms * 1e-3) / 1e12
+        entry = {"fwd_ms": ms, "fwd_tflops": tf, "alg_bytes": fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)}
+        entry.update(naive_leg(torch, fa, w, q, k, v, dev, ms))
+        legs[w.name] = entry
+        log(f"[bench] {w.name}: {entry}")
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+    # fp32 single head
+    w = fa_synth.SINGLE_HEAD_F32
+    q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+    o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+    ms, _ = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 50, torch)
+    entry = {"fwd_ms": ms, "fwd_gflops": fwd_flops(1, 1, w.N, w.d, False) / (ms * 1e-3) / 1e9}
+    entry.update(naive_leg(torch, fa, w, q, k, v, dev, ms))
+    legs[w.name] = entry
+    log(f"[bench] {w.name}: {entry}")
+    return legs
+
+
+def naive_leg(torch, fa, w, q, k, v, dev, fused_ms):
+    """Time the three-kernel path and report its byte model next to the
+    fused one: S and P each written once and read once (N^2 elements of the
+    workspace dtype), plus Q, K, V, O and LSE."""
+    ws_dtype = torch.float32 if w.dtype == "f32" else torch.float16
+    e_ws = 4 if w.dtype == "f32" else 2
+    e_in = 4 if w.dtype == "f32" else 2
+    s = torch.empty((w.B, w.H, w.N, w.N), dtype=ws_dtype, device=dev)
+    p = torch.empty_like(s)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s, p_ws=p)
+    ms, _ = time_reps(lambda: fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s, p_ws=p), 5, torch)
+    naive_bytes = naive_fwd_bytes(w.B, w.H, w.N, w.d, e_in, e_ws)
+    fused_bytes = fused_fwd_bytes(w.B, w.H, w.N, w.d, e_in)
+    del s, p, o, lse
+    torch.cuda.empty_cache()
+    return {"naive_ms": ms, "speedup_fused_over_naive": ms / fused_ms, "naive_model_bytes": naive_bytes,
+            "fused_model_bytes": fused_bytes, "model_byte_ratio": naive_bytes / fused_bytes,
+            "naive_model_gbs": naive_bytes / (ms * 1e-3) / 1e9}
+
+
+if __name__ == "__main__":
+    main()

@@ -101,6 +101,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * One launch of fa_bwd, for timing each kernel on its own: stage 1 writes
+ * Delta, stage 2 writes dK and dV (needs Delta), stage 3 writes dQ (needs
+ * Delta).  Calling stages 1, 2, 3 in order on one stream does exactly what
+ * fa_bwd does.  Same arguments and checks as fa_bwd; a stage outside 1..3
+ * -> FA_ERR_ARG.
+ */
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, float* delta_ws, float* dq, float* dk,
+                 float* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                 void* stream);
+
+/*
  * Naive three-kernel forward ("Flash Attention -- five lessons converging
  * into 80 lines", "Two implementations"; Algorithm 0 of the FlashAttention
  * paper review): kernel 1 writes S = scale * Q K^T for all N x N into

@@ -19,6 +19,7 @@ _ip = ctypes.POINTER(ctypes.c_int)
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_bwd_stage": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_naive_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_naive_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_strerror": (ctypes.c_char_p, [_i]),

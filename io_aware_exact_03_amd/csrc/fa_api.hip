@@ -95,9 +95,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(fa::launch_fwd(a));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-           float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
-           int dtype, void* stream) {
+static int bwd_common(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                      float scale, int causal, int dtype, void* stream) {
+  if (stage < 0 || stage > 3) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !dout || !lse || !delta_ws || !dq || !dk || !dv) return FA_ERR_ARG;
   const int st = check_shape(B, H, N, d, dtype, causal, scale);
   if (st != FA_OK) return st;
@@ -110,7 +111,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.delta = delta_ws; a.dq = dq; a.dk = dk; a.dv = dv;
   a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
-  return hip_status(fa::launch_bwd(a));
+  return hip_status(fa::launch_bwd(a, stage));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+           int dtype, void* stream) {
+  return bwd_common(0, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                 float scale, int causal, int dtype, void* stream) {
+  if (stage < 1) return FA_ERR_ARG;
+  return bwd_common(stage, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream);
 }
 
 int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* s_ws, void* p_ws, int B,

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-hipError_t run(const BwdArgs& a) {
+hipError_t run(const BwdArgs& a, int stage) {
   const long long rows = (long long)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
   const long long g1 = (rows + RPB - 1) / RPB;
@@ -452,29 +452,37 @@ hipError_t run(const BwdArgs& a) {
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* o = static_cast<const uint16_t*>(a.o);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g1), dim3(256), 0, a.stream, o, dout, a.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(256), 0, a.stream, q, k, v, dout,
-                     a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, fabsf(a.scale), qsign);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(256), 0, a.stream, q, k, v, dout,
-                     a.lse, a.delta, a.dq, a.N, n_qblk, qk_scale, a.scale, qsign);
-  return hipGetLastError();
+  if (stage == 0 || stage == 1) {
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g1), dim3(256), 0, a.stream, o, dout, a.delta, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage == 0 || stage == 2) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(256), 0, a.stream, q, k, v, dout,
+                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, fabsf(a.scale), qsign);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage == 0 || stage == 3) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(256), 0, a.stream, q, k, v, dout,
+                       a.lse, a.delta, a.dq, a.N, n_qblk, qk_scale, a.scale, qsign);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T>
-hipError_t dispatch(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? run<T, 64, true>(a) : run<T, 64, false>(a);
-  return a.causal ? run<T, 128, true>(a) : run<T, 128, false>(a);
+hipError_t dispatch(const BwdArgs& a, int stage) {
+  if (a.d == 64) return a.causal ? run<T, 64, true>(a, stage) : run<T, 64, false>(a, stage);
+  return a.causal ? run<T, 128, true>(a, stage) : run<T, 128, false>(a, stage);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.dtype == 1) return dispatch<F16>(a);
-  if (a.dtype == 2) return dispatch<BF16>(a);
+hipError_t launch_bwd(const BwdArgs& a, int stage) {
+  if (a.dtype == 1) return dispatch<F16>(a, stage);
+  if (a.dtype == 2) return dispatch<BF16>(a, stage);
   return hipErrorNotSupported;  // fp32 is rejected by the ABI before this point
 }
 

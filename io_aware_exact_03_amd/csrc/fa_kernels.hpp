@@ -61,7 +61,8 @@ struct NaiveArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// stage 0 = all three launches in order; 1 = Delta, 2 = dK/dV, 3 = dQ.
+hipError_t launch_bwd(const BwdArgs& a, int stage);
 hipError_t launch_naive(const NaiveArgs& a);
 
 }  // namespace fa

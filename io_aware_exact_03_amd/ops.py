@@ -61,6 +61,18 @@ def bwd(q, k, v, o, dout, lse, scale: float, causal: bool, delta=None, dq=None, 
     return dq, dk, dv, delta
 
 
+def bwd_stage(stage: int, q, k, v, o, dout, lse, scale: float, causal: bool, delta, dq, dk, dv):
+    """One of fa_bwd's three launches (1 Delta, 2 dK/dV, 3 dQ) into caller
+    buffers; stages 1, 2, 3 in order equal one bwd() call."""
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    st = _lib.load().fa_bwd_stage(int(stage), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype],
+                                  _stream(q))
+    _lib.check(st, f"fa_bwd_stage({stage})")
+
+
 def naive_workspace_bytes(B: int, H: int, N: int, dtype: torch.dtype) -> int:
     return int(_lib.load().fa_naive_workspace_bytes(B, H, N, DTYPE_CODES[dtype]))
 

@@ -116,3 +116,19 @@ def test_train_step_full_size():
     w = fa_synth.TRAIN_STEP
     run_and_check(w.B, w.H, w.N, w.d, w.dtype, w.causal, w.scale, w.seed, w.name,
                   heads=P.heads_to_check(w.B, w.H, 2, seed=w.seed))
+
+
+def test_stages_equal_full_backward():
+    """fa_bwd_stage 1, 2, 3 in order reproduce fa_bwd bitwise (the bench
+    times the stages one by one)."""
+    fa = _fa()
+    q, k, v, do = P.to_dev(*fa_synth.make_inputs(1, 3, 777, 128, "bf16", seed=9400, with_dout=True))
+    o, lse = fa.fwd(q, k, v, 0.088, True)
+    ref = fa.bwd(q, k, v, o, do, lse, 0.088, True)
+    outs = [torch.full_like(t, float("nan")) for t in ref]
+    dq, dk, dv, delta = outs
+    for s in (1, 2, 3):
+        fa.bwd_stage(s, q, k, v, o, do, lse, 0.088, True, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, outs):
+        assert torch.equal(a, b)
