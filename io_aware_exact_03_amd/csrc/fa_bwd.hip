@@ -36,33 +36,6 @@ namespace {
 
 constexpr float kPosInf = __builtin_huge_valf();
 
-// Position of row kappa of a 16-row group in a transposed LDS tile: bits 2
-// and 3 swapped, which puts the rows a lane half holds in accumulator
-// registers 0..7 at 8 consecutive positions (see the forward kernel).
-__device__ __forceinline__ int tpos(int kappa) {
-  return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
-
-// Write KPT rows x 8 columns (16-bit, one uint4 per row) transposed into 8
-// rows of `dst` (row stride `stride` elements) at column `pos`.
-template <int KPT>
-__device__ __forceinline__ void store_transposed(uint16_t* dst, int stride, int pos, const uint4 (&x)[KPT]) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(x);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int sh = (t & 1) ? 16 : 0;
-    uint16_t* p = dst + t * stride + pos;
-    if constexpr (KPT == 4) {
-      const uint32_t e0 = (w[0 + t / 2] >> sh) & 0xffffu, e1 = (w[4 + t / 2] >> sh) & 0xffffu;
-      const uint32_t e2 = (w[8 + t / 2] >> sh) & 0xffffu, e3 = (w[12 + t / 2] >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(p) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-    } else {
-      const uint32_t e0 = (w[0 + t / 2] >> sh) & 0xffffu, e1 = (w[4 + t / 2] >> sh) & 0xffffu;
-      *reinterpret_cast<uint32_t*>(p) = e0 | (e1 << 16);
-    }
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ uint4 pack8(T, const f32x16& v, int h) {
   return make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),

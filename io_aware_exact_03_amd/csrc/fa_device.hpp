@@ -94,26 +94,19 @@ __device__ __forceinline__ float halves_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// One online-softmax step for the KB 32x32 score blocks S^T of one 32-query
-// column block.  Lane l owns query n = l % 32; register r of block kb is key
+// Online softmax, split so the kernel can decide on the correction once per
+// wave.  Scores are the KB 32x32 blocks S^T of one 32-query column block:
+// lane l owns query n = l % 32; register r of block kb is key
 // key_base + 32*kb + 8*(r/4) + (r%4), where key_base already includes 4*g.
-//
-//   m_new = max(m, rowmax(S) * qk_scale)           (cross-half max)
-//   p     = exp2(S * qk_scale - m_new)              (in place in s)
-//   l     = alpha * l + sum(p),  alpha = exp2(m - m_new)
-//
-// l is this lane's partial sum over its own keys: alpha is the same on both
-// halves, so the halves are added once, at the end.  qk_scale >= 0 (a
-// negative scale is folded into the sign of Q), so max(S) * qk_scale is
-// the max of the scaled scores.  MASKED keeps only keys < key_lim (the
-// causal limit query+1 and the sequence end); masked p are exactly 0 even
-// when qk_scale is 0.  A row with no key yet keeps m = -inf and uses 0 in
-// place of m_new, so -inf - (-inf) never occurs.
-// Returns alpha for the accumulator correction.
+// qk_scale >= 0 (a negative scale is folded into the sign of Q), so the max
+// of the raw scores times qk_scale is the max of the scaled scores.  MASKED
+// keeps only keys < key_lim (the causal limit query+1 and the sequence end).
 // ---------------------------------------------------------------------------
+
+// Row max of the scaled scores of this block (same on both lane halves);
+// -inf when the row has no visible key here.
 template <int KB, bool MASKED>
-__device__ __forceinline__ float softmax_step(f32x16 (&s)[KB], float& m, float& l, float qk_scale,
-                                              int key_base, int key_lim) {
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[KB], float qk_scale, int key_base, int key_lim) {
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -128,16 +121,19 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[KB], float& m, float& 
     }
   }
   mx = halves_max(mx);
-  const float mt = (mx == kNegInf) ? kNegInf : mx * qk_scale;
-  const float m_new = fmaxf(m, mt);
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = fast_exp2(m - m_use);
+  return (mx == kNegInf) ? kNegInf : mx * qk_scale;
+}
+
+// p = exp2(S * qk_scale - m) in place; masked p are exactly 0 (also when
+// qk_scale is 0).  Returns this lane's sum of p.
+template <int KB, bool MASKED>
+__device__ __forceinline__ float tile_exp(f32x16 (&s)[KB], float qk_scale, float m, int key_base, int key_lim) {
   float sum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(__builtin_fmaf(s[kb][r], qk_scale, -m_use));
+      float p = fast_exp2(__builtin_fmaf(s[kb][r], qk_scale, -m));
       if constexpr (MASKED) {
         const int key = key_base + 32 * kb + 8 * (r / 4) + (r % 4);
         p = key < key_lim ? p : 0.f;
@@ -146,9 +142,69 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[KB], float& m, float& 
       sum += p;
     }
   }
-  l = l * alpha + sum;
+  return sum;
+}
+
+// Running-max bookkeeping with a tolerance.  The reference for the exponent
+// (m) is raised only when a block's max exceeds it by more than kMaxSlack
+// (log2 units); until then the weights exp2(t - m) may reach 2^kMaxSlack,
+// which fp32 accumulators and 16-bit P represent with the same relative
+// precision.  Because the accumulator, the row sum and the final LSE all
+// use the same m, the result is the same exact softmax: only the points at
+// which the accumulator is rescaled change, and a wave skips the rescale
+// (a multiply over the whole accumulator) whenever no lane needs it.
+constexpr float kMaxSlack = 8.f;
+
+// Returns true (wave-uniform) when some lane of the wave must rescale; then
+// *alpha holds this lane's factor (1 for lanes that keep their m) and m, l
+// are updated.  m = -inf means "no visible key yet".
+__device__ __forceinline__ bool raise_max(float mt, float& m, float& l, float* alpha) {
+  const bool grow = mt > m + kMaxSlack;  // false while mt is -inf
+  if (__builtin_amdgcn_ballot_w64(grow) == 0) return false;
+  const float m_new = grow ? mt : m;
+  *alpha = grow ? fast_exp2(m - m_new) : 1.f;  // m = -inf gives 0
+  l *= *alpha;
   m = m_new;
-  return alpha;
+  return true;
+}
+
+
+// ---------------------------------------------------------------------------
+// Transposed LDS tiles.  A 16-bit tile that feeds an MFMA operand with the
+// row index as contraction index is stored transposed (row index
+// contiguous).  Inside every 16-row group, row kappa sits at position
+// tpos(kappa) = kappa with bits 2 and 3 swapped: a 32x32 accumulator gives
+// lane half g the rows {4g..4g+3, 8+4g..8+4g+3} of each 16-row group in
+// registers 0..7, and tpos puts exactly those rows at positions 8g..8g+7,
+// so one 16-byte LDS read returns a lane's eight elements in register order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tpos(int kappa) {
+  return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
+}
+
+// Write KPT consecutive rows x 8 columns (16-bit, one uint4 per row, rows
+// starting at a multiple of KPT) transposed: column t goes to row t of
+// `dst` (row stride `stride` elements) at position `pos` = tpos(first row).
+// One v_perm_b32 builds each output dword from two input dwords.
+template <int KPT>
+__device__ __forceinline__ void store_transposed(uint16_t* dst, int stride, int pos, const uint4 (&x)[KPT]) {
+  static_assert(KPT == 2 || KPT == 4, "2 or 4 rows per thread");
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(x);  // w[4*row + i]: columns 2i, 2i+1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sel = h ? 0x07060302u : 0x05040100u;  // high or low halves of the two words
+      uint16_t* p = dst + (2 * i + h) * stride + pos;
+      const uint32_t a = __builtin_amdgcn_perm(w[4 + i], w[i], sel);
+      if constexpr (KPT == 4) {
+        const uint32_t b = __builtin_amdgcn_perm(w[12 + i], w[8 + i], sel);
+        *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+      } else {
+        *reinterpret_cast<uint32_t*>(p) = a;
+      }
+    }
+  }
 }
 
 }  // namespace fa

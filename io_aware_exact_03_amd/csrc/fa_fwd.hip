@@ -35,15 +35,6 @@
 
 namespace fa {
 
-// Position of key kappa (within a BN block) in a V^T row: bits 2 and 3 of the
-// key index swapped.  Inside a 16-key group, lane half g holds keys
-// {4g..4g+3, 8+4g..8+4g+3} in its accumulator registers 0..7; the swap puts
-// exactly those keys at positions 8g..8g+7, so one 16-byte LDS read gives a
-// lane its 8 V^T elements in accumulator order.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
-
 // ===========================================================================
 // 16-bit (bf16 / fp16) forward
 // ===========================================================================
@@ -153,22 +144,8 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(&k_lds[buf][row * C::KROW + col]) = kst[i];
     }
-    // Transpose KPT keys x 8 d of V into 8 rows of V^T.
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(vst);  // w[4*e + t/2]
-    const int pos = vt_pos(C::KPT * va);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int sh = (t & 1) ? 16 : 0;
-      uint16_t* dst = &v_lds[buf][(8 * vdc + t) * C::VROW + pos];
-      if constexpr (C::KPT == 4) {
-        const uint32_t e0 = (w[0 * 4 + t / 2] >> sh) & 0xffffu, e1 = (w[1 * 4 + t / 2] >> sh) & 0xffffu;
-        const uint32_t e2 = (w[2 * 4 + t / 2] >> sh) & 0xffffu, e3 = (w[3 * 4 + t / 2] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-      } else {
-        const uint32_t e0 = (w[0 * 4 + t / 2] >> sh) & 0xffffu, e1 = (w[1 * 4 + t / 2] >> sh) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(dst) = e0 | (e1 << 16);
-      }
-    }
+    // V^T: KPT keys x 8 d of V become 8 rows of V^T (keys in tpos order).
+    store_transposed<C::KPT>(&v_lds[buf][8 * vdc * C::VROW], C::VROW, tpos(C::KPT * va), vst);
   };
 
   // ---- running state --------------------------------------------------
@@ -220,13 +197,16 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
         const int query = qw0 + 32 * qb + n;
         const int key_base = j * BN + 4 * g;
         const int key_lim = CAUSAL ? min(query + 1, N) : N;
+        const float mt = need_mask ? tile_max<C::KB, true>(s[qb], qk_scale, key_base, key_lim)
+                                   : tile_max<C::KB, false>(s[qb], qk_scale, key_base, key_lim);
         float alpha;
-        if (need_mask)
-          alpha = softmax_step<C::KB, true>(s[qb], m_run[qb], l_run[qb], qk_scale, key_base, key_lim);
-        else
-          alpha = softmax_step<C::KB, false>(s[qb], m_run[qb], l_run[qb], qk_scale, key_base, key_lim);
+        if (raise_max(mt, m_run[qb], l_run[qb], &alpha)) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
+          for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
+        }
+        const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
+        l_run[qb] += need_mask ? tile_exp<C::KB, true>(s[qb], qk_scale, m_use, key_base, key_lim)
+                               : tile_exp<C::KB, false>(s[qb], qk_scale, m_use, key_base, key_lim);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
@@ -388,13 +368,16 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
       }
       const int key_base = j * BN + 4 * g;
       const int key_lim = CAUSAL ? min(query + 1, N) : N;
+      const float mt = need_mask ? tile_max<C::KB, true>(s, qk_scale, key_base, key_lim)
+                                 : tile_max<C::KB, false>(s, qk_scale, key_base, key_lim);
       float alpha;
-      if (need_mask)
-        alpha = softmax_step<C::KB, true>(s, m_run, l_run, qk_scale, key_base, key_lim);
-      else
-        alpha = softmax_step<C::KB, false>(s, m_run, l_run, qk_scale, key_base, key_lim);
+      if (raise_max(mt, m_run, l_run, &alpha)) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      l_run += need_mask ? tile_exp<C::KB, true>(s, qk_scale, m_use, key_base, key_lim)
+                         : tile_exp<C::KB, false>(s, qk_scale, m_use, key_base, key_lim);
       // O^T += V^T P^T: k-step r of key block kb uses key 32 kb + 8(r/4) + 4g + r%4
       // on both operands (the accumulator register r and the V row read).
 #pragma unroll
@@ -433,9 +416,17 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 // ===========================================================================
 namespace {
 
+// Tile per head dim: 8 waves x 32 queries (two waves per SIMD, so one wave's
+// softmax overlaps the other's matrix products), 64 keys per block for
+// d = 128 and 128 for d = 64.  Must agree with fwd_tile() in fa_plan.hpp.
+template <int D>
+struct Tile16 {
+  static constexpr int BN = D == 128 ? 64 : 128, NW = 8, QB = 1;
+};
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const FwdArgs& a) {
-  constexpr int BN = 64, NW = 4, QB = 2;
+  constexpr int BN = Tile16<D>::BN, NW = Tile16<D>::NW, QB = Tile16<D>::QB;
   using C = Fwd16<T, D, BN, NW, QB, CAUSAL>;
   const int n_qblk = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)n_qblk * a.BH;

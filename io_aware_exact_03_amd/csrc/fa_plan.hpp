@@ -62,7 +62,7 @@ struct FwdTile {
 
 FA_HD FwdTile fwd_tile(int d, bool is_f32) {
   if (is_f32) return FwdTile{128, 64, 4};
-  return d == 128 ? FwdTile{256, 64, 4} : FwdTile{256, 64, 4};
+  return d == 128 ? FwdTile{256, 64, 8} : FwdTile{256, 128, 8};
 }
 
 }  // namespace fa
