@@ -35,6 +35,8 @@ int check_shape(int B, int H, int N, int d, int dtype, int causal, float scale) 
   // bytes of one [B,H,N,d] tensor must fit in int64 (and then some)
   const long double bytes = (long double)bh * N * d * elem_bytes(dtype);
   if (bytes > (long double)(1LL << 62)) return FA_ERR_ARG;
+  // the kernels address one (batch, head) slice with 32-bit buffer offsets
+  if ((long long)N * d * elem_bytes(dtype) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

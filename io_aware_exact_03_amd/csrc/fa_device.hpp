@@ -94,6 +94,28 @@ __device__ __forceinline__ float halves_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
+// Buffer loads.  A buffer resource covers one (batch, head) slice of
+// `bytes` bytes; the hardware range check returns zeros for any read at or
+// past the end, which is how ragged tails are zero-filled without branches.
+// Offsets are 32-bit: the host rejects heads of 2 GiB or more.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float4 load16f(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float load4f(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
 // Online softmax, split so the kernel can decide on the correction once per
 // wave.  Scores are the KB 32x32 blocks S^T of one 32-query column block:
 // lane l owns query n = l % 32; register r of block kb is key
@@ -128,7 +150,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[KB], float qk_scale,
 // qk_scale is 0).  Returns this lane's sum of p.
 template <int KB, bool MASKED>
 __device__ __forceinline__ float tile_exp(f32x16 (&s)[KB], float qk_scale, float m, int key_base, int key_lim) {
-  float sum = 0.f;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};  // four chains instead of one long dependent one
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -139,10 +161,10 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[KB], float qk_scale, float
         p = key < key_lim ? p : 0.f;
       }
       s[kb][r] = p;
-      sum += p;
+      sum[r % 4] += p;
     }
   }
-  return sum;
+  return (sum[0] + sum[1]) + (sum[2] + sum[3]);
 }
 
 // Running-max bookkeeping with a tolerance.  The reference for the exponent

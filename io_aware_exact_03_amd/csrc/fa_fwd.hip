@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_plan.hpp"
 #include "fa_kernels.hpp"
@@ -76,41 +78,50 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
   int bh, qblk;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* qh = qg + head;
-  const uint16_t* kh = kg + head;
-  const uint16_t* vh = vg + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
+  const rsrc_t krs = make_rsrc(kg + head, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
 
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * C::QW;  // first query of this wave
 
   // ---- Q fragments, held in registers for the whole kernel --------------
   // B operand of S^T = K Q^T: lane supplies Q[query n][16 s + 8 g + 0..7].
+  // Rows past N read as zeros.
   uint4 qf[QB][C::DS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + 32 * qb + n;
+    const uint32_t row = qw0 + 32 * qb + n;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < N) x = *reinterpret_cast<const uint4*>(qh + (size_t)row * D + 16 * s + 8 * g);
+      uint4 x = load16(qrs, (row * D + 16 * s + 8 * g) * 2);
       x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
       qf[qb][s] = x;
     }
   }
 
-  // ---- key-block range -----------------------------------------------
+  // ---- key-block plan ---------------------------------------------------
+  // Blocks [0, j_unm) hold only keys visible to every query of the
+  // workgroup and lie before the sequence tail: no mask at all (the pages'
+  // unmasked stage).  Blocks [j_unm, j_end) straddle the diagonal or hold
+  // the tail: masked per key; each wave also skips blocks wholly in its
+  // future.  Blocks from j_end on are never read.
   const int n_kv = (N + BN - 1) / BN;
-  int j_end = n_kv;
+  const int full_blocks = N / BN;
+  int j_end = n_kv, j_unm = full_blocks;
   if (CAUSAL) {
-    const int last_row = min(q0 + C::BM, N) - 1;
-    j_end = min(n_kv, last_row / BN + 1);
+    j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / BN + 1);
+    int s1, s2;
+    causal_stages(q0, min(q0 + C::BM, N), BN, &s1, &s2);
+    j_unm = min(s1, full_blocks);
   }
-  // This wave's causal plan: blocks < w_s1 need no causal mask, blocks in
-  // [w_s1, w_s2) are masked, later ones hold no visible key for the wave.
-  int w_s1 = n_kv, w_s2 = n_kv;
+  int w_s2 = n_kv;
   const bool wave_live = qw0 < N;
-  if (CAUSAL && wave_live) causal_stages(qw0, min(qw0 + C::QW, N), BN, &w_s1, &w_s2);
-  const int full_blocks = N / BN;  // blocks with no sequence-end tail
+  if (CAUSAL && wave_live) {
+    int w_s1;
+    causal_stages(qw0, min(qw0 + C::QW, N), BN, &w_s1, &w_s2);
+  }
 
   // ---- global -> register staging of one K/V block -----------------------
   uint4 kst[C::KLD];
@@ -119,24 +130,19 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
   const int vdc = tid / (BN / C::KPT);  // d chunk (8 elements) of this thread
 
   auto load_block = [&](int j) {
-    const int key0 = j * BN;
+    const uint32_t key0 = j * BN;
 #pragma unroll
     for (int i = 0; i < C::KLD; ++i) {
       const int c = tid + i * C::NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (key0 + row < N) x = *reinterpret_cast<const uint4*>(kh + (size_t)(key0 + row) * D + col);
-      kst[i] = x;
+      const uint32_t row = key0 + c / (D / 8), col = (c % (D / 8)) * 8;
+      kst[i] = load16(krs, (row * D + col) * 2);
     }
 #pragma unroll
     for (int e = 0; e < C::KPT; ++e) {
-      const int row = key0 + C::KPT * va + e;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < N) x = *reinterpret_cast<const uint4*>(vh + (size_t)row * D + 8 * vdc);
-      vst[e] = x;
+      const uint32_t row = key0 + C::KPT * va + e;
+      vst[e] = load16(vrs, (row * D + 8 * vdc) * 2);
     }
   };
-
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::KLD; ++i) {
@@ -159,78 +165,80 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     for (int db = 0; db < C::DB; ++db) oacc[qb][db] = f32x16{};
   }
 
+  // One K/V block on this wave's queries.  MASKED is a compile-time choice
+  // so the unmasked stage carries no per-key compare at all.
+  auto tile = [&](int j, int buf, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // S^T = K_j Q^T  (keys x queries), fp32 accumulate.
+    f32x16 s[QB][C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+      for (int st = 0; st < C::DS; ++st) {
+        const uint4 a =
+            *reinterpret_cast<const uint4*>(&k_lds[buf][(32 * kb + n) * C::KROW + 16 * st + 8 * g]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mma16(T{}, a, qf[qb][st], st == 0 ? f32x16{} : s[qb][kb]);
+      }
+    }
+    // Online softmax, then P^T packed to 16-bit as the B operand.
+    uint4 pp[QB][C::KB * 2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int query = qw0 + 32 * qb + n;
+      const int key_base = j * BN + 4 * g;
+      const int key_lim = CAUSAL ? min(query + 1, N) : N;
+      const float mt = tile_max<C::KB, MASKED>(s[qb], qk_scale, key_base, key_lim);
+      float alpha;
+      if (raise_max(mt, m_run[qb], l_run[qb], &alpha)) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
+      }
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
+      l_run[qb] += tile_exp<C::KB, MASKED>(s[qb], qk_scale, m_use, key_base, key_lim);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x16& v = s[qb][kb];
+          pp[qb][2 * kb + h] = make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
+                                          pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
+        }
+      }
+    }
+    // O^T += V_j^T P^T  (d x queries), accumulator as C operand.
+#pragma unroll
+    for (int kk = 0; kk < C::KB * 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const uint4 a =
+            *reinterpret_cast<const uint4*>(&v_lds[buf][(32 * db + n) * C::VROW + 16 * kk + 8 * g]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mma16(T{}, a, pp[qb][kk], oacc[qb][db]);
+      }
+    }
+  };
+
   if (j_end > 0) {
     load_block(0);
     store_block(0);
   }
   __syncthreads();
 
-  for (int j = 0; j < j_end; ++j) {
+  int j = 0;
+  for (; j < j_unm; ++j) {  // unmasked stage: every wave, every key visible
     const int buf = j & 1;
     const bool more = j + 1 < j_end;
     if (more) load_block(j + 1);
-
-    const bool need_mask = (CAUSAL && j >= w_s1) || j >= full_blocks;
-    const bool active = wave_live && (!CAUSAL || j < w_s2);
-    if (active) {
-      // S^T = K_j Q^T  (keys x queries), fp32 accumulate.
-      f32x16 s[QB][C::KB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int st = 0; st < C::DS; ++st) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(&k_lds[buf][(32 * kb + n) * C::KROW + 16 * st + 8 * g]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mma16(T{}, a, qf[qb][st], s[qb][kb]);
-        }
-      }
-
-      // Online softmax, then P^T packed to 16-bit as the B operand.
-      uint4 pp[QB][C::KB * 2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int query = qw0 + 32 * qb + n;
-        const int key_base = j * BN + 4 * g;
-        const int key_lim = CAUSAL ? min(query + 1, N) : N;
-        const float mt = need_mask ? tile_max<C::KB, true>(s[qb], qk_scale, key_base, key_lim)
-                                   : tile_max<C::KB, false>(s[qb], qk_scale, key_base, key_lim);
-        float alpha;
-        if (raise_max(mt, m_run[qb], l_run[qb], &alpha)) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
-        }
-        const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
-        l_run[qb] += need_mask ? tile_exp<C::KB, true>(s[qb], qk_scale, m_use, key_base, key_lim)
-                               : tile_exp<C::KB, false>(s[qb], qk_scale, m_use, key_base, key_lim);
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const f32x16& v = s[qb][kb];
-            pp[qb][2 * kb + h] = make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
-                                            pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
-          }
-        }
-      }
-
-      // O^T += V_j^T P^T  (d x queries), accumulator as C operand.
-#pragma unroll
-      for (int kk = 0; kk < C::KB * 2; ++kk) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(&v_lds[buf][(32 * db + n) * C::VROW + 16 * kk + 8 * g]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mma16(T{}, a, pp[qb][kk], oacc[qb][db]);
-        }
-      }
-    }
-
+    tile(j, buf, std::false_type{});
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+  for (; j < j_end; ++j) {  // masked stage: diagonal blocks and the sequence tail
+    const int buf = j & 1;
+    const bool more = j + 1 < j_end;
+    if (more) load_block(j + 1);
+    if (wave_live && (!CAUSAL || j < w_s2)) tile(j, buf, std::true_type{});
     if (more) store_block(buf ^ 1);
     __syncthreads();
   }
@@ -292,40 +300,43 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   int bh, qblk;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const float* qh = qg + head;
-  const float* kh = kg + head;
-  const float* vh = vg + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 4;
+  const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
+  const rsrc_t krs = make_rsrc(kg + head, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * 32;
   const int query = qw0 + n;
 
-  // B operand of S^T: lane supplies Q[query][2 s + g].
+  // B operand of S^T: lane supplies Q[query][2 s + g] (zeros past N).
   float qf[D / 2];
 #pragma unroll
-  for (int s = 0; s < D / 2; ++s) qf[s] = (query < N) ? qh[(size_t)query * D + 2 * s + g] * qsign : 0.f;
+  for (int s = 0; s < D / 2; ++s) qf[s] = load4f(qrs, ((uint32_t)query * D + 2 * s + g) * 4) * qsign;
 
   const int n_kv = (N + BN - 1) / BN;
-  int j_end = n_kv;
-  if (CAUSAL) j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / BN + 1);
-  int w_s1 = n_kv, w_s2 = n_kv;
-  const bool wave_live = qw0 < N;
-  if (CAUSAL && wave_live) causal_stages(qw0, min(qw0 + 32, N), BN, &w_s1, &w_s2);
   const int full_blocks = N / BN;
+  int j_end = n_kv, j_unm = full_blocks;
+  if (CAUSAL) {
+    j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / BN + 1);
+    int s1, s2;
+    causal_stages(q0, min(q0 + C::BM, N), BN, &s1, &s2);
+    j_unm = min(s1, full_blocks);
+  }
+  int w_s2 = n_kv;
+  const bool wave_live = qw0 < N;
+  if (CAUSAL && wave_live) {
+    int w_s1;
+    causal_stages(qw0, min(qw0 + 32, N), BN, &w_s1, &w_s2);
+  }
 
   float4 kst[C::LD], vst[C::LD];
   auto load_block = [&](int j) {
 #pragma unroll
     for (int i = 0; i < C::LD; ++i) {
       const int c = tid + i * C::NT;
-      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
-      const int key = j * BN + row;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (key < N) {
-        a = *reinterpret_cast<const float4*>(kh + (size_t)key * D + col);
-        b = *reinterpret_cast<const float4*>(vh + (size_t)key * D + col);
-      }
-      kst[i] = a;
-      vst[i] = b;
+      const uint32_t row = j * BN + c / (D / 4), col = (c % (D / 4)) * 4;
+      kst[i] = load16f(krs, (row * D + col) * 4);
+      vst[i] = load16f(vrs, (row * D + col) * 4);
     }
   };
   auto store_block = [&](int buf) {
@@ -345,52 +356,59 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
+  auto tile = [&](int j, int buf, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16 s[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 2; ++st)
+        s[kb] = mma32(k_lds[buf][(32 * kb + n) * C::KROW + 2 * st + g], qf[st], s[kb]);
+    }
+    const int key_base = j * BN + 4 * g;
+    const int key_lim = CAUSAL ? min(query + 1, N) : N;
+    const float mt = tile_max<C::KB, MASKED>(s, qk_scale, key_base, key_lim);
+    float alpha;
+    if (raise_max(mt, m_run, l_run, &alpha)) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    l_run += tile_exp<C::KB, MASKED>(s, qk_scale, m_use, key_base, key_lim);
+    // O^T += V^T P^T: k-step r of key block kb uses key 32 kb + 8(r/4) + 4g + r%4
+    // on both operands (the accumulator register r and the V row read).
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          oacc[db] = mma32(v_lds[buf][key * C::VROW + 32 * db + n], s[kb][r], oacc[db]);
+      }
+    }
+  };
+
   if (j_end > 0) {
     load_block(0);
     store_block(0);
   }
   __syncthreads();
-
-  for (int j = 0; j < j_end; ++j) {
+  int j = 0;
+  for (; j < j_unm; ++j) {
     const int buf = j & 1;
     const bool more = j + 1 < j_end;
     if (more) load_block(j + 1);
-    const bool need_mask = (CAUSAL && j >= w_s1) || j >= full_blocks;
-    const bool active = wave_live && (!CAUSAL || j < w_s2);
-    if (active) {
-      f32x16 s[C::KB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < D / 2; ++st)
-          s[kb] = mma32(k_lds[buf][(32 * kb + n) * C::KROW + 2 * st + g], qf[st], s[kb]);
-      }
-      const int key_base = j * BN + 4 * g;
-      const int key_lim = CAUSAL ? min(query + 1, N) : N;
-      const float mt = need_mask ? tile_max<C::KB, true>(s, qk_scale, key_base, key_lim)
-                                 : tile_max<C::KB, false>(s, qk_scale, key_base, key_lim);
-      float alpha;
-      if (raise_max(mt, m_run, l_run, &alpha)) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-      l_run += need_mask ? tile_exp<C::KB, true>(s, qk_scale, m_use, key_base, key_lim)
-                         : tile_exp<C::KB, false>(s, qk_scale, m_use, key_base, key_lim);
-      // O^T += V^T P^T: k-step r of key block kb uses key 32 kb + 8(r/4) + 4g + r%4
-      // on both operands (the accumulator register r and the V row read).
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-            oacc[db] = mma32(v_lds[buf][key * C::VROW + 32 * db + n], s[kb][r], oacc[db]);
-        }
-      }
-    }
+    tile(j, buf, std::false_type{});
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+  for (; j < j_end; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < j_end;
+    if (more) load_block(j + 1);
+    if (wave_live && (!CAUSAL || j < w_s2)) tile(j, buf, std::true_type{});
     if (more) store_block(buf ^ 1);
     __syncthreads();
   }
