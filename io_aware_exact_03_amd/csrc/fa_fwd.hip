@@ -21,9 +21,18 @@
 //   needs V with keys contiguous per lane, so V is stored transposed in LDS,
 //   with the keys of each 16-key group permuted (bits 2 and 3 of the key
 //   index swapped) to match the accumulator's key order.
-// * K (row-major, 16-byte row padding) and V^T (padded rows) are
-//   double-buffered in LDS; the next block's global loads are in flight
-//   while the current block computes; one barrier per block.
+// * K (row-major, 16-byte row padding) and V^T (padded rows) sit in three
+//   LDS buffers: the block being consumed, the next one (whose first
+//   S product starts inside the current block's last step), and the one
+//   after, whose global loads are in flight meanwhile; one barrier per block.
+// * Software pipeline inside each wave, per 32-key sub-block u: the S^T
+//   product of sub-block u+1 is issued in chunks interleaved with the
+//   exponentials of sub-block u, and the PV product of u is interleaved with
+//   the row max of u+1, so the matrix cores and the vector/transcendental
+//   units overlap within one wave; eight waves (two per SIMD) cover the rest.
+// * The reference max is raised lazily (only when a sub-block's max exceeds
+//   it by more than a fixed slack), so the O rescale is rare; exact, since
+//   O, l and the LSE all use the same reference.
 // * Workgroups are renumbered so each XCD (own L2) works on whole heads,
 //   heaviest causal query blocks first.
 #include <hip/hip_runtime.h>
@@ -66,8 +75,12 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, float qk_scale,
     uint32_t qsign) {
   using C = Fwd16<T, D, BN, NW, QB, CAUSAL>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::LDS_K];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::LDS_V];
+  static_assert(QB == 1, "one 32-query block per wave");
+  constexpr int KB = C::KB, DB = C::DB, DS = C::DS;
+  // Three K/V buffers: iteration j reads K_{j+1} and V_j while block j+2 is
+  // staged into the third.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][C::LDS_K];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[3][C::LDS_V];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,28 +98,24 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
 
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * C::QW;  // first query of this wave
+  const int query = qw0 + n;          // this lane's query
 
   // ---- Q fragments, held in registers for the whole kernel --------------
-  // B operand of S^T = K Q^T: lane supplies Q[query n][16 s + 8 g + 0..7].
-  // Rows past N read as zeros.
-  uint4 qf[QB][C::DS];
+  // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
+  // rows past N read as zeros.
+  uint4 qf[DS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint32_t row = qw0 + 32 * qb + n;
-#pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
-      uint4 x = load16(qrs, (row * D + 16 * s + 8 * g) * 2);
-      x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
-      qf[qb][s] = x;
-    }
+  for (int s = 0; s < DS; ++s) {
+    uint4 x = load16(qrs, ((uint32_t)query * D + 16 * s + 8 * g) * 2);
+    x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
+    qf[s] = x;
   }
 
   // ---- key-block plan ---------------------------------------------------
   // Blocks [0, j_unm) hold only keys visible to every query of the
-  // workgroup and lie before the sequence tail: no mask at all (the pages'
+  // workgroup and lie before the sequence tail: no mask (the pages'
   // unmasked stage).  Blocks [j_unm, j_end) straddle the diagonal or hold
-  // the tail: masked per key; each wave also skips blocks wholly in its
-  // future.  Blocks from j_end on are never read.
+  // the tail and are masked per key.  Blocks from j_end on are never read.
   const int n_kv = (N + BN - 1) / BN;
   const int full_blocks = N / BN;
   int j_end = n_kv, j_unm = full_blocks;
@@ -116,19 +125,13 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     causal_stages(q0, min(q0 + C::BM, N), BN, &s1, &s2);
     j_unm = min(s1, full_blocks);
   }
-  int w_s2 = n_kv;
-  const bool wave_live = qw0 < N;
-  if (CAUSAL && wave_live) {
-    int w_s1;
-    causal_stages(qw0, min(qw0 + C::QW, N), BN, &w_s1, &w_s2);
-  }
+  const int key_lim = CAUSAL ? min(query + 1, N) : N;
 
-  // ---- global -> register staging of one K/V block -----------------------
+  // ---- global -> register -> LDS staging of one K/V block -----------------
   uint4 kst[C::KLD];
   uint4 vst[C::KPT];
   const int va = tid % (BN / C::KPT);   // key group of this thread
   const int vdc = tid / (BN / C::KPT);  // d chunk (8 elements) of this thread
-
   auto load_block = [&](int j) {
     const uint32_t key0 = j * BN;
 #pragma unroll
@@ -154,115 +157,222 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     store_transposed<C::KPT>(&v_lds[buf][8 * vdc * C::VROW], C::VROW, tpos(C::KPT * va), vst);
   };
 
-  // ---- running state --------------------------------------------------
-  f32x16 oacc[QB][C::DB];
-  float m_run[QB], l_run[QB];
+  // ---- pieces of one 32-key sub-block --------------------------------------
+  // A K/V tile of BN keys holds SUB = BN/32 sub-blocks; sub-block u is
+  // sub-block u % SUB of tile u / SUB.  The softmax pipeline runs per
+  // sub-block (two 16-register score sets in flight); barriers and staging
+  // run per tile.
+  constexpr int SUB = BN / 32;
+  // S^T = K Q^T for sub-block `sb` of tile buffer `buf` (32 keys x 32 queries).
+  auto s_gemm = [&](int buf, int sb, f32x16 (&s)[1]) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[qb][db] = f32x16{};
-  }
-
-  // One K/V block on this wave's queries.  MASKED is a compile-time choice
-  // so the unmasked stage carries no per-key compare at all.
-  auto tile = [&](int j, int buf, auto masked) {
+    for (int st = 0; st < DS; ++st) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[buf][(32 * sb + n) * C::KROW + 16 * st + 8 * g]);
+      s[0] = mma16(T{}, a, qf[st], st == 0 ? f32x16{} : s[0]);
+    }
+  };
+  // p = exp2(S * qk_scale - m) packed to 16-bit (the B operand of the PV
+  // product); returns this lane's sum of p.  key0 = first key of the sub-block.
+  auto exp_pack = [&](int key0, f32x16 (&s)[1], float m_use, uint4 (&pp)[2], auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    // S^T = K_j Q^T  (keys x queries), fp32 accumulate.
-    f32x16 s[QB][C::KB];
+    const float sum = tile_exp<1, MASKED>(s, qk_scale, m_use, key0 + 4 * g, key_lim);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-      for (int st = 0; st < C::DS; ++st) {
-        const uint4 a =
-            *reinterpret_cast<const uint4*>(&k_lds[buf][(32 * kb + n) * C::KROW + 16 * st + 8 * g]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mma16(T{}, a, qf[qb][st], st == 0 ? f32x16{} : s[qb][kb]);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const f32x16& v = s[0];
+      pp[h] = make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
+                         pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
     }
-    // Online softmax, then P^T packed to 16-bit as the B operand.
-    uint4 pp[QB][C::KB * 2];
+    return sum;
+  };
+  f32x16 oacc[DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int query = qw0 + 32 * qb + n;
-      const int key_base = j * BN + 4 * g;
-      const int key_lim = CAUSAL ? min(query + 1, N) : N;
-      const float mt = tile_max<C::KB, MASKED>(s[qb], qk_scale, key_base, key_lim);
-      float alpha;
-      if (raise_max(mt, m_run[qb], l_run[qb], &alpha)) {
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  // O^T += V^T P^T for sub-block `sb` of tile buffer `buf`.
+  auto pv_gemm = [&](int buf, int sb, const uint4 (&pp)[2]) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
-      }
-      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
-      l_run[qb] += tile_exp<C::KB, MASKED>(s[qb], qk_scale, m_use, key_base, key_lim);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x16& v = s[qb][kb];
-          pp[qb][2 * kb + h] = make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
-                                          pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
-        }
-      }
-    }
-    // O^T += V_j^T P^T  (d x queries), accumulator as C operand.
-#pragma unroll
-    for (int kk = 0; kk < C::KB * 2; ++kk) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const uint4 a =
-            *reinterpret_cast<const uint4*>(&v_lds[buf][(32 * db + n) * C::VROW + 16 * kk + 8 * g]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mma16(T{}, a, pp[qb][kk], oacc[qb][db]);
+            *reinterpret_cast<const uint4*>(&v_lds[buf][(32 * db + n) * C::VROW + 32 * sb + 16 * h + 8 * g]);
+        oacc[db] = mma16(T{}, a, pp[h], oacc[db]);
       }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  auto m_ref = [&] { return m_run == kNegInf ? 0.f : m_run; };
+  // Raise the reference max if a sub-block's scores need it; rescale the
+  // accumulator (only when some lane of the wave raised).
+  auto update_max = [&](float mt) {
+    float alpha;
+    if (raise_max(mt, m_run, l_run, &alpha)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
   };
 
-  if (j_end > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
-
-  int j = 0;
-  for (; j < j_unm; ++j) {  // unmasked stage: every wave, every key visible
-    const int buf = j & 1;
-    const bool more = j + 1 < j_end;
-    if (more) load_block(j + 1);
-    tile(j, buf, std::false_type{});
-    if (more) store_block(buf ^ 1);
-    __syncthreads();
-  }
-  for (; j < j_end; ++j) {  // masked stage: diagonal blocks and the sequence tail
-    const int buf = j & 1;
-    const bool more = j + 1 < j_end;
-    if (more) load_block(j + 1);
-    if (wave_live && (!CAUSAL || j < w_s2)) tile(j, buf, std::true_type{});
-    if (more) store_block(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: one divide per row, store O and the natural-log LSE ------
+  // One pipeline step: sub-block u's softmax and PV product, overlapped with
+  // sub-block u+1's score product and row max.
+  //   phase A: S_{u+1} = K Q^T   ||  p_u = exp2(S_u - m), packed
+  //   phase B: O += V P_u        ||  rowmax(S_{u+1})
+  // Each phase is written as chunks of one matrix product plus its share of
+  // the VALU work, fenced so the compiler keeps the interleave; LDS reads
+  // run two fragments ahead of their products.
+  auto step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1], int kbuf_n, int ksb_n, f32x16 (&nxt)[1],
+                  auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr int EPC = 16 / DS;  // exponentials per product in phase A
+    const float m_use = m_ref();
+    const int kbase = key_u + 4 * g;
+    const uint16_t* krow = &k_lds[kbuf_n][(32 * ksb_n + n) * C::KROW + 8 * g];
+    uint4 a[3];
+    a[0] = *reinterpret_cast<const uint4*>(krow);
+    a[1] = *reinterpret_cast<const uint4*>(krow + 16);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t pk[8];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int query = qw0 + 32 * qb + n;
-    const float l_tot = halves_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
-    if (query < N) {
-      uint16_t* orow = og + head + (size_t)query * D;
+    for (int st = 0; st < DS; ++st) {
+      if (st + 2 < DS) a[(st + 2) % 3] = *reinterpret_cast<const uint4*>(krow + 16 * (st + 2));
+      nxt[0] = mma16(T{}, a[st % 3], qf[st], st == 0 ? f32x16{} : nxt[0]);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
+      for (int e = 0; e < EPC; e += 2) {
+        const int r = st * EPC + e;  // registers r, r+1 of cur
+        float p0 = fast_exp2(__builtin_fmaf(cur[0][r], qk_scale, -m_use));
+        float p1 = fast_exp2(__builtin_fmaf(cur[0][r + 1], qk_scale, -m_use));
+        if constexpr (MASKED) {
+          p0 = kbase + 8 * (r / 4) + (r % 4) < key_lim ? p0 : 0.f;
+          p1 = kbase + 8 * ((r + 1) / 4) + ((r + 1) % 4) < key_lim ? p1 : 0.f;
+        }
+        part[r % 4] += p0;
+        part[(r + 1) % 4] += p1;
+        pk[r / 2] = pack2(T{}, p0, p1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += (part[0] + part[1]) + (part[2] + part[3]);
+    const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+    // phase B: 2 x DB products; the row max of S_{u+1} is spread over them.
+    const uint16_t* vrow = &v_lds[vbuf][n * C::VROW + 32 * vsb + 8 * g];
+    uint4 b[3];
+    b[0] = *reinterpret_cast<const uint4*>(vrow);
+    b[1] = *reinterpret_cast<const uint4*>(vrow + 32 * C::VROW);
+    constexpr int NB = 2 * DB;  // products in phase B, index i -> (h = i / DB, db = i % DB)
+    constexpr int MPC = (16 + NB - 1) / NB;  // S_{u+1} registers folded into the max per product
+    float mx = kNegInf;
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const f32x16& v = oacc[qb][db];
-          const uint2 w = make_uint2(pack2(T{}, v[4 * rq + 0] * inv, v[4 * rq + 1] * inv),
-                                     pack2(T{}, v[4 * rq + 2] * inv, v[4 * rq + 3] * inv));
-          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
+    for (int i = 0; i < NB; ++i) {
+      if (i + 2 < NB) {
+        const int h = (i + 2) / DB, db = (i + 2) % DB;
+        b[(i + 2) % 3] = *reinterpret_cast<const uint4*>(vrow + 32 * db * C::VROW + 16 * h);
+      }
+      oacc[i % DB] = mma16(T{}, b[i % 3], pp[i / DB], oacc[i % DB]);
+      if (i >= 1) {  // S_{u+1} is complete once phase A's products drained
+#pragma unroll
+        for (int r = (i - 1) * MPC; r < i * MPC && r < 16; ++r) {
+          if constexpr (MASKED) {
+            const int key = kbase + 32 + 8 * (r / 4) + (r % 4);
+            mx = fmaxf(mx, key < key_lim ? nxt[0][r] : kNegInf);
+          } else {
+            mx = fmaxf(mx, nxt[0][r]);
+          }
         }
       }
-      if (g == 0) lseg[(size_t)bh * N + query] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int r = (NB - 1) * MPC; r < 16; ++r) {
+      if constexpr (MASKED) {
+        const int key = kbase + 32 + 8 * (r / 4) + (r % 4);
+        mx = fmaxf(mx, key < key_lim ? nxt[0][r] : kNegInf);
+      } else {
+        mx = fmaxf(mx, nxt[0][r]);
+      }
+    }
+    mx = halves_max(mx);
+    update_max(mx == kNegInf ? kNegInf : mx * qk_scale);
+  };
+  // The last sub-block: softmax and PV only.
+  auto last_step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1]) {
+    uint4 pp[2];
+    l_run += exp_pack(key_u, cur, m_ref(), pp, std::true_type{});
+    pv_gemm(vbuf, vsb, pp);
+  };
+
+  // One tile j (tiles j and j+1 are in LDS at buffers b0, b1): its SUB
+  // pipeline steps, the last of which starts on tile j+1; tile j+2 is staged
+  // into the third buffer meanwhile.
+  f32x16 sA[1], sB[1];  // sub-blocks with even / odd index
+  // With an odd number of sub-blocks per tile the register roles swap from
+  // one tile to the next, so the tile body exists in both orders.
+  auto tile_iter_p = [&](int j, auto masked, f32x16 (&e)[1], f32x16 (&o)[1]) {
+    const bool stage = j + 2 < j_end;
+    if (stage) load_block(j + 2);
+    const int b0 = j % 3, b1 = b0 == 2 ? 0 : b0 + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const int key_u = j * BN + 32 * i;
+      const int kb_n = i + 1 < SUB ? b0 : b1, ks_n = i + 1 < SUB ? i + 1 : 0;
+      if (i % 2 == 0) step(key_u, b0, i, e, kb_n, ks_n, o, masked);
+      else step(key_u, b0, i, o, kb_n, ks_n, e, masked);
+    }
+    if (stage) store_block(b2);
+    __syncthreads();
+  };
+  auto tile_iter = [&](int j, auto masked) {
+    if ((SUB % 2 == 1) && (j & 1)) tile_iter_p(j, masked, sB, sA);
+    else tile_iter_p(j, masked, sA, sB);
+  };
+
+  // ---- prologue: tiles 0 and 1 into LDS, S of sub-block 0 and its max ------
+  load_block(0);
+  store_block(0);
+  if (j_end > 1) {
+    load_block(1);
+    store_block(1);
+  }
+  __syncthreads();
+  s_gemm(0, 0, sA);
+  if (0 < j_unm) update_max(tile_max<1, false>(sA, qk_scale, 4 * g, key_lim));
+  else update_max(tile_max<1, true>(sA, qk_scale, 4 * g, key_lim));
+
+  // ---- main loop over tiles that have a next tile ---------------------------
+  int j = 0;
+  for (; j + 1 < j_unm; ++j) tile_iter(j, std::false_type{});  // tiles j, j+1 unmasked
+  for (; j + 1 < j_end; ++j) tile_iter(j, std::true_type{});
+  // ---- last tile: its sub-blocks, the final one without a successor -------
+  auto last_tile = [&](f32x16 (&e)[1], f32x16 (&o)[1]) {
+    const int b0 = j % 3;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const int key_u = j * BN + 32 * i;
+      if (i + 1 < SUB) {
+        if (i % 2 == 0) step(key_u, b0, i, e, b0, i + 1, o, std::true_type{});
+        else step(key_u, b0, i, o, b0, i + 1, e, std::true_type{});
+      } else {
+        if (i % 2 == 0) last_step(key_u, b0, i, e);
+        else last_step(key_u, b0, i, o);
+      }
+    }
+  };
+  if ((SUB % 2 == 1) && (j & 1)) last_tile(sB, sA);
+  else last_tile(sA, sB);
+
+  // ---- epilogue: one divide per row, store O and the natural-log LSE ------
+  const float l_tot = halves_sum(l_run);
+  const float inv = 1.f / l_tot;
+  if (query < N) {
+    uint16_t* orow = og + head + (size_t)query * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x16& v = oacc[db];
+        const uint2 w = make_uint2(pack2(T{}, v[4 * rq + 0] * inv, v[4 * rq + 1] * inv),
+                                   pack2(T{}, v[4 * rq + 2] * inv, v[4 * rq + 3] * inv));
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
+      }
+    }
+    if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -439,7 +549,8 @@ namespace {
 // d = 128 and 128 for d = 64.  Must agree with fwd_tile() in fa_plan.hpp.
 template <int D>
 struct Tile16 {
-  static constexpr int BN = D == 128 ? 64 : 128, NW = 8, QB = 1;
+  static constexpr int NW = 8, QB = 1;
+  static constexpr int BN = D == 128 ? 64 : 128;
 };
 
 template <typename T, int D, bool CAUSAL>
