@@ -69,105 +69,94 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.  Workgroup = 4 waves x 32 keys; inner loop over 64-query blocks.
+// 2. dK, dV.  A workgroup owns NP groups of 32 keys and loops over 64-query
+// blocks.  Each key group is served by a pair of waves on one SIMD with
+// split roles, two of the four products each:
+//   wave A (waves 0..NP-1):  S = Q K^T, P = exp2(S*c - LSE2), dV += P^T dO
+//   wave B (waves NP..2NP-1): dP = dO V^T, dS = P * (dP - Delta), dK += dS^T Q
+// P goes from A to B through LDS in fp32 (lane-private slots).  Two barriers
+// per block: after the first phase P is visible to B; after the second the
+// block's Q/dO buffer is free and the next block is in LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KV {
-  static constexpr int NW = 4, NT = 256, KW = 32, BNK = NW * KW, BMQ = 64;
-  static constexpr int QROW = D + 8;      // row-major Q / dO stride (elements)
-  static constexpr int TROW = BMQ + 8;    // transposed Q^T / dO^T stride
-  static constexpr int DS = D / 16, DB = D / 32;
-  static constexpr int KPT = BMQ * D / 8 / NT;  // query rows per thread in staging
-  static_assert(KPT == 2 || KPT == 4, "staging packs 2 or 4 rows per thread");
+  static constexpr int NP = 4, NW = 2 * NP, NT = 64 * NW, KW = 32, BNK = NP * KW, BMQ = 64;
+  static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  static constexpr int LDC = BMQ * CPR / NT;  // 16-byte chunks of Q (and of dO) per thread per block
+  static_assert(LDC >= 1 && BMQ * CPR % NT == 0, "staging split");
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
     float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, float qk_scale, float dk_scale,
     uint32_t qsign) {
   using C = KV<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::BMQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::BMQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][D * C::TROW];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::BMQ * D];   // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::BMQ * D];
+  __shared__ __attribute__((aligned(16))) float4 x_lds[C::NP][8][64];      // P, A -> B
   __shared__ __attribute__((aligned(16))) float lse_lds[2][C::BMQ];
   __shared__ __attribute__((aligned(16))) float dl_lds[2][C::BMQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
+  const bool role_a = wave < C::NP;  // wave-uniform
+  const int pw = wave % C::NP;       // key group; waves pw and pw + NP share a SIMD
   int bh, kblk;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), n_kblk, false, &bh, &kblk);  // ascending = heaviest first
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* qh = qg + head;
-  const uint16_t* doh = dog + head;
-  const float* lseh = lseg + (size_t)bh * N;
-  const float* dlh = deltag + (size_t)bh * N;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
+  const rsrc_t lrs = make_rsrc(lseg + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t drs = make_rsrc(deltag + (size_t)bh * N, (uint32_t)N * 4);
 
-  const int kw0 = kblk * C::BNK + wave * C::KW;  // first key of this wave
-  const int key = kw0 + n;                       // this lane's key
-  const bool wave_live = kw0 < N;
+  const int kw0 = kblk * C::BNK + pw * C::KW;  // first key of this pair
+  const bool pair_live = kw0 < N;
 
-  // K and V as B operands of S = Q K^T and dP = dO V^T: K[key][16 s + 8 g ..].
-  uint4 kf[C::DS], vf[C::DS];
+  // A holds K, B holds V, as the B operand of Q K^T / dO V^T:
+  // kv[s] = row (kw0 + n), columns 16 s + 8 g .. + 8 (zero past the end).
+  uint4 kv[C::DS];
+  {
+    const rsrc_t rs = make_rsrc((role_a ? kg : vg) + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < C::DS; ++s) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (key < N) {
-      a = *reinterpret_cast<const uint4*>(kg + head + (size_t)key * D + 16 * s + 8 * g);
-      b = *reinterpret_cast<const uint4*>(vg + head + (size_t)key * D + 16 * s + 8 * g);
-    }
-    kf[s] = a;
-    vf[s] = b;
+    for (int s = 0; s < C::DS; ++s) kv[s] = load16(rs, ((uint32_t)(kw0 + n) * D + 16 * s + 8 * g) * 2);
   }
-  f32x16 dk[C::DB], dv[C::DB];
+  f32x16 acc[C::DB];  // A: dV, B: dK (unscaled); rows = keys, columns = d
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
   const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
   const int i_lo = CAUSAL ? (kblk * C::BNK) / C::BMQ : 0;
 
-  // staging: thread owns KPT consecutive query rows x one 8-column chunk
-  const int sa = tid % (C::BMQ / C::KPT), sc = tid / (C::BMQ / C::KPT);
-  uint4 qs[C::KPT], dos[C::KPT];
-  float lse_s = 0.f, dl_s = 0.f;
-
+  // staging: chunk tid + e NT of the block -> row / CPR, column chunk % CPR
+  uint4 qs[C::LDC], dos[C::LDC];
+  float ls = 0.f;
   auto load_block = [&](int i) {
 #pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const int row = i * C::BMQ + C::KPT * sa + e;
-      uint4 a = make_uint4(0, 0, 0, 0), b = a;
-      if (row < N) {
-        a = *reinterpret_cast<const uint4*>(qh + (size_t)row * D + 8 * sc);
-        b = *reinterpret_cast<const uint4*>(doh + (size_t)row * D + 8 * sc);
-        a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
-      }
+    for (int e = 0; e < C::LDC; ++e) {
+      const int c = tid + e * C::NT;
+      const uint32_t off = ((uint32_t)(i * C::BMQ + c / C::CPR) * D + 8 * (c % C::CPR)) * 2;
+      uint4 a = load16(qrs, off);
+      a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
       qs[e] = a;
-      dos[e] = b;
+      dos[e] = load16(dors, off);
     }
-    if (tid < C::BMQ) {
-      const int row = i * C::BMQ + tid;
-      // A query past the end gets LSE = +inf, so its recomputed P is 0.
-      lse_s = row < N ? lseh[row] * kLog2e : kPosInf;
-      dl_s = row < N ? dlh[row] : 0.f;
-    }
+    // threads 0..63 carry LSE (as log2), threads 64..127 Delta; a query past
+    // the end gets LSE = +inf, so its recomputed P is 0.
+    const int r = i * C::BMQ + (tid & 63);
+    if (tid < 64) ls = r < N ? load4f(lrs, r * 4) * kLog2e : kPosInf;
+    else if (tid < 128) ls = load4f(drs, r * 4);
   };
   auto store_block = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const int r = C::KPT * sa + e;
-      *reinterpret_cast<uint4*>(&q_lds[buf][r * C::QROW + 8 * sc]) = qs[e];
-      *reinterpret_cast<uint4*>(&do_lds[buf][r * C::QROW + 8 * sc]) = dos[e];
+    for (int e = 0; e < C::LDC; ++e) {
+      const int c = tid + e * C::NT;
+      const int off = swz<D>(c / C::CPR, 8 * (c % C::CPR));
+      *reinterpret_cast<uint4*>(&q_lds[buf][off]) = qs[e];
+      *reinterpret_cast<uint4*>(&do_lds[buf][off]) = dos[e];
     }
-    store_transposed<C::KPT>(&qt_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), qs);
-    store_transposed<C::KPT>(&dot_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), dos);
-    if (tid < C::BMQ) {
-      lse_lds[buf][tid] = lse_s;
-      dl_lds[buf][tid] = dl_s;
-    }
+    if (tid < 64) lse_lds[buf][tid] = ls;
+    else if (tid < 128) dl_lds[buf][tid - 64] = ls;
   };
 
   if (i_lo < n_qblk) {
@@ -176,6 +165,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   }
   __syncthreads();
 
+  f32x16 sd[2];   // A: S then P; B: dP then dS.  Register r of block qc is
+                  // query q_first + 32 qc + 8 (r/4) + 4 g + r%4, lane key kw0 + n.
+  uint4 pk[4];    // packed 16-bit P (A) or dS (B), query chunk kk = 2 qc + h
   for (int i = i_lo; i < n_qblk; ++i) {
     const int buf = i & 1;
     const bool more = i + 1 < n_qblk;
@@ -183,74 +175,82 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 
     const int q_first = i * C::BMQ;
     const int q_last = min(q_first + C::BMQ, N) - 1;
-    const bool active = wave_live && (!CAUSAL || q_last >= kw0);
+    const bool active = pair_live && (!CAUSAL || q_last >= kw0);
     const bool need_mask = CAUSAL && q_first < kw0 + C::KW - 1;
+    const uint16_t* lhs = role_a ? q_lds[buf] : do_lds[buf];  // row-read operand
+    const uint16_t* rhs = role_a ? do_lds[buf] : q_lds[buf];  // transposed-read operand
+
+    // ---- phase 1: S = Q K^T (A) or dP = dO V^T (B) -------------------------
     if (active) {
-      f32x16 s[2], dp[2];
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
-        s[qc] = f32x16{};
-        dp[qc] = f32x16{};
+        sd[qc] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < C::DS; ++st) {
-          const int off = (32 * qc + n) * C::QROW + 16 * st + 8 * g;
-          s[qc] = mma16(T{}, *reinterpret_cast<const uint4*>(&q_lds[buf][off]), kf[st], s[qc]);
-          dp[qc] = mma16(T{}, *reinterpret_cast<const uint4*>(&do_lds[buf][off]), vf[st], dp[qc]);
-        }
+        for (int st = 0; st < C::DS; ++st)
+          sd[qc] = mma16(T{}, read_row<D>(lhs, 32 * qc + n, 16 * st + 8 * g), kv[st], sd[qc]);
       }
-      // P = exp2(S * qk_scale - LSE2), dS = P * (dP - Delta); register r of
-      // block qc is query q_first + 32 qc + 8 (r/4) + 4 g + r%4.
-      uint4 pp[4], dsp[4];
+      if (role_a) {
+        const int key = kw0 + n;
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) {
+        for (int qc = 0; qc < 2; ++qc) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int ql = 32 * qc + 8 * rq + 4 * g;
-          const float4 l4 = *reinterpret_cast<const float4*>(&lse_lds[buf][ql]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][ql]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          for (int rq = 0; rq < 4; ++rq) {
+            const int ql = 32 * qc + 8 * rq + 4 * g;
+            const float4 l4 = *reinterpret_cast<const float4*>(&lse_lds[buf][ql]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            float p = fast_exp2(__builtin_fmaf(s[qc][r], qk_scale, -lv[e]));
-            if (need_mask) p = (key <= q_first + ql + e) ? p : 0.f;
-            s[qc][r] = p;
-            dp[qc][r] = p * (dp[qc][r] - dv4[e]);
+            for (int e = 0; e < 4; ++e) {
+              float p = fast_exp2(__builtin_fmaf(sd[qc][4 * rq + e], qk_scale, -lv[e]));
+              if (need_mask) p = (key <= q_first + ql + e) ? p : 0.f;
+              sd[qc][4 * rq + e] = p;
+            }
+            x_lds[pw][4 * qc + rq][lane] =
+                make_float4(sd[qc][4 * rq], sd[qc][4 * rq + 1], sd[qc][4 * rq + 2], sd[qc][4 * rq + 3]);
           }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          pp[2 * qc + h] = pack8(T{}, s[qc], h);
-          dsp[2 * qc + h] = pack8(T{}, dp[qc], h);
+          pk[2 * qc] = pack8(T{}, sd[qc], 0);
+          pk[2 * qc + 1] = pack8(T{}, sd[qc], 1);
         }
       }
-      // dV += P^T dO, dK += dS^T Q (contraction over the 64 queries).
+    }
+    __syncthreads();
+
+    // ---- phase 2: dV += P^T dO (A) or dS, dK += dS^T Q (B) ------------------
+    if (active) {
+      if (!role_a) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+        for (int qc = 0; qc < 2; ++qc) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int off = (32 * db + n) * C::TROW + 16 * kk + 8 * g;
-          dv[db] = mma16(T{}, pp[kk], *reinterpret_cast<const uint4*>(&dot_lds[buf][off]), dv[db]);
-          dk[db] = mma16(T{}, dsp[kk], *reinterpret_cast<const uint4*>(&qt_lds[buf][off]), dk[db]);
+          for (int rq = 0; rq < 4; ++rq) {
+            const int ql = 32 * qc + 8 * rq + 4 * g;
+            const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][ql]);
+            const float4 p4 = x_lds[pw][4 * qc + rq][lane];
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w}, pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sd[qc][4 * rq + e] = pv[e] * (sd[qc][4 * rq + e] - dv4[e]);
+          }
+          pk[2 * qc] = pack8(T{}, sd[qc], 0);
+          pk[2 * qc + 1] = pack8(T{}, sd[qc], 1);
         }
       }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = mma16(T{}, pk[kk], read_tr<D>(rhs, 16 * kk, 32 * db, lane), acc[db]);
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
   }
 
   // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
-  float* dkh = dkg + head;
-  float* dvh = dvg + head;
+  float* out = (role_a ? dvg : dkg) + head;
+  const float sc = role_a ? 1.f : dk_scale;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kw0 + 8 * (r / 4) + 4 * g + (r % 4);
-      if (kr < N) {
-        dkh[(size_t)kr * D + 32 * db + n] = dk[db][r] * dk_scale;
-        dvh[(size_t)kr * D + 32 * db + n] = dv[db][r];
-      }
+      if (kr < N) out[(size_t)kr * D + 32 * db + n] = acc[db][r] * sc;
     }
 }
 
@@ -431,7 +431,7 @@ hipError_t run(const BwdArgs& a, int stage) {
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 2) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(256), 0, a.stream, q, k, v, dout,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q, k, v, dout,
                        a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, fabsf(a.scale), qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

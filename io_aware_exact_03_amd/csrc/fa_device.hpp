@@ -229,4 +229,52 @@ __device__ __forceinline__ void store_transposed(uint16_t* dst, int stride, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled row-major LDS tiles.  A 16-bit tile with rows of D elements
+// (D = 64 or 128, no padding) keeps its 16-byte chunks XOR-permuted per row,
+// chunk c of row r at chunk c ^ swz_chunk(r).  The permutation makes two
+// access patterns bank-conflict free at once:
+//  * 16-byte row reads: 16 consecutive rows, one chunk each (an MFMA operand
+//    whose contraction index runs along the row);
+//  * transposing 8-byte reads (ds_read_b64_tr_b16): per half wave 4
+//    consecutive rows x 64 bytes (an MFMA operand whose contraction index
+//    runs down the columns).
+// Row padding serves only one of the two.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row) {
+  static_assert(D == 64 || D == 128, "row width");
+  return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {  // element offset of (row, col)
+  return row * D + (((col >> 3) ^ swz_chunk<D>(row)) << 3) + (col & 7);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr_b64(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// An MFMA 16-bit operand fragment read across rows of a swizzled tile: lane
+// (c = lane % 32, g = lane / 32) receives column col0 + c of rows
+// r0 + 4g + {0..3} and then r0 + 8 + 4g + {0..3} (r0 a multiple of 16, col0
+// a multiple of 32), i.e. the row order of a 32x32 accumulator packed to
+// 16 bits.  ds_read_b64_tr_b16 hands lane i of each 16-lane group element e
+// of the 4-element vector addressed by lane 4e + i/4, so lane p addresses
+// row p/4 and columns 4(p%4)..4(p%4)+3 of its group's 4 x 16 block.
+template <int D>
+__device__ __forceinline__ uint4 read_tr(const uint16_t* tile, int r0, int col0, int lane) {
+  const int p = lane & 15, row = r0 + 4 * (lane >> 5) + (p >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (p & 3);
+  const uint2 a = read_tr_b64(tile + swz<D>(row, col));
+  const uint2 b = read_tr_b64(tile + swz<D>(row + 8, col));
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+template <int D>
+__device__ __forceinline__ uint4 read_row(const uint16_t* tile, int row, int col) {
+  return *reinterpret_cast<const uint4*>(tile + swz<D>(row, col));
+}
+
 }  // namespace fa
