@@ -255,53 +255,55 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.  Workgroup = 4 waves x 32 queries; inner loop over 64-key blocks.
+// 3. dQ.  Workgroup = 8 waves x 32 queries (two waves per SIMD); inner loop
+// over 64-key blocks, each taken as two 32-key sub-blocks.  K and V sit
+// row-major (swizzled) in LDS: rows feed S^T = K Q^T and dP^T = V dO^T,
+// transposing reads give K^T for dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QG {
-  static constexpr int NW = 4, NT = 256, BM = NW * 32, BN = 64;
-  static constexpr int KROW = D + 8, TROW = BN + 8;
-  static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32;
-  static constexpr int KPT = BN * D / 8 / NT;
-  static_assert(KPT == 2 || KPT == 4, "staging packs 2 or 4 rows per thread");
+  static constexpr int NW = 8, NT = 64 * NW, BM = NW * 32, BN = 64;
+  static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32, CPR = D / 8;
+  static constexpr int LDC = BN * CPR / NT;  // 16-byte chunks of K (and of V) per thread per block
+  static_assert(LDC >= 1 && BN * CPR % NT == 0, "staging split");
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
     float* __restrict__ dqg, int N, int n_qblk, float qk_scale, float dq_scale, uint32_t qsign) {
   using C = QG<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * D];  // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
   int bh, qblk;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* kh = kg + head;
-  const uint16_t* vh = vg + head;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const rsrc_t krs = make_rsrc(kg + head, head_bytes), vrs = make_rsrc(vg + head, head_bytes);
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * 32;
   const int query = qw0 + n;
 
+  // Q and dO of this lane's query as the B operands (zero past the end).
   uint4 qf[C::DS], dof[C::DS];
+  {
+    const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < C::DS; ++s) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (query < N) {
-      a = *reinterpret_cast<const uint4*>(qg + head + (size_t)query * D + 16 * s + 8 * g);
-      b = *reinterpret_cast<const uint4*>(dog + head + (size_t)query * D + 16 * s + 8 * g);
+    for (int s = 0; s < C::DS; ++s) {
+      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * g) * 2;
+      uint4 a = load16(qrs, off);
       a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
+      qf[s] = a;
+      dof[s] = load16(dors, off);
     }
-    qf[s] = a;
-    dof[s] = b;
   }
   const float lse2 = query < N ? lseg[(size_t)bh * N + query] * kLog2e : kPosInf;
   const float dl = query < N ? deltag[(size_t)bh * N + query] : 0.f;
 
-  f32x16 dq[C::DB];
+  f32x16 dq[C::DB];  // dQ^T: rows = d, columns = queries
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dq[db] = f32x16{};
 
@@ -312,30 +314,26 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
   const bool wave_live = qw0 < N;
   if (CAUSAL && wave_live) causal_stages(qw0, min(qw0 + 32, N), C::BN, &w_s1, &w_s2);
   const int full_blocks = N / C::BN;
+  const int key_lim = CAUSAL ? min(query + 1, N) : N;
 
-  const int sa = tid % (C::BN / C::KPT), sc = tid / (C::BN / C::KPT);
-  uint4 ks[C::KPT], vs[C::KPT];
+  uint4 ks[C::LDC], vs[C::LDC];
   auto load_block = [&](int j) {
 #pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const int row = j * C::BN + C::KPT * sa + e;
-      uint4 a = make_uint4(0, 0, 0, 0), b = a;
-      if (row < N) {
-        a = *reinterpret_cast<const uint4*>(kh + (size_t)row * D + 8 * sc);
-        b = *reinterpret_cast<const uint4*>(vh + (size_t)row * D + 8 * sc);
-      }
-      ks[e] = a;
-      vs[e] = b;
+    for (int e = 0; e < C::LDC; ++e) {
+      const int c = tid + e * C::NT;
+      const uint32_t off = ((uint32_t)(j * C::BN + c / C::CPR) * D + 8 * (c % C::CPR)) * 2;
+      ks[e] = load16(krs, off);
+      vs[e] = load16(vrs, off);
     }
   };
   auto store_block = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const int r = C::KPT * sa + e;
-      *reinterpret_cast<uint4*>(&k_lds[buf][r * C::KROW + 8 * sc]) = ks[e];
-      *reinterpret_cast<uint4*>(&v_lds[buf][r * C::KROW + 8 * sc]) = vs[e];
+    for (int e = 0; e < C::LDC; ++e) {
+      const int c = tid + e * C::NT;
+      const int off = swz<D>(c / C::CPR, 8 * (c % C::CPR));
+      *reinterpret_cast<uint4*>(&k_lds[buf][off]) = ks[e];
+      *reinterpret_cast<uint4*>(&v_lds[buf][off]) = vs[e];
     }
-    store_transposed<C::KPT>(&kt_lds[buf][8 * sc * C::TROW], C::TROW, tpos(C::KPT * sa), ks);
   };
 
   if (j_end > 0) {
@@ -351,42 +349,30 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const bool need_mask = (CAUSAL && j >= w_s1) || j >= full_blocks;
     const bool active = wave_live && (!CAUSAL || j < w_s2);
     if (active) {
-      f32x16 s[C::KB], dp[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int st = 0; st < C::DS; ++st) {
-          const int off = (32 * kb + n) * C::KROW + 16 * st + 8 * g;
-          s[kb] = mma16(T{}, *reinterpret_cast<const uint4*>(&k_lds[buf][off]), qf[st], s[kb]);
-          dp[kb] = mma16(T{}, *reinterpret_cast<const uint4*>(&v_lds[buf][off]), dof[st], dp[kb]);
+          s = mma16(T{}, read_row<D>(k_lds[buf], 32 * kb + n, 16 * st + 8 * g), qf[st], s);
+          dp = mma16(T{}, read_row<D>(v_lds[buf], 32 * kb + n, 16 * st + 8 * g), dof[st], dp);
         }
-      }
-      // Register r of key block kb is key j BN + 32 kb + 8(r/4) + 4g + r%4.
-      const int key_lim = CAUSAL ? min(query + 1, N) : N;
-      uint4 dsp[C::KB * 2];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+        // Register r is key j BN + 32 kb + 8(r/4) + 4g + r%4.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][r], qk_scale, -lse2));
+          float p = fast_exp2(__builtin_fmaf(s[r], qk_scale, -lse2));
           if (need_mask) {
             const int kr = j * C::BN + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
             p = kr < key_lim ? p : 0.f;
           }
-          dp[kb][r] = p * (dp[kb][r] - dl);
+          dp[r] = p * (dp[r] - dl);
         }
-        dsp[2 * kb] = pack8(T{}, dp[kb], 0);
-        dsp[2 * kb + 1] = pack8(T{}, dp[kb], 1);
-      }
-      // dQ^T += K^T dS^T (contraction over the 64 keys).
-#pragma unroll
-      for (int kk = 0; kk < C::KB * 2; ++kk) {
+        const uint4 ds0 = pack8(T{}, dp, 0), ds1 = pack8(T{}, dp, 1);
+        // dQ^T += K^T dS^T over this sub-block's 32 keys (two 16-key chunks).
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int off = (32 * db + n) * C::TROW + 16 * kk + 8 * g;
-          dq[db] = mma16(T{}, *reinterpret_cast<const uint4*>(&kt_lds[buf][off]), dsp[kk], dq[db]);
+          dq[db] = mma16(T{}, read_tr<D>(k_lds[buf], 32 * kb, 32 * db, lane), ds0, dq[db]);
+          dq[db] = mma16(T{}, read_tr<D>(k_lds[buf], 32 * kb + 16, 32 * db, lane), ds1, dq[db]);
         }
       }
     }
@@ -437,7 +423,7 @@ hipError_t run(const BwdArgs& a, int stage) {
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 3) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(256), 0, a.stream, q, k, v, dout,
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(QG<D>::NT), 0, a.stream, q, k, v, dout,
                        a.lse, a.delta, a.dq, a.N, n_qblk, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
