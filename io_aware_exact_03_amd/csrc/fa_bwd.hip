@@ -128,34 +128,36 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
   const int i_lo = CAUSAL ? (kblk * C::BNK) / C::BMQ : 0;
 
-  // staging: chunk tid + e NT of the block -> row / CPR, column chunk % CPR
+  // staging: chunk tid + e NT of the block -> row / CPR, column chunk % CPR.
+  // Loaded values are only transformed when stored, so nothing waits for
+  // the loads before the block's products have been issued.
   uint4 qs[C::LDC], dos[C::LDC];
   float ls = 0.f;
+  bool l_in = false;
   auto load_block = [&](int i) {
 #pragma unroll
     for (int e = 0; e < C::LDC; ++e) {
       const int c = tid + e * C::NT;
       const uint32_t off = ((uint32_t)(i * C::BMQ + c / C::CPR) * D + 8 * (c % C::CPR)) * 2;
-      uint4 a = load16(qrs, off);
-      a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
-      qs[e] = a;
+      qs[e] = load16(qrs, off);
       dos[e] = load16(dors, off);
     }
-    // threads 0..63 carry LSE (as log2), threads 64..127 Delta; a query past
-    // the end gets LSE = +inf, so its recomputed P is 0.
+    // threads 0..63 carry LSE, threads 64..127 Delta
     const int r = i * C::BMQ + (tid & 63);
-    if (tid < 64) ls = r < N ? load4f(lrs, r * 4) * kLog2e : kPosInf;
-    else if (tid < 128) ls = load4f(drs, r * 4);
+    l_in = r < N;
+    if (tid < 128) ls = load4f(tid < 64 ? lrs : drs, r * 4);
   };
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < C::LDC; ++e) {
       const int c = tid + e * C::NT;
       const int off = swz<D>(c / C::CPR, 8 * (c % C::CPR));
-      *reinterpret_cast<uint4*>(&q_lds[buf][off]) = qs[e];
+      const uint4 a = qs[e];
+      *reinterpret_cast<uint4*>(&q_lds[buf][off]) = make_uint4(a.x ^ qsign, a.y ^ qsign, a.z ^ qsign, a.w ^ qsign);
       *reinterpret_cast<uint4*>(&do_lds[buf][off]) = dos[e];
     }
-    if (tid < 64) lse_lds[buf][tid] = ls;
+    // LSE as log2; a query past the end gets LSE = +inf, so its recomputed P is 0.
+    if (tid < 64) lse_lds[buf][tid] = l_in ? ls * kLog2e : kPosInf;
     else if (tid < 128) dl_lds[buf][tid - 64] = ls;
   };
 
@@ -163,6 +165,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     load_block(i_lo);
     store_block(i_lo & 1);
   }
+  wait_vmem();  // K or V fragments above
   __syncthreads();
 
   f32x16 sd[2];   // A: S then P; B: dP then dS.  Register r of block qc is
@@ -340,6 +343,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     load_block(0);
     store_block(0);
   }
+  wait_vmem();  // Q, dO fragments above
   __syncthreads();
 
   for (int j = 0; j < j_end; ++j) {

@@ -99,6 +99,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // past the end, which is how ragged tails are zero-filled without branches.
 // Offsets are 32-bit: the host rejects heads of 2 GiB or more.
 // ---------------------------------------------------------------------------
+// Wait until every vector-memory load this wave issued has returned
+// (s_waitcnt vmcnt(0), the other counters left free).  Placed after the
+// loads that precede a prefetching loop: the compiler's wait insertion cannot
+// tell those loads from the loop's own prefetches once the loop has been
+// entered, and otherwise puts a wait for the whole prefetch in front of the
+// first matrix products of every iteration.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 
