@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 #include "fa_plan.hpp"
@@ -69,57 +71,181 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.  A workgroup owns NP groups of 32 keys and loops over 64-query
+// 2. dK, dV.  A workgroup owns NP groups of 32 keys and loops over 32-query
 // blocks.  Each key group is served by a pair of waves on one SIMD with
 // split roles, two of the four products each:
 //   wave A (waves 0..NP-1):  S = Q K^T, P = exp2(S*c - LSE2), dV += P^T dO
 //   wave B (waves NP..2NP-1): dP = dO V^T, dS = P * (dP - Delta), dK += dS^T Q
-// P goes from A to B through LDS in fp32 (lane-private slots).  Two barriers
-// per block: after the first phase P is visible to B; after the second the
-// block's Q/dO buffer is free and the next block is in LDS.
+// B runs one query block behind A: in iteration i, A works on block i while
+// B works on block i-1, whose P (fp32, lane-private LDS slots) A wrote in
+// iteration i-1.  So the two waves of a SIMD never wait for each other
+// inside an iteration, and A's exponentials overlap B's products.
+// Q, dO, LSE and Delta go from global memory straight into LDS (no
+// registers), two blocks ahead, through four slots: A's block, B's block and
+// the two blocks in flight.  P cycles through two buffers.  One barrier per
+// iteration, which waits only for the older block in flight.  A negative
+// scale is applied by negating K, so Q lands in LDS unchanged.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KV {
-  static constexpr int NP = 4, NW = 2 * NP, NT = 64 * NW, KW = 32, BNK = NP * KW, BMQ = 64;
+  static constexpr int NP = 4, NW = 2 * NP, NT = 64 * NW, KW = 32, BNK = NP * KW, BMQ = 32;
   static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  static constexpr int LDC = BMQ * CPR / NT;  // 16-byte chunks of Q (and of dO) per thread per block
-  static_assert(LDC >= 1 && BMQ * CPR % NT == 0, "staging split");
+  static constexpr int RPL = 64 / CPR;            // tile rows per 1 KB wave load
+  static constexpr int PPA = BMQ / RPL;           // 1 KB pieces per Q (or dO) block
+  static constexpr int LPB = 2 * PPA / NW;        // pieces per wave per block
+  static_assert(LPB >= 1 && 2 * PPA == LPB * NW, "staging split");
 };
+
+// Uniform state of one dK/dV wave.
+struct KVWave {
+  int wave, lane, n, g, pw, kw0, N;
+  bool role_a;
+  float qk_scale;
+  rsrc_t qrs, dors, lrs, drs;
+};
+
+// Issue the loads of query block i into LDS: piece t = wave LPB + e covers
+// tile rows (t % PPA) RPL .. + RPL of Q (t < PPA) or of dO; lane l fills LDS
+// bytes 16 l of the piece, i.e. tile row l / CPR and stored chunk l % CPR,
+// which holds the row's logical chunk (l % CPR) ^ swz_chunk(row).  Waves 0
+// and 1 also load LSE and Delta.  Returns nothing; the caller counts loads.
+template <int D>
+__device__ __forceinline__ void kv_issue(const KVWave& w, int i, uint16_t* __restrict__ q_dst,
+                                         uint16_t* __restrict__ do_dst, float* __restrict__ l_dst,
+                                         float* __restrict__ d_dst) {
+  using C = KV<D>;
+  const int lrow = w.lane / C::CPR;
+#pragma unroll
+  for (int e = 0; e < C::LPB; ++e) {
+    const int t = w.wave * C::LPB + e;
+    const bool is_q = t < C::PPA;  // wave-uniform
+    const int row = (t % C::PPA) * C::RPL + lrow;
+    const int chunk = (w.lane % C::CPR) ^ swz_chunk<D>(row);
+    const uint32_t off = ((uint32_t)(i * C::BMQ + row) * D + 8 * chunk) * 2;
+    const int piece = (t % C::PPA) * C::RPL * D;
+    if (is_q) load_lds16(w.qrs, q_dst + piece, off);
+    else load_lds16(w.dors, do_dst + piece, off);
+  }
+  if (w.wave == 0) load_lds4(w.lrs, l_dst, (uint32_t)(i * C::BMQ + w.lane) * 4);
+  if (w.wave == 1) load_lds4(w.drs, d_dst, (uint32_t)(i * C::BMQ + w.lane) * 4);
+}
+
+// One iteration of a wave's work.  Every LDS tile it touches arrives as a
+// distinct __restrict__ pointer, which tells the compiler that the loads it
+// issues into the next slots do not alias what it reads this iteration, so
+// it does not wait for those loads before each read.
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void kv_iter(
+    const KVWave& w, int i, bool work, bool ahead, const uint4 (&kv)[KV<D>::DS], f32x16 (&acc)[KV<D>::DB],
+    const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const float* __restrict__ rowv,
+    float4* __restrict__ x_out, const float4* __restrict__ x_in, uint16_t* __restrict__ nq,
+    uint16_t* __restrict__ ndo, float* __restrict__ nl, float* __restrict__ nd) {
+  using C = KV<D>;
+  if (ahead) kv_issue<D>(w, i + 2, nq, ndo, nl, nd);
+  if (!work) return;
+  const int n = w.n, g = w.g, lane = w.lane;
+  // Register r of the 32x32 accumulator is query 8 (r/4) + 4 g + r%4 of the
+  // block; the lane's key is kw0 + n.  A chain's LDS operands are all
+  // requested before its first product, and the second chain's transposed
+  // operands before the vector work; the fences keep them there.
+  uint4 ra[C::DS];
+#pragma unroll
+  for (int st = 0; st < C::DS; ++st) ra[st] = read_row<D>(lhs, n, 16 * st + 8 * g);
+  float4 v4[4], p4[4];
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) {
+    v4[rq] = *reinterpret_cast<const float4*>(&rowv[8 * rq + 4 * g]);  // A: LSE, B: Delta
+    if (!w.role_a) p4[rq] = x_in[64 * rq + lane];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 sd = f32x16{};  // A: S, B: dP
+#pragma unroll
+  for (int st = 0; st < C::DS; ++st) sd = mma16(T{}, ra[st], kv[st], sd);
+  uint4 rb[2 * C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    rb[2 * db] = read_tr<D>(rhs, 0, 32 * db, lane);
+    rb[2 * db + 1] = read_tr<D>(rhs, 16, 32 * db, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (w.role_a) {
+    const int q_first = i * C::BMQ;
+    const bool need_mask = CAUSAL && q_first < w.kw0 + C::KW - 1;
+    const int key = w.kw0 + n;
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float lv[4] = {v4[rq].x, v4[rq].y, v4[rq].z, v4[rq].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // P = exp2(s |scale| log2 e - LSE log2 e).  A query past the end has
+        // Q, dO and Delta all zero (LSE reads as 0), so its P adds nothing.
+        float p = fast_exp2(__builtin_fmaf(sd[4 * rq + e], w.qk_scale, -lv[e] * kLog2e));
+        if (need_mask) p = (key <= q_first + 8 * rq + 4 * g + e) ? p : 0.f;
+        sd[4 * rq + e] = p;
+      }
+      x_out[64 * rq + lane] = make_float4(sd[4 * rq], sd[4 * rq + 1], sd[4 * rq + 2], sd[4 * rq + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float dv4[4] = {v4[rq].x, v4[rq].y, v4[rq].z, v4[rq].w};
+      const float pv[4] = {p4[rq].x, p4[rq].y, p4[rq].z, p4[rq].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sd[4 * rq + e] = pv[e] * (sd[4 * rq + e] - dv4[e]);
+    }
+  }
+  const uint4 pk0 = pack8(T{}, sd, 0), pk1 = pack8(T{}, sd, 1);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    acc[db] = mma16(T{}, pk0, rb[2 * db], acc[db]);
+    acc[db] = mma16(T{}, pk1, rb[2 * db + 1], acc[db]);
+  }
+}
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
     float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, float qk_scale, float dk_scale,
-    uint32_t qsign) {
+    uint32_t ksign) {
   using C = KV<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::BMQ * D];   // swizzled row-major
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::BMQ * D];
-  __shared__ __attribute__((aligned(16))) float4 x_lds[C::NP][8][64];      // P, A -> B
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][C::BMQ];
-  __shared__ __attribute__((aligned(16))) float dl_lds[2][C::BMQ];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][C::BMQ * D];   // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[4][C::BMQ * D];
+  __shared__ __attribute__((aligned(16))) float4 x_lds[2][C::NP][4 * 64];  // P, A -> B
+  __shared__ __attribute__((aligned(16))) float lse_lds[4][64];            // raw LSE (first BMQ used)
+  __shared__ __attribute__((aligned(16))) float dl_lds[4][64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
-  const bool role_a = wave < C::NP;  // wave-uniform
-  const int pw = wave % C::NP;       // key group; waves pw and pw + NP share a SIMD
+  KVWave w;
+  w.lane = threadIdx.x & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform, in a scalar register
+  w.n = w.lane & 31;
+  w.g = w.lane >> 5;
+  w.role_a = w.wave < C::NP;
+  w.pw = w.wave % C::NP;  // key group; waves pw and pw + NP share a SIMD
+  w.N = N;
+  w.qk_scale = qk_scale;
   int bh, kblk;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), n_kblk, false, &bh, &kblk);  // ascending = heaviest first
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
-  const rsrc_t lrs = make_rsrc(lseg + (size_t)bh * N, (uint32_t)N * 4);
-  const rsrc_t drs = make_rsrc(deltag + (size_t)bh * N, (uint32_t)N * 4);
+  w.qrs = make_rsrc(qg + head, head_bytes);
+  w.dors = make_rsrc(dog + head, head_bytes);
+  w.lrs = make_rsrc(lseg + (size_t)bh * N, (uint32_t)N * 4);
+  w.drs = make_rsrc(deltag + (size_t)bh * N, (uint32_t)N * 4);
+  w.kw0 = kblk * C::BNK + w.pw * C::KW;  // first key of this pair
+  const bool pair_live = w.kw0 < N;
 
-  const int kw0 = kblk * C::BNK + pw * C::KW;  // first key of this pair
-  const bool pair_live = kw0 < N;
-
-  // A holds K, B holds V, as the B operand of Q K^T / dO V^T:
-  // kv[s] = row (kw0 + n), columns 16 s + 8 g .. + 8 (zero past the end).
+  // A holds K (sign-flipped for a negative scale), B holds V, as the B
+  // operand of Q K^T / dO V^T: kv[s] = row kw0 + n, columns 16 s + 8 g .. + 8.
   uint4 kv[C::DS];
   {
-    const rsrc_t rs = make_rsrc((role_a ? kg : vg) + head, head_bytes);
+    const rsrc_t rs = make_rsrc((w.role_a ? kg : vg) + head, head_bytes);
+    const uint32_t sgn = w.role_a ? ksign : 0u;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) kv[s] = load16(rs, ((uint32_t)(kw0 + n) * D + 16 * s + 8 * g) * 2);
+    for (int s = 0; s < C::DS; ++s) {
+      const uint4 a = load16(rs, ((uint32_t)(w.kw0 + w.n) * D + 16 * s + 8 * w.g) * 2);
+      kv[s] = make_uint4(a.x ^ sgn, a.y ^ sgn, a.z ^ sgn, a.w ^ sgn);
+    }
   }
   f32x16 acc[C::DB];  // A: dV, B: dK (unscaled); rows = keys, columns = d
 #pragma unroll
@@ -127,133 +253,53 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 
   const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
   const int i_lo = CAUSAL ? (kblk * C::BNK) / C::BMQ : 0;
-
-  // staging: chunk tid + e NT of the block -> row / CPR, column chunk % CPR.
-  // Loaded values are only transformed when stored, so nothing waits for
-  // the loads before the block's products have been issued.
-  uint4 qs[C::LDC], dos[C::LDC];
-  float ls = 0.f;
-  bool l_in = false;
-  auto load_block = [&](int i) {
-#pragma unroll
-    for (int e = 0; e < C::LDC; ++e) {
-      const int c = tid + e * C::NT;
-      const uint32_t off = ((uint32_t)(i * C::BMQ + c / C::CPR) * D + 8 * (c % C::CPR)) * 2;
-      qs[e] = load16(qrs, off);
-      dos[e] = load16(dors, off);
-    }
-    // threads 0..63 carry LSE, threads 64..127 Delta
-    const int r = i * C::BMQ + (tid & 63);
-    l_in = r < N;
-    if (tid < 128) ls = load4f(tid < 64 ? lrs : drs, r * 4);
+  auto block_active = [&](int i) {
+    return pair_live && (!CAUSAL || min((i + 1) * C::BMQ, N) - 1 >= w.kw0);
   };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < C::LDC; ++e) {
-      const int c = tid + e * C::NT;
-      const int off = swz<D>(c / C::CPR, 8 * (c % C::CPR));
-      const uint4 a = qs[e];
-      *reinterpret_cast<uint4*>(&q_lds[buf][off]) = make_uint4(a.x ^ qsign, a.y ^ qsign, a.z ^ qsign, a.w ^ qsign);
-      *reinterpret_cast<uint4*>(&do_lds[buf][off]) = dos[e];
-    }
-    // LSE as log2; a query past the end gets LSE = +inf, so its recomputed P is 0.
-    if (tid < 64) lse_lds[buf][tid] = l_in ? ls * kLog2e : kPosInf;
-    else if (tid < 128) dl_lds[buf][tid - 64] = ls;
-  };
+  // Loads this wave issues per block (the barrier count below depends on it).
+  const bool extra = w.wave < 2;
 
-  if (i_lo < n_qblk) {
-    load_block(i_lo);
-    store_block(i_lo & 1);
-  }
   wait_vmem();  // K or V fragments above
-  __syncthreads();
+  kv_issue<D>(w, i_lo, q_lds[i_lo & 3], do_lds[i_lo & 3], lse_lds[i_lo & 3], dl_lds[i_lo & 3]);
+  if (i_lo + 1 < n_qblk) {
+    const int s1 = (i_lo + 1) & 3;
+    kv_issue<D>(w, i_lo + 1, q_lds[s1], do_lds[s1], lse_lds[s1], dl_lds[s1]);
+    if (extra) lds_barrier<C::LPB + 1>();
+    else lds_barrier<C::LPB>();
+  } else {
+    lds_barrier<0>();
+  }
 
-  f32x16 sd[2];   // A: S then P; B: dP then dS.  Register r of block qc is
-                  // query q_first + 32 qc + 8 (r/4) + 4 g + r%4, lane key kw0 + n.
-  uint4 pk[4];    // packed 16-bit P (A) or dS (B), query chunk kk = 2 qc + h
-  for (int i = i_lo; i < n_qblk; ++i) {
-    const int buf = i & 1;
-    const bool more = i + 1 < n_qblk;
-    if (more) load_block(i + 1);
-
-    const int q_first = i * C::BMQ;
-    const int q_last = min(q_first + C::BMQ, N) - 1;
-    const bool active = pair_live && (!CAUSAL || q_last >= kw0);
-    const bool need_mask = CAUSAL && q_first < kw0 + C::KW - 1;
-    const uint16_t* lhs = role_a ? q_lds[buf] : do_lds[buf];  // row-read operand
-    const uint16_t* rhs = role_a ? do_lds[buf] : q_lds[buf];  // transposed-read operand
-
-    // ---- phase 1: S = Q K^T (A) or dP = dO V^T (B) -------------------------
-    if (active) {
-#pragma unroll
-      for (int qc = 0; qc < 2; ++qc) {
-        sd[qc] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < C::DS; ++st)
-          sd[qc] = mma16(T{}, read_row<D>(lhs, 32 * qc + n, 16 * st + 8 * g), kv[st], sd[qc]);
-      }
-      if (role_a) {
-        const int key = kw0 + n;
-#pragma unroll
-        for (int qc = 0; qc < 2; ++qc) {
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int ql = 32 * qc + 8 * rq + 4 * g;
-            const float4 l4 = *reinterpret_cast<const float4*>(&lse_lds[buf][ql]);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float p = fast_exp2(__builtin_fmaf(sd[qc][4 * rq + e], qk_scale, -lv[e]));
-              if (need_mask) p = (key <= q_first + ql + e) ? p : 0.f;
-              sd[qc][4 * rq + e] = p;
-            }
-            x_lds[pw][4 * qc + rq][lane] =
-                make_float4(sd[qc][4 * rq], sd[qc][4 * rq + 1], sd[qc][4 * rq + 2], sd[qc][4 * rq + 3]);
-          }
-          pk[2 * qc] = pack8(T{}, sd[qc], 0);
-          pk[2 * qc + 1] = pack8(T{}, sd[qc], 1);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 2: dV += P^T dO (A) or dS, dK += dS^T Q (B) ------------------
-    if (active) {
-      if (!role_a) {
-#pragma unroll
-        for (int qc = 0; qc < 2; ++qc) {
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int ql = 32 * qc + 8 * rq + 4 * g;
-            const float4 d4 = *reinterpret_cast<const float4*>(&dl_lds[buf][ql]);
-            const float4 p4 = x_lds[pw][4 * qc + rq][lane];
-            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w}, pv[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sd[qc][4 * rq + e] = pv[e] * (sd[qc][4 * rq + e] - dv4[e]);
-          }
-          pk[2 * qc] = pack8(T{}, sd[qc], 0);
-          pk[2 * qc + 1] = pack8(T{}, sd[qc], 1);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = mma16(T{}, pk[kk], read_tr<D>(rhs, 16 * kk, 32 * db, lane), acc[db]);
-    }
-    if (more) store_block(buf ^ 1);
-    __syncthreads();
+  // Iteration i: A works on block i (slot i & 3), B on block i - 1 (slot
+  // (i - 1) & 3); block i + 2 is loaded into slot (i + 2) & 3, whose last
+  // reader (B, block i - 2) finished before the previous barrier.
+  for (int i = i_lo; i <= n_qblk; ++i) {
+    const bool ahead = i + 2 < n_qblk;
+    const int sa = i & 3, sb = (i - 1) & 3, sn = (i + 2) & 3;
+    const bool work = w.role_a ? (i < n_qblk && block_active(i)) : (i > i_lo && block_active(i - 1));
+    const int s_own = w.role_a ? sa : sb;
+    kv_iter<T, D, CAUSAL>(w, i, work, ahead, kv, acc,
+                          w.role_a ? q_lds[s_own] : do_lds[s_own],   // row-read operand
+                          w.role_a ? do_lds[s_own] : q_lds[s_own],   // transposed-read operand
+                          w.role_a ? lse_lds[s_own] : dl_lds[s_own],
+                          x_lds[i & 1][w.pw], x_lds[(i - 1) & 1][w.pw],
+                          q_lds[sn], do_lds[sn], lse_lds[sn], dl_lds[sn]);
+    // Block i + 1 (loaded one iteration ago) must be in LDS after this barrier;
+    // block i + 2's loads may stay in flight.
+    if (!ahead) lds_barrier<0>();
+    else if (extra) lds_barrier<C::LPB + 1>();
+    else lds_barrier<C::LPB>();
   }
 
   // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
-  float* out = (role_a ? dvg : dkg) + head;
-  const float sc = role_a ? 1.f : dk_scale;
+  float* out = (w.role_a ? dvg : dkg) + head;
+  const float sc = w.role_a ? 1.f : dk_scale;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + 8 * (r / 4) + 4 * g + (r % 4);
-      if (kr < N) out[(size_t)kr * D + 32 * db + n] = acc[db][r] * sc;
+      const int kr = w.kw0 + 8 * (r / 4) + 4 * w.g + (r % 4);
+      if (kr < N) out[(size_t)kr * D + 32 * db + w.n] = acc[db][r] * sc;
     }
 }
 
@@ -422,7 +468,7 @@ hipError_t run(const BwdArgs& a, int stage) {
   }
   if (stage == 0 || stage == 2) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, fabsf(a.scale), qsign);
+                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

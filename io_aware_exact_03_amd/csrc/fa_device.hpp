@@ -108,6 +108,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_void_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -121,6 +122,36 @@ __device__ __forceinline__ float4 load16f(rsrc_t r, uint32_t byte_off) {
 }
 __device__ __forceinline__ float load4f(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// Loads straight into LDS (no registers): the wave's 64 lanes each fetch
+// 16 (or 4) bytes from byte offset `byte_off` of the buffer and the hardware
+// writes lane l's bytes to dst + 16 l (or 4 l); dst must be the same for the
+// whole wave (it travels in M0).  Reads past the buffer's end write zeros.
+// The data is in LDS once this wave's vmcnt says the load has returned; other
+// waves see it after a barrier that follows that wait.  dst must be an
+// element pointer into a __shared__ array, not the bare array name.
+__device__ __forceinline__ void load_lds16(rsrc_t r, void* dst, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 16, byte_off, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(rsrc_t r, void* dst, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 4, byte_off, 0, 0, 0);
+}
+// Workgroup barrier for loops that keep loads into LDS in flight across
+// it.  __syncthreads() fences all LDS writes, including those loads, so it
+// would wait for every one of them; here the caller names how many of its
+// most recent vector-memory loads may stay outstanding (NCNT, in issue
+// order), all LDS instructions of the wave are waited for, and the empty
+// asm statements keep the compiler from moving memory accesses across the
+// barrier.  A wave that reads data loaded by another wave must do so only
+// after a barrier at which the loading wave waited for that load.
+template <int NCNT>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(NCNT >= 0 && NCNT < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0070 | NCNT);  // vmcnt(NCNT) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
