@@ -15,6 +15,13 @@ single-head forward.  `cpu_baseline` times the fp64 oracle on a sample of the
 step's heads on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Traffic counters (`roofline.traffic`): run the step under two rocprofv3
+counter passes (FETCH_SIZE, then WRITE_SIZE) with `--calib-copy-mib M`, which
+also runs an elementwise copy of M MiB of known traffic, then
+`python bench.py --traffic FETCH.csv WRITE.csv --calib-copy-mib M` writes
+profiles/traffic_<kernel>_<workload>.txt: each kernel's per-dispatch bytes
+past L2, scaled by what the same counter reads for the copy.
 """
 from __future__ import annotations
 
@@ -189,7 +196,14 @@ def main():
     ap.add_argument("--legs", type=int, default=1, help="also time the other workloads (1) or not (0)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run an elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_*.txt from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.calib_copy_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only (the attention kernels "
               f"run per (batch, head) on a single MI355X; no multi-GPU path exists)", file=sys.stderr)
@@ -227,6 +241,16 @@ def main():
             fa.bwd_stage(s, qd, kd, vd, o, dod, lse, w.scale, w.causal, delta, dq, dk, dv)
         if ev is not None:
             ev[4].record()
+
+    if args.calib_copy_mib:
+        # Counter calibration: reads and writes exactly M MiB each.
+        src = torch.ones(args.calib_copy_mib * (1 << 18), **f32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     for _ in range(args.warmup):
         step()
@@ -313,6 +337,71 @@ def main():
         "source_digest": digest,
     }
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_KERNELS = {"fwd16_kernel": "fa_fwd", "bwd_delta_kernel": "bwd_delta", "bwd_dkdv_kernel": "bwd_dkdv",
+                   "bwd_dq_kernel": "bwd_dq"}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, calib_mib: int):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each step kernel, scaled
+    by the copy's reading of the same counter, to profiles/traffic_*.txt."""
+    import csv
+
+    import fa_synth
+
+    if calib_mib <= 0:
+        sys.exit("--traffic needs the --calib-copy-mib the counter runs used")
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = next((v for k_, v in TRAFFIC_KERNELS.items() if k_ in name), None)
+            if key is None and "add" in name and "elementwise" in name:
+                key = "calib_copy"
+            if key is None:
+                continue
+            acc.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(acc)), 0.0)
+            acc[key][r.get("Dispatch_Id", len(acc))] += float(r["Counter_Value"])
+        return {k_: sum(v.values()) / len(v) for k_, v in acc.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    expect_kib = calib_mib * 1024.0
+    if "calib_copy" not in fetch or "calib_copy" not in write:
+        sys.exit("no calibration copy found in the counter files")
+    f_scale = expect_kib / fetch["calib_copy"]
+    w_scale = expect_kib / write["calib_copy"]
+    w = fa_synth.TRAIN_STEP
+    digest = source_digest()
+    for key in TRAFFIC_KERNELS.values():
+        if key not in fetch or key not in write:
+            continue
+        byts = (fetch[key] * f_scale + write[key] * w_scale) * 1024.0
+        path = os.path.join(PROFILES, f"traffic_{key}_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM-side traffic of {key} per launch on {w.name} (bytes past L2: HBM or the\n"
+                    f"# memory-side cache), from rocprofv3 counter passes over bench.py; the calibration\n"
+                    f"# copy (torch elementwise add, {calib_mib} MiB in + {calib_mib} MiB out) fixes the scale.\n"
+                    f"# Passes (repo root, TMPDIR=/tmp):\n"
+                    f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_fetch -o run -- "
+                    f"python3 bench.py --steps 2 --warmup 1 --legs 0 --cpu-baseline 0 --calib-copy-mib {calib_mib}\n"
+                    f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o run -- "
+                    f"python3 bench.py --steps 2 --warmup 1 --legs 0 --cpu-baseline 0 --calib-copy-mib {calib_mib}\n"
+                    f"#   python3 bench.py --traffic gpurun_out/traffic_fetch/run_counter_collection.csv "
+                    f"gpurun_out/traffic_write/run_counter_collection.csv --calib-copy-mib {calib_mib}\n")
+            f.write(f"fetch_kib_per_dispatch = {fetch[key]:.1f}\n")
+            f.write(f"write_kib_per_dispatch = {write[key]:.1f}\n")
+            f.write(f"calib_fetch_kib = {fetch['calib_copy']:.1f}\n")
+            f.write(f"calib_write_kib = {write['calib_copy']:.1f}\n")
+            f.write(f"fetch_scale = {f_scale:.4f}\n")
+            f.write(f"write_scale = {w_scale:.4f}\n")
+            f.write(f"hbm_bytes_per_launch = {byts:.0f}\n")
+            f.write(f"source_digest = {digest}\n")
+        print(f"wrote {path}: {byts / 1e6:.1f} MB per launch")
 
 
 def run_legs(torch, fa, fa_synth, dev):
