@@ -28,7 +28,9 @@
  *
  * Supported values.  d in {64, 128} (else FA_ERR_UNSUPPORTED); N >= 1 (any
  * value; ragged tails are masked); B, H >= 1; causal in {0, 1}; scale finite
- * (zero and negative allowed).  causal = 1 keeps key j for query i iff
+ * (zero and negative allowed).  One (batch, head) slice of Q must stay below
+ * 2 GiB, N * d * element size < 2^31 (the kernels address a head with
+ * 32-bit buffer offsets), else FA_ERR_UNSUPPORTED.  causal = 1 keeps key j for query i iff
  * j <= i (square, top-left aligned, diagonal kept).
  *
  * Ownership.  The caller allocates and frees every buffer, workspaces

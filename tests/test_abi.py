@@ -58,6 +58,14 @@ def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
 
 
+def test_head_size_limit(lib):
+    # one (batch, head) slice must stay below 2 GiB: N * d * element size < 2^31
+    assert fwd(lib, N=(1 << 31) // (128 * 2), d=128, dtype=2) == FA_ERR_UNSUPPORTED
+    assert fwd(lib, N=(1 << 31) // (64 * 4), d=64, dtype=0) == FA_ERR_UNSUPPORTED
+    args = [A] * 10
+    assert lib.fa_bwd(*args, 1, 1, (1 << 31) // (64 * 2), 64, 1.0, 0, 1, None) == FA_ERR_UNSUPPORTED
+
+
 def test_bwd_rejects(lib):
     args = [A] * 10
     base = dict(B=1, H=1, N=8, d=64, scale=1.0, causal=0, dtype=2)
