@@ -392,11 +392,17 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   wait_vmem();  // Q, dO fragments above
   __syncthreads();
 
-  for (int j = 0; j < j_end; ++j) {
+  // Blocks [0, j_unm) need no mask for this wave (every key visible to all
+  // its queries, none past the end); the rest are masked per key.  The two
+  // stages are separate loops with the mask fixed at compile time; every
+  // iteration of either ends in the same barrier, so all waves of the
+  // workgroup still meet at each block.
+  const int j_unm = min(CAUSAL ? w_s1 : n_kv, full_blocks);
+  auto block = [&](int j, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int buf = j & 1;
     const bool more = j + 1 < j_end;
     if (more) load_block(j + 1);
-    const bool need_mask = (CAUSAL && j >= w_s1) || j >= full_blocks;
     const bool active = wave_live && (!CAUSAL || j < w_s2);
     if (active) {
 #pragma unroll
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], qk_scale, -lse2));
-          if (need_mask) {
+          if constexpr (MASKED) {
             const int kr = j * C::BN + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
             p = kr < key_lim ? p : 0.f;
           }
@@ -428,7 +434,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
-  }
+  };
+  int j = 0;
+  for (; j < min(j_unm, j_end); ++j) block(j, std::false_type{});
+  for (; j < j_end; ++j) block(j, std::true_type{});
 
   if (query < N) {
     float* row = dqg + head + (size_t)query * D;
