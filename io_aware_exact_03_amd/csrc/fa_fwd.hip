@@ -200,6 +200,9 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
   };
 
   float m_run = kNegInf, l_run = 0.f;
+  // Scaled row max (log2 units) of the sub-block whose exponentials run in
+  // the next step, found in the current step and checked in the next one.
+  float m_pend = kNegInf;
   auto m_ref = [&] { return m_run == kNegInf ? 0.f : m_run; };
   // Raise the reference max if a sub-block's scores need it; rescale the
   // accumulator (only when some lane of the wave raised).
@@ -218,10 +221,20 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
   // Each phase is written as chunks of one matrix product plus its share of
   // the VALU work, fenced so the compiler keeps the interleave; LDS reads
   // run two fragments ahead of their products.
+  //
+  // The reference max for S_u is checked lazily: phase A starts the
+  // exponentials with the current reference while the compare and the
+  // wave vote on S_u's max (found in the previous step) complete under its
+  // products.  Only if some lane's max exceeds the reference by more than
+  // the slack (rare) are the reference raised, O and l rescaled and the
+  // exponentials redone from S_u, still in registers.  So the max no longer
+  // sits between two steps.
   auto step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1], int kbuf_n, int ksb_n, f32x16 (&nxt)[1],
                   auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr int EPC = 16 / DS;  // exponentials per product in phase A
+    const bool grow = m_pend > m_run + kMaxSlack;  // false while m_pend is -inf
+    const bool redo = __builtin_amdgcn_ballot_w64(grow) != 0;  // wave-uniform
     const float m_use = m_ref();
     const int kbase = key_u + 4 * g;
     const uint16_t* krow = &k_lds[kbuf_n][(32 * ksb_n + n) * C::KROW + 8 * g];
@@ -249,8 +262,19 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+    if (redo) {
+      const float m_new = grow ? m_pend : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // m_run = -inf gives 0
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      const float sum = exp_pack(key_u, cur, m_ref(), pp, masked);
+      part[0] = sum;
+      part[1] = part[2] = part[3] = 0.f;
+    }
     l_run += (part[0] + part[1]) + (part[2] + part[3]);
-    const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
     // phase B: 2 x DB products; the row max of S_{u+1} is spread over them.
     const uint16_t* vrow = &v_lds[vbuf][n * C::VROW + 32 * vsb + 8 * g];
     uint4 b[3];
@@ -289,10 +313,11 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
       }
     }
     mx = halves_max(mx);
-    update_max(mx == kNegInf ? kNegInf : mx * qk_scale);
+    m_pend = mx == kNegInf ? kNegInf : mx * qk_scale;
   };
   // The last sub-block: softmax and PV only.
   auto last_step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1]) {
+    update_max(m_pend);
     uint4 pp[2];
     l_run += exp_pack(key_u, cur, m_ref(), pp, std::true_type{});
     pv_gemm(vbuf, vsb, pp);
