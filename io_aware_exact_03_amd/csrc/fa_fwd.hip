@@ -49,42 +49,44 @@ namespace fa {
 // ===========================================================================
 // 16-bit (bf16 / fp16) forward
 // ===========================================================================
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
+// Workgroup: 8 waves x 32 queries (BM = 256, two waves per SIMD).  K/V tiles
+// of BN keys go from global memory straight into LDS (no registers), row-major
+// with the XOR chunk swizzle, into four buffers: the tile being consumed, the
+// next one (whose first score product starts in the current tile's last
+// step) and two in flight.  K feeds S^T = K Q^T with 16-byte row reads; V
+// feeds O^T += V^T P^T through transposing reads (ds_read_b64_tr_b16).
+template <typename T, int D, int BN, bool CAUSAL>
 struct Fwd16 {
-  static constexpr int NT = NW * 64;
-  static constexpr int QW = 32 * QB;        // queries per wave
-  static constexpr int BM = NW * QW;        // queries per workgroup
-  static constexpr int KROW = D + 8;        // K row stride in LDS (elements)
-  static constexpr int VROW = BN + 8;       // V^T row stride in LDS (elements)
-  static constexpr int DS = D / 16;         // k-steps of the S product
-  static constexpr int KB = BN / 32;        // 32-key blocks per K/V block
-  static constexpr int DB = D / 32;         // 32-wide d blocks of O
-  static constexpr int KCH = BN * D / 8;    // 16-byte chunks of a K block
-  static constexpr int KLD = KCH / NT;      // K chunks per thread
-  static constexpr int KPT = BN * D / 8 / NT;  // keys per thread in the V transpose
-  static_assert(KCH % NT == 0, "K block must split evenly over threads");
-  static_assert(KPT == 2 || KPT == 4, "V transpose packs 2 or 4 keys per thread");
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static constexpr int LDS_K = BN * KROW;   // elements per K buffer
-  static constexpr int LDS_V = D * VROW;    // elements per V^T buffer
+  static constexpr int NW = 8, NT = NW * 64, BM = NW * 32;
+  static constexpr int DS = D / 16;          // k-steps of the S product
+  static constexpr int DB = D / 32;          // 32-wide d blocks of O
+  static constexpr int SUB = BN / 32;        // 32-key sub-blocks per tile
+  static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+  static constexpr int RPP = 64 / CPR;       // tile rows per 1 KB wave load
+  static constexpr int PPT = BN / RPP;       // 1 KB pieces per K (or V) tile
+  static constexpr int LPW = 2 * PPT / NW;   // loads per wave per tile
+  static constexpr int NBUF = 4;
+  static_assert(SUB % 2 == 0, "score registers alternate per sub-block");
+  static_assert(LPW >= 1 && LPW * NW == 2 * PPT, "tile loads split evenly over waves");
+  static_assert(LPW < 16, "vmcnt range");
 };
 
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd16_kernel(
-    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, float qk_scale,
-    uint32_t qsign) {
-  using C = Fwd16<T, D, BN, NW, QB, CAUSAL>;
-  static_assert(QB == 1, "one 32-query block per wave");
-  constexpr int KB = C::KB, DB = C::DB, DS = C::DS;
-  // Three K/V buffers: iteration j reads K_{j+1} and V_j while block j+2 is
-  // staged into the third.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][C::LDS_K];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[3][C::LDS_V];
+// A sub-block's weights p = exp2(S q - m) are accepted when this lane's sum
+// of its 16 weights stays at or below 2^8 (so every weight does); otherwise
+// the reference max is raised to the true row max and the weights are redone.
+constexpr float kSumLimit = 256.f;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+template <typename T, int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512) void fwd16_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, float qk_scale, uint32_t qsign) {
+  using C = Fwd16<T, D, BN, CAUSAL>;
+  constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::NBUF][BN * D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int g = lane >> 5;
 
@@ -97,12 +99,12 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
   const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
 
   const int q0 = qblk * C::BM;
-  const int qw0 = q0 + wave * C::QW;  // first query of this wave
-  const int query = qw0 + n;          // this lane's query
+  const int qw0 = q0 + 32 * wave;  // first query of this wave
+  const int query = qw0 + n;       // this lane's query
 
   // ---- Q fragments, held in registers for the whole kernel --------------
   // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
-  // rows past N read as zeros.
+  // rows past N read as zeros.  A negative scale flips Q's sign bits.
   uint4 qf[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
@@ -111,281 +113,216 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     qf[s] = x;
   }
 
-  // ---- key-block plan ---------------------------------------------------
-  // Blocks [0, j_unm) hold only keys visible to every query of the
-  // workgroup and lie before the sequence tail: no mask (the pages'
-  // unmasked stage).  Blocks [j_unm, j_end) straddle the diagonal or hold
-  // the tail and are masked per key.  Blocks from j_end on are never read.
-  const int n_kv = (N + BN - 1) / BN;
-  const int full_blocks = N / BN;
-  int j_end = n_kv, j_unm = full_blocks;
-  if (CAUSAL) {
-    j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / BN + 1);
-    int s1, s2;
-    causal_stages(q0, min(q0 + C::BM, N), BN, &s1, &s2);
-    j_unm = min(s1, full_blocks);
-  }
+  // ---- key plan ------------------------------------------------------------
+  // The wave's queries see the 32-key sub-blocks [0, u_last].  Every
+  // sub-block before u_last is visible to all of them and lies before the
+  // sequence end, so only u_last is masked: for the causal case it is the
+  // diagonal sub-block (keys qw0 .. qw0 + 31, the pages' masked stage),
+  // otherwise the sub-block holding the sequence tail.  Sub-blocks after
+  // u_last (the future) are never computed.  A wave whose queries all lie
+  // past N (u_last = -1) only helps load tiles.
+  const int n_sub = (N + 31) / 32;
+  const bool wave_live = qw0 < N;
+  const int u_last = !wave_live ? -1 : (CAUSAL ? qw0 / 32 : n_sub - 1);
+  const int last_live = min(C::NW - 1, (N - 1 - q0) / 32);  // q0 < N always
+  const int u_end = CAUSAL ? (q0 / 32 + last_live) : (n_sub - 1);
+  const int j_end = u_end / SUB + 1;  // tiles this workgroup reads
   const int key_lim = CAUSAL ? min(query + 1, N) : N;
 
-  // ---- global -> register -> LDS staging of one K/V block -----------------
-  uint4 kst[C::KLD];
-  uint4 vst[C::KPT];
-  const int va = tid % (BN / C::KPT);   // key group of this thread
-  const int vdc = tid / (BN / C::KPT);  // d chunk (8 elements) of this thread
-  auto load_block = [&](int j) {
-    const uint32_t key0 = j * BN;
+  // ---- tile loads: global -> LDS ------------------------------------------
+  // Piece t (0 .. 2 PPT - 1) = wave LPW + e holds RPP tile rows of K
+  // (t < PPT) or V.  Lane l fills LDS bytes 16 l of the piece: row l / CPR,
+  // stored chunk l % CPR, which holds the row's logical chunk
+  // (l % CPR) ^ swz_chunk(row).  Rows past N read as zeros.
+  auto issue = [&](int j, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
+    const int lrow = lane / C::CPR;
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int c = tid + i * C::NT;
-      const uint32_t row = key0 + c / (D / 8), col = (c % (D / 8)) * 8;
-      kst[i] = load16(krs, (row * D + col) * 2);
+    for (int e = 0; e < C::LPW; ++e) {
+      const int t = wave * C::LPW + e;
+      const int p = t % C::PPT;
+      const int row = p * C::RPP + lrow;
+      const int chunk = (lane % C::CPR) ^ swz_chunk<D>(row);
+      const uint32_t off = ((uint32_t)(j * BN + row) * D + 8 * chunk) * 2;
+      if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
+      else load_lds16(vrs, vd + p * C::RPP * D, off);
     }
-#pragma unroll
-    for (int e = 0; e < C::KPT; ++e) {
-      const uint32_t row = key0 + C::KPT * va + e;
-      vst[e] = load16(vrs, (row * D + 8 * vdc) * 2);
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int c = tid + i * C::NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[buf][row * C::KROW + col]) = kst[i];
-    }
-    // V^T: KPT keys x 8 d of V become 8 rows of V^T (keys in tpos order).
-    store_transposed<C::KPT>(&v_lds[buf][8 * vdc * C::VROW], C::VROW, tpos(C::KPT * va), vst);
   };
 
-  // ---- pieces of one 32-key sub-block --------------------------------------
-  // A K/V tile of BN keys holds SUB = BN/32 sub-blocks; sub-block u is
-  // sub-block u % SUB of tile u / SUB.  The softmax pipeline runs per
-  // sub-block (two 16-register score sets in flight); barriers and staging
-  // run per tile.
-  constexpr int SUB = BN / 32;
-  // S^T = K Q^T for sub-block `sb` of tile buffer `buf` (32 keys x 32 queries).
-  auto s_gemm = [&](int buf, int sb, f32x16 (&s)[1]) {
-#pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[buf][(32 * sb + n) * C::KROW + 16 * st + 8 * g]);
-      s[0] = mma16(T{}, a, qf[st], st == 0 ? f32x16{} : s[0]);
-    }
-  };
-  // p = exp2(S * qk_scale - m) packed to 16-bit (the B operand of the PV
-  // product); returns this lane's sum of p.  key0 = first key of the sub-block.
-  auto exp_pack = [&](int key0, f32x16 (&s)[1], float m_use, uint4 (&pp)[2], auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const float sum = tile_exp<1, MASKED>(s, qk_scale, m_use, key0 + 4 * g, key_lim);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x16& v = s[0];
-      pp[h] = make_uint4(pack2(T{}, v[8 * h + 0], v[8 * h + 1]), pack2(T{}, v[8 * h + 2], v[8 * h + 3]),
-                         pack2(T{}, v[8 * h + 4], v[8 * h + 5]), pack2(T{}, v[8 * h + 6], v[8 * h + 7]));
-    }
-    return sum;
-  };
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  // O^T += V^T P^T for sub-block `sb` of tile buffer `buf`.
-  auto pv_gemm = [&](int buf, int sb, const uint4 (&pp)[2]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint4 a =
-            *reinterpret_cast<const uint4*>(&v_lds[buf][(32 * db + n) * C::VROW + 32 * sb + 16 * h + 8 * g]);
-        oacc[db] = mma16(T{}, a, pp[h], oacc[db]);
-      }
-  };
+  float m_run = 0.f, l_run = 0.f;  // m_run: reference max, log2 units
+  f32x16 sA, sB;                    // scores of even / odd sub-blocks
 
-  float m_run = kNegInf, l_run = 0.f;
-  // Scaled row max (log2 units) of the sub-block whose exponentials run in
-  // the next step, found in the current step and checked in the next one.
-  float m_pend = kNegInf;
-  auto m_ref = [&] { return m_run == kNegInf ? 0.f : m_run; };
-  // Raise the reference max if a sub-block's scores need it; rescale the
-  // accumulator (only when some lane of the wave raised).
-  auto update_max = [&](float mt) {
-    float alpha;
-    if (raise_max(mt, m_run, l_run, &alpha)) {
+  // S^T of one sub-block (32 keys x 32 queries) from rows 32 sb .. of a K tile.
+  auto s_gemm = [&](const uint16_t* kt, int sb, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    for (int st = 0; st < DS; ++st)
+      s = mma16(T{}, read_row<D>(kt, 32 * sb + n, 16 * st + 8 * g), qf[st], st == 0 ? f32x16{} : s);
+  };
+  // Weights of sub-block `cur` (first key key0) with the current reference,
+  // packed to 16-bit as the B operand of the PV product; returns the lane sum.
+  auto exp_pack = [&](const f32x16& cur, int key0, uint32_t (&pk)[8], auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
+      float p1 = fast_exp2(__builtin_fmaf(cur[r + 1], qk_scale, -m_run));
+      if constexpr (MASKED) {
+        const int kb = key0 + 4 * g + 8 * (r / 4) + (r % 4);
+        p0 = kb < key_lim ? p0 : 0.f;
+        p1 = kb + 1 < key_lim ? p1 : 0.f;
+      }
+      part[r % 4] += p0;
+      part[(r + 1) % 4] += p1;
+      pk[r / 2] = pack2(T{}, p0, p1);
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+  // Rare path: some lane's weights exceeded the limit.  Raise the reference
+  // to the true row max of this sub-block where it is higher, rescale O and
+  // l, and redo the weights.  Exact: O, l and the LSE share the reference.
+  auto raise_redo = [&](const f32x16& cur, int key0, uint32_t (&pk)[8], auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16 c1[1] = {cur};
+    const float mt = tile_max<1, MASKED>(c1, qk_scale, key0 + 4 * g, key_lim);
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    return exp_pack(cur, key0, pk, masked);
+  };
+  // O^T += V^T P^T over sub-block sb of a V tile.
+  auto pv_gemm = [&](const uint16_t* vt, int sb, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
+    const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+    constexpr int NB = 2 * DB;  // product i: 16-key half i / DB, d block i % DB
+    uint4 b[3];
+    b[0] = read_tr<D>(vt, 32 * sb, 0, lane);
+    b[1] = read_tr<D>(vt, 32 * sb + 16 * (1 / DB), 32 * (1 % DB), lane);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + 2 < NB) b[(i + 2) % 3] = read_tr<D>(vt, 32 * sb + 16 * ((i + 2) / DB), 32 * ((i + 2) % DB), lane);
+      oacc[i % DB] = mma16(T{}, b[i % 3], pp[i / DB], oacc[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // One pipeline step: sub-block u's softmax and PV product, overlapped with
-  // sub-block u+1's score product and row max.
-  //   phase A: S_{u+1} = K Q^T   ||  p_u = exp2(S_u - m), packed
-  //   phase B: O += V P_u        ||  rowmax(S_{u+1})
-  // Each phase is written as chunks of one matrix product plus its share of
-  // the VALU work, fenced so the compiler keeps the interleave; LDS reads
-  // run two fragments ahead of their products.
-  //
-  // The reference max for S_u is checked lazily: phase A starts the
-  // exponentials with the current reference while the compare and the
-  // wave vote on S_u's max (found in the previous step) complete under its
-  // products.  Only if some lane's max exceeds the reference by more than
-  // the slack (rare) are the reference raised, O and l rescaled and the
-  // exponentials redone from S_u, still in registers.  So the max no longer
-  // sits between two steps.
-  auto step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1], int kbuf_n, int ksb_n, f32x16 (&nxt)[1],
-                  auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    constexpr int EPC = 16 / DS;  // exponentials per product in phase A
-    const bool grow = m_pend > m_run + kMaxSlack;  // false while m_pend is -inf
-    const bool redo = __builtin_amdgcn_ballot_w64(grow) != 0;  // wave-uniform
-    const float m_use = m_ref();
-    const int kbase = key_u + 4 * g;
-    const uint16_t* krow = &k_lds[kbuf_n][(32 * ksb_n + n) * C::KROW + 8 * g];
-    uint4 a[3];
-    a[0] = *reinterpret_cast<const uint4*>(krow);
-    a[1] = *reinterpret_cast<const uint4*>(krow + 16);
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  // One pipeline step for an unmasked sub-block u (scores in `cur`): the
+  // score product of sub-block u+1 (K rows 32 nsb.. of tile kt_n) is issued in
+  // DS chunks, each followed by its share of u's exponentials, so matrix
+  // products and vector work overlap inside the wave; then the limit check
+  // and the PV product of u.
+  auto step = [&](const f32x16& cur, int key0, f32x16& nxt, const uint16_t* kt_n, int nsb, const uint16_t* vt,
+                  int sb) __attribute__((always_inline)) {
+    constexpr int EPC = 16 / DS;  // weights per product
+    const uint16_t* krow = kt_n + 0;  // rows of sub-block nsb
+    float part[4];
     uint32_t pk[8];
+    uint4 a[3];
+    a[0] = read_row<D>(krow, 32 * nsb + n, 8 * g);
+    a[1] = read_row<D>(krow, 32 * nsb + n, 16 + 8 * g);
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
-      if (st + 2 < DS) a[(st + 2) % 3] = *reinterpret_cast<const uint4*>(krow + 16 * (st + 2));
-      nxt[0] = mma16(T{}, a[st % 3], qf[st], st == 0 ? f32x16{} : nxt[0]);
+      if (st + 2 < DS) a[(st + 2) % 3] = read_row<D>(krow, 32 * nsb + n, 16 * (st + 2) + 8 * g);
+      nxt = mma16(T{}, a[st % 3], qf[st], st == 0 ? f32x16{} : nxt);
 #pragma unroll
       for (int e = 0; e < EPC; e += 2) {
-        const int r = st * EPC + e;  // registers r, r+1 of cur
-        float p0 = fast_exp2(__builtin_fmaf(cur[0][r], qk_scale, -m_use));
-        float p1 = fast_exp2(__builtin_fmaf(cur[0][r + 1], qk_scale, -m_use));
-        if constexpr (MASKED) {
-          p0 = kbase + 8 * (r / 4) + (r % 4) < key_lim ? p0 : 0.f;
-          p1 = kbase + 8 * ((r + 1) / 4) + ((r + 1) % 4) < key_lim ? p1 : 0.f;
-        }
-        part[r % 4] += p0;
-        part[(r + 1) % 4] += p1;
+        const int r = st * EPC + e;
+        const float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
+        const float p1 = fast_exp2(__builtin_fmaf(cur[r + 1], qk_scale, -m_run));
+        part[r % 4] = r < 4 ? p0 : part[r % 4] + p0;
+        part[(r + 1) % 4] = r < 4 ? p1 : part[(r + 1) % 4] + p1;
         pk[r / 2] = pack2(T{}, p0, p1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
-    if (redo) {
-      const float m_new = grow ? m_pend : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // m_run = -inf gives 0
-      l_run *= alpha;
-      m_run = m_new;
+    // The rare redo below rebuilds pk; this use keeps the compiler from
+    // moving the packs into the common branch, out of the interleave.
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      const float sum = exp_pack(key_u, cur, m_ref(), pp, masked);
-      part[0] = sum;
-      part[1] = part[2] = part[3] = 0.f;
-    }
-    l_run += (part[0] + part[1]) + (part[2] + part[3]);
-    // phase B: 2 x DB products; the row max of S_{u+1} is spread over them.
-    const uint16_t* vrow = &v_lds[vbuf][n * C::VROW + 32 * vsb + 8 * g];
-    uint4 b[3];
-    b[0] = *reinterpret_cast<const uint4*>(vrow);
-    b[1] = *reinterpret_cast<const uint4*>(vrow + 32 * C::VROW);
-    constexpr int NB = 2 * DB;  // products in phase B, index i -> (h = i / DB, db = i % DB)
-    constexpr int MPC = (16 + NB - 1) / NB;  // S_{u+1} registers folded into the max per product
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i + 2 < NB) {
-        const int h = (i + 2) / DB, db = (i + 2) % DB;
-        b[(i + 2) % 3] = *reinterpret_cast<const uint4*>(vrow + 32 * db * C::VROW + 16 * h);
-      }
-      oacc[i % DB] = mma16(T{}, b[i % 3], pp[i / DB], oacc[i % DB]);
-      if (i >= 1) {  // S_{u+1} is complete once phase A's products drained
-#pragma unroll
-        for (int r = (i - 1) * MPC; r < i * MPC && r < 16; ++r) {
-          if constexpr (MASKED) {
-            const int key = kbase + 32 + 8 * (r / 4) + (r % 4);
-            mx = fmaxf(mx, key < key_lim ? nxt[0][r] : kNegInf);
-          } else {
-            mx = fmaxf(mx, nxt[0][r]);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int r = (NB - 1) * MPC; r < 16; ++r) {
-      if constexpr (MASKED) {
-        const int key = kbase + 32 + 8 * (r / 4) + (r % 4);
-        mx = fmaxf(mx, key < key_lim ? nxt[0][r] : kNegInf);
-      } else {
-        mx = fmaxf(mx, nxt[0][r]);
-      }
-    }
-    mx = halves_max(mx);
-    m_pend = mx == kNegInf ? kNegInf : mx * qk_scale;
+    for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[i]));
+    float lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) lsum = raise_redo(cur, key0, pk, std::false_type{});
+    l_run += lsum;
+    pv_gemm(vt, sb, pk);
   };
-  // The last sub-block: softmax and PV only.
-  auto last_step = [&](int key_u, int vbuf, int vsb, f32x16 (&cur)[1]) {
-    update_max(m_pend);
-    uint4 pp[2];
-    l_run += exp_pack(key_u, cur, m_ref(), pp, std::true_type{});
-    pv_gemm(vbuf, vsb, pp);
+  // The wave's last sub-block: masked weights and the PV product only.
+  auto last_step = [&](const f32x16& cur, int key0, const uint16_t* vt, int sb) __attribute__((always_inline)) {
+    uint32_t pk[8];
+    float lsum = exp_pack(cur, key0, pk, std::true_type{});
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) lsum = raise_redo(cur, key0, pk, std::true_type{});
+    l_run += lsum;
+    pv_gemm(vt, sb, pk);
   };
 
-  // One tile j (tiles j and j+1 are in LDS at buffers b0, b1): its SUB
-  // pipeline steps, the last of which starts on tile j+1; tile j+2 is staged
-  // into the third buffer meanwhile.
-  f32x16 sA[1], sB[1];  // sub-blocks with even / odd index
-  // With an odd number of sub-blocks per tile the register roles swap from
-  // one tile to the next, so the tile body exists in both orders.
-  auto tile_iter_p = [&](int j, auto masked, f32x16 (&e)[1], f32x16 (&o)[1]) {
-    const bool stage = j + 2 < j_end;
-    if (stage) load_block(j + 2);
-    const int b0 = j % 3, b1 = b0 == 2 ? 0 : b0 + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+  // One tile j: this wave's unmasked sub-blocks of it, and the loads of
+  // tile j + 3.  The tiles arrive as separate __restrict__ pointers, which
+  // tells the compiler that the loads into kl / vl do not alias the tiles
+  // read here, so it does not wait for them before each LDS read.
+  auto tile = [&](int j, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                  const uint16_t* __restrict__ kn, uint16_t* __restrict__ kl, uint16_t* __restrict__ vl,
+                  bool load) __attribute__((always_inline)) {
+    if (load) issue(j + 3, kl, vl);
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-      const int key_u = j * BN + 32 * i;
-      const int kb_n = i + 1 < SUB ? b0 : b1, ks_n = i + 1 < SUB ? i + 1 : 0;
-      if (i % 2 == 0) step(key_u, b0, i, e, kb_n, ks_n, o, masked);
-      else step(key_u, b0, i, o, kb_n, ks_n, e, masked);
+      const int u = j * SUB + i;
+      f32x16& cur = (i % 2 == 0) ? sA : sB;
+      f32x16& nxt = (i % 2 == 0) ? sB : sA;
+      if (u < u_last) {
+        if (i + 1 < SUB) step(cur, 32 * u, nxt, kc, i + 1, vc, i);
+        else step(cur, 32 * u, nxt, kn, 0, vc, i);
+      }
     }
-    if (stage) store_block(b2);
-    __syncthreads();
-  };
-  auto tile_iter = [&](int j, auto masked) {
-    if ((SUB % 2 == 1) && (j & 1)) tile_iter_p(j, masked, sB, sA);
-    else tile_iter_p(j, masked, sA, sB);
   };
 
-  // ---- prologue: tiles 0 and 1 into LDS, S of sub-block 0 and its max ------
-  load_block(0);
-  store_block(0);
-  if (j_end > 1) {
-    load_block(1);
-    store_block(1);
+  // ---- prologue: tiles 0..2 in flight, wait for 0 and 1 ------------------
+  issue(0, k_lds[0], v_lds[0]);
+  if (j_end > 1) issue(1, k_lds[1], v_lds[1]);
+  if (j_end > 2) {
+    issue(2, k_lds[2], v_lds[2]);
+    lds_barrier<C::LPW>();
+  } else {
+    lds_barrier<0>();
   }
-  __syncthreads();
-  s_gemm(0, 0, sA);
-  if (0 < j_unm) update_max(tile_max<1, false>(sA, qk_scale, 4 * g, key_lim));
-  else update_max(tile_max<1, true>(sA, qk_scale, 4 * g, key_lim));
+  if (wave_live) {
+    s_gemm(k_lds[0], 0, sA);
+    f32x16 s1[1] = {sA};
+    m_run = tile_max<1, true>(s1, qk_scale, 4 * g, key_lim);  // key 0 is visible to every query
+  }
 
-  // ---- main loop over tiles that have a next tile ---------------------------
-  int j = 0;
-  for (; j + 1 < j_unm; ++j) tile_iter(j, std::false_type{});  // tiles j, j+1 unmasked
-  for (; j + 1 < j_end; ++j) tile_iter(j, std::true_type{});
-  // ---- last tile: its sub-blocks, the final one without a successor -------
-  auto last_tile = [&](f32x16 (&e)[1], f32x16 (&o)[1]) {
-    const int b0 = j % 3;
+  // ---- main loop, unrolled over the four buffers so that every LDS offset
+  // is a compile-time immediate ---------------------------------------------
+  for (int j0 = 0; j0 < j_end; j0 += C::NBUF) {
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) {
-      const int key_u = j * BN + 32 * i;
-      if (i + 1 < SUB) {
-        if (i % 2 == 0) step(key_u, b0, i, e, b0, i + 1, o, std::true_type{});
-        else step(key_u, b0, i, o, b0, i + 1, e, std::true_type{});
-      } else {
-        if (i % 2 == 0) last_step(key_u, b0, i, e);
-        else last_step(key_u, b0, i, o);
+    for (int jj = 0; jj < C::NBUF; ++jj) {
+      const int j = j0 + jj;
+      if (j < j_end) {
+        const bool load = j + 3 < j_end;
+        tile(j, k_lds[jj], v_lds[jj], k_lds[(jj + 1) % C::NBUF], k_lds[(jj + 3) % C::NBUF],
+             v_lds[(jj + 3) % C::NBUF], load);
+        // Tiles j + 1 and j + 2 must be in LDS after this barrier; tile
+        // j + 3's loads may stay in flight.
+        if (load) lds_barrier<C::LPW>();
+        else lds_barrier<0>();
       }
     }
-  };
-  if ((SUB % 2 == 1) && (j & 1)) last_tile(sB, sA);
-  else last_tile(sA, sB);
+  }
+  // The wave's last (masked) sub-block.  Its tile is among the last four
+  // of the workgroup (a wave's last sub-block is at most seven sub-blocks
+  // before the workgroup's), so it is still in LDS: no load was issued
+  // after the final one.
+  if (wave_live) {
+    const uint16_t* vt = v_lds[(u_last / SUB) % C::NBUF];
+    if (u_last % 2 == 0) last_step(sA, 32 * u_last, vt, u_last % SUB);
+    else last_step(sB, 32 * u_last, vt, u_last % SUB);
+  }
 
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
-  if (query < N) {
+  if (wave_live && query < N) {
     uint16_t* orow = og + head + (size_t)query * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -400,7 +337,6 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(
     if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
-
 // ===========================================================================
 // fp32 forward: same structure on v_mfma_f32_32x32x2_f32, P kept in fp32.
 // ===========================================================================
@@ -569,23 +505,22 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 // ===========================================================================
 namespace {
 
-// Tile per head dim: 8 waves x 32 queries (two waves per SIMD, so one wave's
-// softmax overlaps the other's matrix products), 64 keys per block for
-// d = 128 and 128 for d = 64.  Must agree with fwd_tile() in fa_plan.hpp.
+// Tile per head dim: 8 waves x 32 queries (two waves per SIMD), 64 keys per
+// tile for d = 128 and 128 for d = 64 (16 KB of K and of V per tile either
+// way).  Must agree with fwd_tile() in fa_plan.hpp.
 template <int D>
 struct Tile16 {
-  static constexpr int NW = 8, QB = 1;
   static constexpr int BN = D == 128 ? 64 : 128;
 };
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const FwdArgs& a) {
-  constexpr int BN = Tile16<D>::BN, NW = Tile16<D>::NW, QB = Tile16<D>::QB;
-  using C = Fwd16<T, D, BN, NW, QB, CAUSAL>;
+  constexpr int BN = Tile16<D>::BN;
+  using C = Fwd16<T, D, BN, CAUSAL>;
   const int n_qblk = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)n_qblk * a.BH;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, BN, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
+  hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk,
                      a.qk_scale, a.neg ? 0x80008000u : 0u);
