@@ -65,7 +65,7 @@ struct Fwd16 {
   static constexpr int RPP = 64 / CPR;       // tile rows per 1 KB wave load
   static constexpr int PPT = BN / RPP;       // 1 KB pieces per K (or V) tile
   static constexpr int LPW = 2 * PPT / NW;   // loads per wave per tile
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = 5;
   static_assert(SUB % 2 == 0, "score registers alternate per sub-block");
   static_assert(LPW >= 1 && LPW * NW == 2 * PPT, "tile loads split evenly over waves");
   static_assert(LPW < 16, "vmcnt range");
@@ -195,84 +195,108 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     return exp_pack(cur, key0, pk, masked);
   };
-  // O^T += V^T P^T over sub-block sb of a V tile.
+  // Accept the weights of a sub-block, or raise the reference and redo them.
+  auto settle = [&](const f32x16& cur, int key0, uint32_t (&pk)[8], float lsum, auto masked)
+      __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) lsum = raise_redo(cur, key0, pk, masked);
+    l_run += lsum;
+  };
+
+  // Operand fragments.  Product k (0 .. NS-1) of a sub-block's score product
+  // takes K rows 32 sb + n, columns 16 k + 8 g; product k of its PV product
+  // takes the 16 keys 16 (k / DB) .. of the sub-block, d block k % DB.
+  constexpr int NS = DS;  // = 2 DB: both products of a sub-block have NS steps
+  static_assert(NS == 2 * DB, "slot pairing");
+  auto kfrag = [&](const uint16_t* kt, int sb, int k) __attribute__((always_inline)) {
+    return read_row<D>(kt, 32 * sb + n, 16 * k + 8 * g);
+  };
+  auto vfrag = [&](const uint16_t* vt, int sb, int k) __attribute__((always_inline)) {
+    return read_tr<D>(vt, 32 * sb + 16 * (k / DB), 32 * (k % DB), lane);
+  };
+  // O^T += V^T P^T over one sub-block, not overlapped (the wave's last ones).
   auto pv_gemm = [&](const uint16_t* vt, int sb, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
     const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
-    constexpr int NB = 2 * DB;  // product i: 16-key half i / DB, d block i % DB
     uint4 b[3];
-    b[0] = read_tr<D>(vt, 32 * sb, 0, lane);
-    b[1] = read_tr<D>(vt, 32 * sb + 16 * (1 / DB), 32 * (1 % DB), lane);
+    b[0] = vfrag(vt, sb, 0);
+    b[1] = vfrag(vt, sb, 1);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i + 2 < NB) b[(i + 2) % 3] = read_tr<D>(vt, 32 * sb + 16 * ((i + 2) / DB), 32 * ((i + 2) % DB), lane);
-      oacc[i % DB] = mma16(T{}, b[i % 3], pp[i / DB], oacc[i % DB]);
+    for (int k = 0; k < NS; ++k) {
+      if (k + 2 < NS) b[(k + 2) % 3] = vfrag(vt, sb, k + 2);
+      oacc[k % DB] = mma16(T{}, b[k % 3], pp[k / DB], oacc[k % DB]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // One pipeline step for an unmasked sub-block u (scores in `cur`): the
-  // score product of sub-block u+1 (K rows 32 nsb.. of tile kt_n) is issued in
-  // DS chunks, each followed by its share of u's exponentials, so matrix
-  // products and vector work overlap inside the wave; then the limit check
-  // and the PV product of u.
-  auto step = [&](const f32x16& cur, int key0, f32x16& nxt, const uint16_t* kt_n, int nsb, const uint16_t* vt,
-                  int sb) __attribute__((always_inline)) {
-    constexpr int EPC = 16 / DS;  // weights per product
-    const uint16_t* krow = kt_n + 0;  // rows of sub-block nsb
+  // Software pipeline over the wave's sub-blocks.  Step u issues, in NS
+  // slots, the score product of sub-block u+1 and the PV product of u-1,
+  // one matrix product of each per slot, and spreads the weights of u (whose
+  // scores the previous step produced) evenly over the slots, so the vector
+  // and transcendental work hides under the matrix products.  LDS reads run
+  // two slots ahead and cross into the next step: ka / vb carry the first
+  // two K and V fragments the next step consumes.
+  uint4 ka[2], vb[2];
+  uint32_t pkp[8];  // packed weights of sub-block u-1
+  auto step = [&](f32x16& cur, int key0, f32x16& nxt, const uint16_t* kt, int ksb, const uint16_t* vt, int vsb,
+                  const uint16_t* kt2, int ksb2, const uint16_t* vt2, int vsb2, auto with_pv)
+      __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value;
+    constexpr int EPS = 16 / NS;  // weights per slot
+    const uint4 pp[2] = {make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]), make_uint4(pkp[4], pkp[5], pkp[6], pkp[7])};
+    uint4 a[3] = {ka[0], ka[1], ka[1]};
+    uint4 b[3] = {vb[0], vb[1], vb[1]};
     float part[4];
     uint32_t pk[8];
-    uint4 a[3];
-    a[0] = read_row<D>(krow, 32 * nsb + n, 8 * g);
-    a[1] = read_row<D>(krow, 32 * nsb + n, 16 + 8 * g);
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      if (st + 2 < DS) a[(st + 2) % 3] = read_row<D>(krow, 32 * nsb + n, 16 * (st + 2) + 8 * g);
-      nxt = mma16(T{}, a[st % 3], qf[st], st == 0 ? f32x16{} : nxt);
+    for (int k = 0; k < NS; ++k) {
+      if (k + 2 < NS) {
+        a[(k + 2) % 3] = kfrag(kt, ksb, k + 2);
+        if constexpr (PV) b[(k + 2) % 3] = vfrag(vt, vsb, k + 2);
+      } else {
+        ka[k + 2 - NS] = kfrag(kt2, ksb2, k + 2 - NS);
+        vb[k + 2 - NS] = vfrag(vt2, vsb2, k + 2 - NS);
+      }
+      nxt = mma16(T{}, a[k % 3], qf[k], k == 0 ? f32x16{} : nxt);
 #pragma unroll
-      for (int e = 0; e < EPC; e += 2) {
-        const int r = st * EPC + e;
+      for (int e = 0; e < EPS; e += 2) {
+        const int r = k * EPS + e;
         const float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
         const float p1 = fast_exp2(__builtin_fmaf(cur[r + 1], qk_scale, -m_run));
         part[r % 4] = r < 4 ? p0 : part[r % 4] + p0;
         part[(r + 1) % 4] = r < 4 ? p1 : part[(r + 1) % 4] + p1;
         pk[r / 2] = pack2(T{}, p0, p1);
       }
+      if constexpr (PV) oacc[k % DB] = mma16(T{}, b[k % 3], pp[k / DB], oacc[k % DB]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // The rare redo below rebuilds pk; this use keeps the compiler from
-    // moving the packs into the common branch, out of the interleave.
+    // The rare redo rebuilds pk; this use keeps the compiler from moving the
+    // packs into the common branch, out of the interleave.
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[i]));
-    float lsum = (part[0] + part[1]) + (part[2] + part[3]);
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) lsum = raise_redo(cur, key0, pk, std::false_type{});
-    l_run += lsum;
-    pv_gemm(vt, sb, pk);
-  };
-  // The wave's last sub-block: masked weights and the PV product only.
-  auto last_step = [&](const f32x16& cur, int key0, const uint16_t* vt, int sb) __attribute__((always_inline)) {
-    uint32_t pk[8];
-    float lsum = exp_pack(cur, key0, pk, std::true_type{});
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) lsum = raise_redo(cur, key0, pk, std::true_type{});
-    l_run += lsum;
-    pv_gemm(vt, sb, pk);
+    settle(cur, key0, pk, (part[0] + part[1]) + (part[2] + part[3]), std::false_type{});
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pkp[i] = pk[i];
   };
 
-  // One tile j: this wave's unmasked sub-blocks of it, and the loads of
+  // One tile j (buffers: kc / vc this tile, kn the next, vp the previous):
+  // this wave's steps u = j SUB + i with 1 <= u < u_last, and the loads of
   // tile j + 3.  The tiles arrive as separate __restrict__ pointers, which
   // tells the compiler that the loads into kl / vl do not alias the tiles
   // read here, so it does not wait for them before each LDS read.
   auto tile = [&](int j, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-                  const uint16_t* __restrict__ kn, uint16_t* __restrict__ kl, uint16_t* __restrict__ vl,
-                  bool load) __attribute__((always_inline)) {
+                  const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vp, uint16_t* __restrict__ kl,
+                  uint16_t* __restrict__ vl, bool load) __attribute__((always_inline)) {
     if (load) issue(j + 3, kl, vl);
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
       const int u = j * SUB + i;
       f32x16& cur = (i % 2 == 0) ? sA : sB;
       f32x16& nxt = (i % 2 == 0) ? sB : sA;
-      if (u < u_last) {
-        if (i + 1 < SUB) step(cur, 32 * u, nxt, kc, i + 1, vc, i);
-        else step(cur, 32 * u, nxt, kn, 0, vc, i);
+      if (u >= 1 && u < u_last) {
+        const uint16_t* kt = i + 1 < SUB ? kc : kn;        // sub-block u + 1
+        const uint16_t* vt = i >= 1 ? vc : vp;             // sub-block u - 1
+        const uint16_t* kt2 = i + 2 < SUB ? kc : kn;       // sub-block u + 2
+        step(cur, 32 * u, nxt, kt, (i + 1) % SUB, vt, (i + SUB - 1) % SUB, kt2, (i + 2) % SUB, vc, i,
+             std::true_type{});
       }
     }
   };
@@ -290,18 +314,26 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     s_gemm(k_lds[0], 0, sA);
     f32x16 s1[1] = {sA};
     m_run = tile_max<1, true>(s1, qk_scale, 4 * g, key_lim);  // key 0 is visible to every query
+    if (u_last >= 1) {
+      // step 0: scores of sub-block 1, weights of 0, no PV product yet
+      const uint16_t* k2 = k_lds[2 / SUB];
+      ka[0] = kfrag(k_lds[0], 1, 0);
+      ka[1] = kfrag(k_lds[0], 1, 1);
+      step(sA, 0, sB, k_lds[0], 1, v_lds[0], 0, k2, 2 % SUB, v_lds[0], 0, std::false_type{});
+    }
   }
 
-  // ---- main loop, unrolled over the four buffers so that every LDS offset
-  // is a compile-time immediate ---------------------------------------------
-  for (int j0 = 0; j0 < j_end; j0 += C::NBUF) {
+  // ---- main loop, unrolled over the buffers so that every LDS offset is a
+  // compile-time immediate ---------------------------------------------------
+  constexpr int NB5 = C::NBUF;
+  for (int j0 = 0; j0 < j_end; j0 += NB5) {
 #pragma unroll
-    for (int jj = 0; jj < C::NBUF; ++jj) {
+    for (int jj = 0; jj < NB5; ++jj) {
       const int j = j0 + jj;
       if (j < j_end) {
         const bool load = j + 3 < j_end;
-        tile(j, k_lds[jj], v_lds[jj], k_lds[(jj + 1) % C::NBUF], k_lds[(jj + 3) % C::NBUF],
-             v_lds[(jj + 3) % C::NBUF], load);
+        tile(j, k_lds[jj], v_lds[jj], k_lds[(jj + 1) % NB5], v_lds[(jj + NB5 - 1) % NB5], k_lds[(jj + 3) % NB5],
+             v_lds[(jj + 3) % NB5], load);
         // Tiles j + 1 and j + 2 must be in LDS after this barrier; tile
         // j + 3's loads may stay in flight.
         if (load) lds_barrier<C::LPW>();
@@ -309,14 +341,19 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       }
     }
   }
-  // The wave's last (masked) sub-block.  Its tile is among the last four
-  // of the workgroup (a wave's last sub-block is at most seven sub-blocks
-  // before the workgroup's), so it is still in LDS: no load was issued
-  // after the final one.
+  // The wave's last two sub-blocks: the PV product of u_last - 1 and the
+  // masked weights and PV product of u_last.  Their tiles are among the
+  // last five of the workgroup (a wave's last sub-block is at most seven
+  // sub-blocks before the workgroup's), so they are still in LDS: no load
+  // was issued after the final one.
   if (wave_live) {
-    const uint16_t* vt = v_lds[(u_last / SUB) % C::NBUF];
-    if (u_last % 2 == 0) last_step(sA, 32 * u_last, vt, u_last % SUB);
-    else last_step(sB, 32 * u_last, vt, u_last % SUB);
+    if (u_last >= 1) pv_gemm(v_lds[((u_last - 1) / SUB) % NB5], (u_last - 1) % SUB, pkp);
+    const uint16_t* vt = v_lds[(u_last / SUB) % NB5];
+    const f32x16 cur = (u_last % 2 == 0) ? sA : sB;
+    uint32_t pk[8];
+    const float lsum = exp_pack(cur, 32 * u_last, pk, std::true_type{});
+    settle(cur, 32 * u_last, pk, lsum, std::true_type{});
+    pv_gemm(vt, u_last % SUB, pk);
   }
 
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
