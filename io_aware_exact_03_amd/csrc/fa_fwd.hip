@@ -79,7 +79,8 @@ constexpr float kSumLimit = 256.f;
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, float qk_scale, uint32_t qsign) {
+    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, int BH, float qk_scale,
+    uint32_t qsign) {
   using C = Fwd16<T, D, BN, CAUSAL>;
   constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  int bh, qblk;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
+  // One query block of one (batch, head), start to finish.
+  auto block = [&](int bh, int qblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
@@ -373,6 +374,23 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     }
     if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot)) * kLn2;
   }
+  };
+
+  // Persistent loop: the grid holds one workgroup per CU and each walks
+  // its share of equal-cost work items (see fwd_items / fwd_item_blocks).
+  // Logical item L = r G + xcd_remap(blockIdx), so in every round r each
+  // XCD works on a contiguous range of items, i.e. on shared heads.
+  const int per_head = fwd_items_per_head(n_qblk, CAUSAL);
+  const int n_items = BH * per_head;
+  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
+    const int bh = L / per_head;
+    int qb[2];
+    const int nb = fwd_item_blocks(L % per_head, n_qblk, CAUSAL, &qb[0], &qb[1]);
+    for (int t = 0; t < nb; ++t) {
+      block(bh, qb[t]);
+      __syncthreads();  // the next block's loads reuse the LDS buffers
+    }
+  }
 }
 // ===========================================================================
 // fp32 forward: same structure on v_mfma_f32_32x32x2_f32, P kept in fp32.
@@ -555,11 +573,18 @@ hipError_t launch16(const FwdArgs& a) {
   constexpr int BN = Tile16<D>::BN;
   using C = Fwd16<T, D, BN, CAUSAL>;
   const int n_qblk = (a.N + C::BM - 1) / C::BM;
-  const long long grid = (long long)n_qblk * a.BH;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long items = (long long)fwd_items_per_head(n_qblk, CAUSAL) * a.BH;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // One workgroup per CU (the LDS ring takes the whole 160 KB), never more
+  // workgroups than items.
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = (int)(items < cus ? items : cus);
   hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk,
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk, a.BH,
                      a.qk_scale, a.neg ? 0x80008000u : 0u);
   return hipGetLastError();
 }

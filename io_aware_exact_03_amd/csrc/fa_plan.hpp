@@ -55,6 +55,30 @@ FA_HD void tile_of(int logical, int n_qblk, bool causal, int* bh, int* qblk) {
   *qblk = causal ? (n_qblk - 1 - j) : j;
 }
 
+// Work items of the persistent forward.  The grid holds one workgroup per
+// CU; each walks a list of items.  A causal query block i costs about i + 1
+// key tiles, so item p pairs the heavy block n_qblk - 1 - p with the light
+// block p: every item then costs about n_qblk + 1 tiles and a round-robin
+// deal of items keeps the CUs balanced (an odd middle block is an item of
+// its own).  Non-causal blocks all cost the same: one block per item.
+FA_HD int fwd_items_per_head(int n_qblk, bool causal) { return causal ? (n_qblk + 1) / 2 : n_qblk; }
+
+// Query blocks of item p of a head, heavy first; returns how many (1 or 2).
+FA_HD int fwd_item_blocks(int p, int n_qblk, bool causal, int* first, int* second) {
+  if (!causal) {
+    *first = p;
+    *second = -1;
+    return 1;
+  }
+  *first = n_qblk - 1 - p;
+  *second = p;
+  if (*first == p) {
+    *second = -1;
+    return 1;
+  }
+  return 2;
+}
+
 // Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
 struct FwdTile {
   int bm, bn, waves;
