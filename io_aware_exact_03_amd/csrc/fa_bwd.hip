@@ -206,8 +206,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
-    float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, float qk_scale, float dk_scale,
-    uint32_t ksign) {
+    float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, int BH, float qk_scale,
+    float dk_scale, uint32_t ksign) {
   using C = KV<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][C::BMQ * D];   // swizzled row-major
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[4][C::BMQ * D];
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   w.pw = w.wave % C::NP;  // key group; waves pw and pw + NP share a SIMD
   w.N = N;
   w.qk_scale = qk_scale;
-  int bh, kblk;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), n_kblk, false, &bh, &kblk);  // ascending = heaviest first
+  // One block of BNK keys of one (batch, head), start to finish.
+  auto block = [&](int bh, int kblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   w.qrs = make_rsrc(qg + head, head_bytes);
@@ -301,6 +301,22 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
       const int kr = w.kw0 + 8 * (r / 4) + 4 * w.g + (r % 4);
       if (kr < N) out[(size_t)kr * D + 32 * db + w.n] = acc[db][r] * sc;
     }
+  };
+
+  // Persistent loop over equal-cost items (items_per_head / item_blocks);
+  // in each round every XCD works on a contiguous range of items.  The
+  // heavier key block of a causal pair (the lower one) goes first.
+  const int per_head = items_per_head(n_kblk, CAUSAL);
+  const int n_items = BH * per_head;
+  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
+    const int bh = L / per_head;
+    int lo, hi;
+    const int nb = item_blocks(L % per_head, n_kblk, CAUSAL, &lo, &hi);
+    for (int t = 0; t < nb; ++t) {
+      block(bh, t == 0 ? lo : hi);
+      __syncthreads();  // the next block reuses the LDS buffers
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -321,14 +337,14 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
-    float* __restrict__ dqg, int N, int n_qblk, float qk_scale, float dq_scale, uint32_t qsign) {
+    float* __restrict__ dqg, int N, int n_qblk, int BH, float qk_scale, float dq_scale, uint32_t qsign) {
   using C = QG<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * D];  // swizzled row-major
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
-  int bh, qblk;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), n_qblk, CAUSAL, &bh, &qblk);
+  // One block of BM queries of one (batch, head), start to finish.
+  auto qblock = [&](int bh, int qblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   const rsrc_t krs = make_rsrc(kg + head, head_bytes), vrs = make_rsrc(vg + head, head_bytes);
@@ -451,6 +467,21 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
                         v[4 * rq + 3] * dq_scale);
       }
   }
+  };
+
+  // Persistent loop over equal-cost items, as in the dK/dV pass; the
+  // heavier query block of a causal pair (the higher one) goes first.
+  const int per_head = items_per_head(n_qblk, CAUSAL);
+  const int n_items = BH * per_head;
+  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
+    const int bh = L / per_head;
+    int lo, hi;
+    const int nb = item_blocks(L % per_head, n_qblk, CAUSAL, &lo, &hi);
+    for (int t = 0; t < nb; ++t) {
+      qblock(bh, t + 1 < nb ? hi : lo);
+      __syncthreads();  // the next block reuses the LDS buffers
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -461,8 +492,17 @@ hipError_t run(const BwdArgs& a, int stage) {
   const long long g1 = (rows + RPB - 1) / RPB;
   const int n_kblk = (a.N + KV<D>::BNK - 1) / KV<D>::BNK;
   const int n_qblk = (a.N + QG<D>::BM - 1) / QG<D>::BM;
-  const long long g2 = (long long)n_kblk * a.BH, g3 = (long long)n_qblk * a.BH;
+  long long g2 = (long long)items_per_head(n_kblk, CAUSAL) * a.BH;
+  long long g3 = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // dK/dV and dQ run persistent grids of one workgroup per CU (registers
+  // allow one 512-thread workgroup per CU), never more than their items.
+  int dev = 0, cus = 0;
+  hipError_t de = hipGetDevice(&dev);
+  if (de == hipSuccess) de = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (de != hipSuccess) return de;
+  if (g2 > cus) g2 = cus;
+  if (g3 > cus) g3 = cus;
   const float qk_scale = fabsf(a.scale) * kLog2eHost;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const auto* q = static_cast<const uint16_t*>(a.q);
@@ -477,13 +517,13 @@ hipError_t run(const BwdArgs& a, int stage) {
   }
   if (stage == 0 || stage == 2) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, qk_scale, a.scale, qsign);
+                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, a.BH, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 3) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(QG<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dq, a.N, n_qblk, qk_scale, a.scale, qsign);
+                       a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

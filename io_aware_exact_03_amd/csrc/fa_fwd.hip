@@ -377,17 +377,18 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   };
 
   // Persistent loop: the grid holds one workgroup per CU and each walks
-  // its share of equal-cost work items (see fwd_items / fwd_item_blocks).
+  // its share of equal-cost work items (items_per_head / item_blocks).
   // Logical item L = r G + xcd_remap(blockIdx), so in every round r each
-  // XCD works on a contiguous range of items, i.e. on shared heads.
-  const int per_head = fwd_items_per_head(n_qblk, CAUSAL);
+  // XCD works on a contiguous range of items, i.e. on shared heads.  The
+  // heavier query block of a causal pair goes first.
+  const int per_head = items_per_head(n_qblk, CAUSAL);
   const int n_items = BH * per_head;
   for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
     const int bh = L / per_head;
-    int qb[2];
-    const int nb = fwd_item_blocks(L % per_head, n_qblk, CAUSAL, &qb[0], &qb[1]);
-    for (int t = 0; t < nb; ++t) {
-      block(bh, qb[t]);
+    int lo, hi;
+    const int nb = item_blocks(L % per_head, n_qblk, CAUSAL, &lo, &hi);
+    for (int t = 0; t < nb; ++t) {  // one call site: the block body is large
+      block(bh, t + 1 < nb ? hi : lo);
       __syncthreads();  // the next block's loads reuse the LDS buffers
     }
   }
@@ -573,7 +574,7 @@ hipError_t launch16(const FwdArgs& a) {
   constexpr int BN = Tile16<D>::BN;
   using C = Fwd16<T, D, BN, CAUSAL>;
   const int n_qblk = (a.N + C::BM - 1) / C::BM;
-  const long long items = (long long)fwd_items_per_head(n_qblk, CAUSAL) * a.BH;
+  const long long items = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // One workgroup per CU (the LDS ring takes the whole 160 KB), never more
   // workgroups than items.

@@ -55,28 +55,23 @@ FA_HD void tile_of(int logical, int n_qblk, bool causal, int* bh, int* qblk) {
   *qblk = causal ? (n_qblk - 1 - j) : j;
 }
 
-// Work items of the persistent forward.  The grid holds one workgroup per
-// CU; each walks a list of items.  A causal query block i costs about i + 1
-// key tiles, so item p pairs the heavy block n_qblk - 1 - p with the light
-// block p: every item then costs about n_qblk + 1 tiles and a round-robin
-// deal of items keeps the CUs balanced (an odd middle block is an item of
-// its own).  Non-causal blocks all cost the same: one block per item.
-FA_HD int fwd_items_per_head(int n_qblk, bool causal) { return causal ? (n_qblk + 1) / 2 : n_qblk; }
+// Work items of the persistent kernels.  Their grids hold one workgroup
+// per CU and each workgroup walks a list of items.  Under the causal mask
+// the blocks of a head cost a linear ramp: query block i of the forward and
+// of dQ costs about i + 1 key tiles, key block j of dK/dV about n - j query
+// tiles.  Item p therefore pairs block p with block n_blk - 1 - p, so every
+// item costs about the same and a round-robin deal of items keeps the CUs
+// balanced (an odd middle block is an item of its own).  Without the mask
+// all blocks cost the same: one block per item.
+FA_HD int items_per_head(int n_blk, bool causal) { return causal ? (n_blk + 1) / 2 : n_blk; }
 
-// Query blocks of item p of a head, heavy first; returns how many (1 or 2).
-FA_HD int fwd_item_blocks(int p, int n_qblk, bool causal, int* first, int* second) {
-  if (!causal) {
-    *first = p;
-    *second = -1;
-    return 1;
-  }
-  *first = n_qblk - 1 - p;
-  *second = p;
-  if (*first == p) {
-    *second = -1;
-    return 1;
-  }
-  return 2;
+// Blocks of item p of a head: *lo = p and, for a causal pair, *hi =
+// n_blk - 1 - p (else -1).  Returns how many (1 or 2).
+FA_HD int item_blocks(int p, int n_blk, bool causal, int* lo, int* hi) {
+  *lo = p;
+  *hi = causal ? n_blk - 1 - p : -1;
+  if (*hi == p) *hi = -1;
+  return *hi < 0 ? 1 : 2;
 }
 
 // Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
