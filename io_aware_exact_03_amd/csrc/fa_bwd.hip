@@ -71,29 +71,33 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.  A workgroup owns NP groups of 32 keys and loops over 32-query
+// 2. dK, dV.  A workgroup owns NP groups of 32 keys and loops over 64-query
 // blocks.  Each key group is served by a pair of waves on one SIMD with
 // split roles, two of the four products each:
 //   wave A (waves 0..NP-1):  S = Q K^T, P = exp2(S*c - LSE2), dV += P^T dO
 //   wave B (waves NP..2NP-1): dP = dO V^T, dS = P * (dP - Delta), dK += dS^T Q
 // B runs one query block behind A: in iteration i, A works on block i while
-// B works on block i-1, whose P (fp32, lane-private LDS slots) A wrote in
-// iteration i-1.  So the two waves of a SIMD never wait for each other
-// inside an iteration, and A's exponentials overlap B's products.
-// Q, dO, LSE and Delta go from global memory straight into LDS (no
-// registers), two blocks ahead, through four slots: A's block, B's block and
-// the two blocks in flight.  P cycles through two buffers.  One barrier per
-// iteration, which waits only for the older block in flight.  A negative
-// scale is applied by negating K, so Q lands in LDS unchanged.
+// B works on block i-1, whose P A wrote to LDS (fp16) in iteration i-1.  So
+// the two waves of a SIMD never wait for each other inside an iteration.
+// Each wave takes its block as two 32-query halves in four phases, so the
+// vector work of one half runs under the matrix products of the other:
+//   A: S0 | S1 + weights P0 | dV(P0) + weights P1 | dV(P1)
+//   B: dP0 | dP1 + dS0 | dK(dS0) + dS1 | dK(dS1)
+// Q, dO and Delta go from global memory straight into LDS (no registers)
+// one block ahead through three slots (A's block, B's block, the block in
+// flight); wave 0 stages -LSE log2(e) of the block in flight.  One barrier
+// per iteration.  A negative scale is applied by negating K, so Q lands in
+// LDS unchanged.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KV {
-  static constexpr int NP = 4, NW = 2 * NP, NT = 64 * NW, KW = 32, BNK = NP * KW, BMQ = 32;
+  static constexpr int NP = 4, NW = 2 * NP, NT = 64 * NW, KW = 32, BNK = NP * KW, BMQ = 64, NSLOT = 3;
   static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   static constexpr int RPL = 64 / CPR;            // tile rows per 1 KB wave load
   static constexpr int PPA = BMQ / RPL;           // 1 KB pieces per Q (or dO) block
   static constexpr int LPB = 2 * PPA / NW;        // pieces per wave per block
   static_assert(LPB >= 1 && 2 * PPA == LPB * NW, "staging split");
+  static_assert(2 * DB == DS, "one product per slot in every phase");
 };
 
 // Uniform state of one dK/dV wave.
@@ -104,16 +108,18 @@ struct KVWave {
   rsrc_t qrs, dors, lrs, drs;
 };
 
-// Issue the loads of query block i into LDS: piece t = wave LPB + e covers
-// tile rows (t % PPA) RPL .. + RPL of Q (t < PPA) or of dO; lane l fills LDS
-// bytes 16 l of the piece, i.e. tile row l / CPR and stored chunk l % CPR,
-// which holds the row's logical chunk (l % CPR) ^ swz_chunk(row).  Waves 0
-// and 1 also load LSE and Delta.  Returns nothing; the caller counts loads.
+// Issue the loads of query block i: piece t = wave LPB + e covers tile rows
+// (t % PPA) RPL .. + RPL of Q (t < PPA) or of dO, straight into LDS; lane l
+// fills LDS bytes 16 l of the piece, i.e. tile row l / CPR and stored chunk
+// l % CPR, which holds the row's logical chunk (l % CPR) ^ swz_chunk(row).
+// Wave 1 loads Delta into LDS the same way; wave 0 loads LSE into a register
+// (returned) and stores -LSE log2(e) with kv_stage_lse once it has arrived.
 template <int D>
-__device__ __forceinline__ void kv_issue(const KVWave& w, int i, uint16_t* __restrict__ q_dst,
-                                         uint16_t* __restrict__ do_dst, float* __restrict__ l_dst,
-                                         float* __restrict__ d_dst) {
+__device__ __forceinline__ float kv_issue(const KVWave& w, int i, uint16_t* __restrict__ q_dst,
+                                          uint16_t* __restrict__ do_dst, float* __restrict__ d_dst) {
   using C = KV<D>;
+  float lse = 0.f;
+  if (w.wave == 0) lse = load4f(w.lrs, (uint32_t)(i * C::BMQ + w.lane) * 4);
   const int lrow = w.lane / C::CPR;
 #pragma unroll
   for (int e = 0; e < C::LPB; ++e) {
@@ -126,79 +132,158 @@ __device__ __forceinline__ void kv_issue(const KVWave& w, int i, uint16_t* __res
     if (is_q) load_lds16(w.qrs, q_dst + piece, off);
     else load_lds16(w.dors, do_dst + piece, off);
   }
-  if (w.wave == 0) load_lds4(w.lrs, l_dst, (uint32_t)(i * C::BMQ + w.lane) * 4);
   if (w.wave == 1) load_lds4(w.drs, d_dst, (uint32_t)(i * C::BMQ + w.lane) * 4);
+  return lse;
 }
 
-// One iteration of a wave's work.  Every LDS tile it touches arrives as a
-// distinct __restrict__ pointer, which tells the compiler that the loads it
-// issues into the next slots do not alias what it reads this iteration, so
-// it does not wait for those loads before each read.
-template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void kv_iter(
-    const KVWave& w, int i, bool work, bool ahead, const uint4 (&kv)[KV<D>::DS], f32x16 (&acc)[KV<D>::DB],
-    const uint16_t* __restrict__ lhs, const uint16_t* __restrict__ rhs, const float* __restrict__ rowv,
-    float4* __restrict__ x_out, const float4* __restrict__ x_in, uint16_t* __restrict__ nq,
-    uint16_t* __restrict__ ndo, float* __restrict__ nl, float* __restrict__ nd) {
+// One iteration of a wave's work on its block: four phases over the two
+// halves (see above), each of NS slots with one matrix product and a share
+// of the other half's vector work; LDS reads run two slots ahead.  Register
+// r of a 32x32 accumulator is query 32 h + 8 (r/4) + 4 g + r%4 of the block
+// (half h), the lane's key is kw0 + n.  A query past N has Q = 0, LSE = 0
+// and dO = Delta = 0, so whatever weight it gets adds nothing.  Every LDS
+// tile arrives as a distinct __restrict__ pointer, which tells the compiler
+// that the loads issued into the next slot do not alias what is read here,
+// so it does not wait for those loads before each read.
+template <typename T, int D, bool ROLE_A, bool MASK>
+__device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv)[KV<D>::DS],
+                                        f32x16 (&acc)[KV<D>::DB], const uint16_t* __restrict__ lhs,
+                                        const uint16_t* __restrict__ rhs, const float* __restrict__ rowv,
+                                        uint4* __restrict__ x_out, const uint4* __restrict__ x_in) {
   using C = KV<D>;
-  if (ahead) kv_issue<D>(w, i + 2, nq, ndo, nl, nd);
-  if (!work) return;
+  constexpr int NS = C::DS;        // products per phase
+  constexpr int EP = 16 / NS;      // accumulator elements of vector work per slot (2 or 4)
   const int n = w.n, g = w.g, lane = w.lane;
-  // Register r of the 32x32 accumulator is query 8 (r/4) + 4 g + r%4 of the
-  // block; the lane's key is kw0 + n.  A chain's LDS operands are all
-  // requested before its first product, and the second chain's transposed
-  // operands before the vector work; the fences keep them there.
-  uint4 ra[C::DS];
+  const int q_first = i * C::BMQ;
+  const int key = w.kw0 + n;
+
+  // Row operand (A: Q, B: dO) fragment k of half h; transposed operand (A:
+  // dO, B: Q) fragment k of half h (16-query chunk k / DB, d block k % DB).
+  // In the swizzled layout every fragment sits at a per-lane base XOR a
+  // constant plus a row offset, because the chunk permutation only touches
+  // the low (within-row) address bits: row reads at (R ^ 16 k) + 32 h D,
+  // transposing reads at (T ^ 32 (k % DB) [^ 16 for the second 8 rows]) +
+  // (32 h + 16 (k / DB) [+ 8]) D, in elements.  The two bases pass through an
+  // empty asm so the compiler computes each address next to its read instead
+  // of keeping dozens of precomputed addresses live across the loop.
+  uint32_t R = (uint32_t)swz<D>(n, 8 * g);
+  uint32_t Tb = (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  asm volatile("" : "+v"(R), "+v"(Tb));
+  auto rowf = [&](int h, int k) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(lhs + ((R ^ (16 * k)) + 32 * h * D));
+  };
+  auto trf = [&](int h, int k) __attribute__((always_inline)) {
+    const uint32_t r0 = (32 * h + 16 * (k / C::DB)) * D;
+    const uint32_t t = Tb ^ (32 * (k % C::DB));
+    const uint2 x = read_tr_b64(rhs + (t + r0));
+    const uint2 y = read_tr_b64(rhs + ((t ^ 16) + r0 + 8 * D));
+    return make_uint4(x.x, x.y, y.x, y.y);
+  };
+  // Per-row values (A: -LSE log2 e, B: Delta) of the elements a slot's
+  // vector work touches: elements EP k .. of half h, i.e. rows 32 h +
+  // 8 (r/4) + 4 g + r%4, read EP at a time.
+  typedef float fEP __attribute__((ext_vector_type(EP)));
+  auto rowv_slot = [&](int h, int k) __attribute__((always_inline)) {
+    const int r = EP * k;
+    return *reinterpret_cast<const fEP*>(&rowv[32 * h + 8 * (r / 4) + 4 * g + (r % 4)]);
+  };
+  // fp16 P of half h: 8 words per lane, stored / read in two 16-byte pieces.
+  auto put_p = [&](int h, int piece, const uint32_t (&ph)[8]) __attribute__((always_inline)) {
+    x_out[(2 * h + piece) * 64 + lane] = make_uint4(ph[4 * piece], ph[4 * piece + 1], ph[4 * piece + 2],
+                                                    ph[4 * piece + 3]);
+  };
+  auto get_p = [&](int h, uint32_t (&ph)[8]) __attribute__((always_inline)) {
+    const uint4 x0 = x_in[(2 * h) * 64 + lane], x1 = x_in[(2 * h + 1) * 64 + lane];
+    ph[0] = x0.x; ph[1] = x0.y; ph[2] = x0.z; ph[3] = x0.w;
+    ph[4] = x1.x; ph[5] = x1.y; ph[6] = x1.z; ph[7] = x1.w;
+  };
+  // Vector work of slot k on half h (elements r0 = EP k .. r0 + EP - 1).
+  //  A: p = exp2(s qk - LSE log2 e) (masked on the diagonal), packed to
+  //     16-bit for dV += P^T dO and to fp16 for wave B (stored as soon as a
+  //     16-byte piece is complete).
+  //  B: dS = P (dP - Delta) with P from the fp16 copy, packed to 16-bit for
+  //     dK += dS^T Q.
+  auto vec = [&](int h, int k, const f32x16& sd, const fEP& v, uint32_t (&pk)[8], uint32_t (&ph)[8])
+      __attribute__((always_inline)) {
+    const int r0 = EP * k;
 #pragma unroll
-  for (int st = 0; st < C::DS; ++st) ra[st] = read_row<D>(lhs, n, 16 * st + 8 * g);
-  float4 v4[4], p4[4];
-#pragma unroll
-  for (int rq = 0; rq < 4; ++rq) {
-    v4[rq] = *reinterpret_cast<const float4*>(&rowv[8 * rq + 4 * g]);  // A: LSE, B: Delta
-    if (!w.role_a) p4[rq] = x_in[64 * rq + lane];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 sd = f32x16{};  // A: S, B: dP
-#pragma unroll
-  for (int st = 0; st < C::DS; ++st) sd = mma16(T{}, ra[st], kv[st], sd);
-  uint4 rb[2 * C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    rb[2 * db] = read_tr<D>(rhs, 0, 32 * db, lane);
-    rb[2 * db + 1] = read_tr<D>(rhs, 16, 32 * db, lane);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if (w.role_a) {
-    const int q_first = i * C::BMQ;
-    const bool need_mask = CAUSAL && q_first < w.kw0 + C::KW - 1;
-    const int key = w.kw0 + n;
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const float lv[4] = {v4[rq].x, v4[rq].y, v4[rq].z, v4[rq].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // P = exp2(s |scale| log2 e - LSE log2 e).  A query past the end has
-        // Q, dO and Delta all zero (LSE reads as 0), so its P adds nothing.
-        float p = fast_exp2(__builtin_fmaf(sd[4 * rq + e], w.qk_scale, -lv[e] * kLog2e));
-        if (need_mask) p = (key <= q_first + 8 * rq + 4 * g + e) ? p : 0.f;
-        sd[4 * rq + e] = p;
+    for (int e = 0; e < EP; e += 2) {
+      const int r = r0 + e;
+      if constexpr (ROLE_A) {
+        float p0 = fast_exp2(__builtin_fmaf(sd[r], w.qk_scale, v[e]));
+        float p1 = fast_exp2(__builtin_fmaf(sd[r + 1], w.qk_scale, v[e + 1]));
+        if constexpr (MASK) {
+          const int q = q_first + 32 * h + 8 * (r / 4) + 4 * g + (r % 4);
+          p0 = key <= q ? p0 : 0.f;
+          p1 = key <= q + 1 ? p1 : 0.f;
+        }
+        pk[r / 2] = pack2(T{}, p0, p1);
+        ph[r / 2] = pack2(F16{}, p0, p1);
+      } else {
+        // fp16 P times an fp32 factor, one mixed-precision multiply-add each
+        const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(ph[r / 2] & 0xffffu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(ph[r / 2] >> 16));
+        pk[r / 2] = pack2(T{}, __builtin_fmaf((float)h0, sd[r] - v[e], 0.f),
+                          __builtin_fmaf((float)h1, sd[r + 1] - v[e + 1], 0.f));
       }
-      x_out[64 * rq + lane] = make_float4(sd[4 * rq], sd[4 * rq + 1], sd[4 * rq + 2], sd[4 * rq + 3]);
     }
-  } else {
+    if constexpr (ROLE_A) {
+      if ((r0 + EP) % 8 == 0) put_p(h, (r0 + EP) / 8 - 1, ph);
+    }
+  };
+
+  f32x16 s0, s1;
+  uint4 a[3], b[3];
+  fEP vv[2];
+  uint32_t pk0[8], pk1[8], ph0[8], ph1[8];
+
+  // ---- phase 1: the first half's product chain ----------------------------
+  a[0] = rowf(0, 0);
+  a[1] = rowf(0, 1);
+  if constexpr (!ROLE_A) get_p(0, ph0);
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const float dv4[4] = {v4[rq].x, v4[rq].y, v4[rq].z, v4[rq].w};
-      const float pv[4] = {p4[rq].x, p4[rq].y, p4[rq].z, p4[rq].w};
+  for (int k = 0; k < NS; ++k) {
+    a[(k + 2) % 3] = k + 2 < NS ? rowf(0, k + 2) : rowf(1, k + 2 - NS);
+    if (k == NS - 1) vv[0] = rowv_slot(0, 0);
+    s0 = mma16(T{}, a[k % 3], kv[k], k == 0 ? f32x16{} : s0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- phase 2: the second half's chain, the first half's vector work ----
+  // (The three fragment registers rotate continuously across phases: the
+  // first two fragments of a phase were read into slots NS % 3, (NS+1) % 3.)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sd[4 * rq + e] = pv[e] * (sd[4 * rq + e] - dv4[e]);
+  for (int k = 0; k < NS; ++k) {
+    if (k + 2 < NS) a[(NS + k + 2) % 3] = rowf(1, k + 2);
+    else b[k + 2 - NS] = trf(0, k + 2 - NS);
+    vv[(k + 1) % 2] = k + 1 < NS ? rowv_slot(0, k + 1) : rowv_slot(1, 0);
+    if constexpr (!ROLE_A) {
+      if (k == NS - 2) get_p(1, ph1);
+    }
+    s1 = mma16(T{}, a[(NS + k) % 3], kv[k], k == 0 ? f32x16{} : s1);
+    vec(0, k, s0, vv[k % 2], pk0, ph0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- phase 3: the first half's second product, the second half's vector work
+  {
+    const uint4 pp[2] = {make_uint4(pk0[0], pk0[1], pk0[2], pk0[3]), make_uint4(pk0[4], pk0[5], pk0[6], pk0[7])};
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      b[(k + 2) % 3] = k + 2 < NS ? trf(0, k + 2) : trf(1, k + 2 - NS);
+      if (k + 1 < NS) vv[(k + 1) % 2] = rowv_slot(1, k + 1);
+      acc[k % C::DB] = mma16(T{}, pp[k / C::DB], b[k % 3], acc[k % C::DB]);
+      vec(1, k, s1, vv[k % 2], pk1, ph1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const uint4 pk0 = pack8(T{}, sd, 0), pk1 = pack8(T{}, sd, 1);
+  // ---- phase 4: the second half's second product --------------------------
+  {
+    const uint4 pp[2] = {make_uint4(pk1[0], pk1[1], pk1[2], pk1[3]), make_uint4(pk1[4], pk1[5], pk1[6], pk1[7])};
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    acc[db] = mma16(T{}, pk0, rb[2 * db], acc[db]);
-    acc[db] = mma16(T{}, pk1, rb[2 * db + 1], acc[db]);
+    for (int k = 0; k < NS; ++k) {
+      if (k + 2 < NS) b[(NS + k + 2) % 3] = trf(1, k + 2);
+      acc[k % C::DB] = mma16(T{}, pp[k / C::DB], b[(NS + k) % 3], acc[k % C::DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -209,11 +294,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, int BH, float qk_scale,
     float dk_scale, uint32_t ksign) {
   using C = KV<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[4][C::BMQ * D];   // swizzled row-major
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[4][C::BMQ * D];
-  __shared__ __attribute__((aligned(16))) float4 x_lds[2][C::NP][4 * 64];  // P, A -> B
-  __shared__ __attribute__((aligned(16))) float lse_lds[4][64];            // raw LSE (first BMQ used)
-  __shared__ __attribute__((aligned(16))) float dl_lds[4][64];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[C::NSLOT][C::BMQ * D];   // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::NSLOT][C::BMQ * D];
+  __shared__ __attribute__((aligned(16))) uint4 x_lds[2][C::NP][4 * 64];          // fp16 P, A -> B
+  __shared__ __attribute__((aligned(16))) float lse_lds[C::NSLOT][C::BMQ];        // -LSE log2(e)
+  __shared__ __attribute__((aligned(16))) float dl_lds[C::NSLOT][C::BMQ];         // Delta
 
   KVWave w;
   w.lane = threadIdx.x & 63;
@@ -224,6 +309,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   w.pw = w.wave % C::NP;  // key group; waves pw and pw + NP share a SIMD
   w.N = N;
   w.qk_scale = qk_scale;
+
   // One block of BNK keys of one (batch, head), start to finish.
   auto block = [&](int bh, int kblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -256,39 +342,56 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   auto block_active = [&](int i) {
     return pair_live && (!CAUSAL || min((i + 1) * C::BMQ, N) - 1 >= w.kw0);
   };
-  // Loads this wave issues per block (the barrier count below depends on it).
-  const bool extra = w.wave < 2;
+  // A block needs the causal mask when its first query is left of the
+  // pair's last key (only the diagonal block of the pair).
+  auto block_masked = [&](int i) { return CAUSAL && i * C::BMQ < w.kw0 + C::KW - 1; };
 
   wait_vmem();  // K or V fragments above
-  kv_issue<D>(w, i_lo, q_lds[i_lo & 3], do_lds[i_lo & 3], lse_lds[i_lo & 3], dl_lds[i_lo & 3]);
-  if (i_lo + 1 < n_qblk) {
-    const int s1 = (i_lo + 1) & 3;
-    kv_issue<D>(w, i_lo + 1, q_lds[s1], do_lds[s1], lse_lds[s1], dl_lds[s1]);
-    if (extra) lds_barrier<C::LPB + 1>();
-    else lds_barrier<C::LPB>();
-  } else {
-    lds_barrier<0>();
-  }
+  float lse_in = kv_issue<D>(w, i_lo, q_lds[i_lo % C::NSLOT], do_lds[i_lo % C::NSLOT], dl_lds[i_lo % C::NSLOT]);
+  if (w.wave == 0) lse_lds[i_lo % C::NSLOT][w.lane] = -lse_in * kLog2e;
+  lds_barrier<0>();
 
-  // Iteration i: A works on block i (slot i & 3), B on block i - 1 (slot
-  // (i - 1) & 3); block i + 2 is loaded into slot (i + 2) & 3, whose last
-  // reader (B, block i - 2) finished before the previous barrier.
-  for (int i = i_lo; i <= n_qblk; ++i) {
-    const bool ahead = i + 2 < n_qblk;
-    const int sa = i & 3, sb = (i - 1) & 3, sn = (i + 2) & 3;
-    const bool work = w.role_a ? (i < n_qblk && block_active(i)) : (i > i_lo && block_active(i - 1));
-    const int s_own = w.role_a ? sa : sb;
-    kv_iter<T, D, CAUSAL>(w, i, work, ahead, kv, acc,
-                          w.role_a ? q_lds[s_own] : do_lds[s_own],   // row-read operand
-                          w.role_a ? do_lds[s_own] : q_lds[s_own],   // transposed-read operand
-                          w.role_a ? lse_lds[s_own] : dl_lds[s_own],
-                          x_lds[i & 1][w.pw], x_lds[(i - 1) & 1][w.pw],
-                          q_lds[sn], do_lds[sn], lse_lds[sn], dl_lds[sn]);
-    // Block i + 1 (loaded one iteration ago) must be in LDS after this barrier;
-    // block i + 2's loads may stay in flight.
-    if (!ahead) lds_barrier<0>();
-    else if (extra) lds_barrier<C::LPB + 1>();
-    else lds_barrier<C::LPB>();
+  // Iteration i: A works on block i (slot i % 3), B on block i - 1 (slot
+  // (i - 1) % 3); block i + 1 is loaded into slot (i + 1) % 3, whose last
+  // reader (B, block i - 2) finished before the previous barrier.  MAY_MASK
+  // marks the call sites that can meet A's masked block.
+  auto iter = [&](int i, uint16_t* __restrict__ qa, uint16_t* __restrict__ da, float* __restrict__ la,
+                  float* __restrict__ dla, uint16_t* __restrict__ qb, uint16_t* __restrict__ db_,
+                  float* __restrict__ dlb, uint16_t* __restrict__ qn, uint16_t* __restrict__ dn,
+                  float* __restrict__ ln, float* __restrict__ dln, auto may_mask) __attribute__((always_inline)) {
+    constexpr bool MAY_MASK = decltype(may_mask)::value;
+    const bool ahead = i + 1 < n_qblk;
+    if (ahead) lse_in = kv_issue<D>(w, i + 1, qn, dn, dln);
+    if (w.role_a) {
+      if (i < n_qblk && block_active(i)) {
+        if (MAY_MASK && block_masked(i))
+          kv_iter<T, D, true, true>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+        else
+          kv_iter<T, D, true, false>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+      }
+    } else if (i > i_lo && block_active(i - 1)) {
+      kv_iter<T, D, false, false>(w, i - 1, kv, acc, db_, qb, dlb, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+    }
+    // Block i + 1 must be in LDS after this barrier (wave 0 first stores its
+    // -LSE log2 e, whose load has arrived by now).
+    if (ahead && w.wave == 0) ln[w.lane] = -lse_in * kLog2e;
+    lds_barrier<0>();
+  };
+  // A pair's keys start at kw0 = 128 kblk + 32 pw, so its only masked block
+  // (the one holding query kw0) is block 2 kblk + pw / 2: i_lo or i_lo + 1.
+  // Only those two iterations carry the masked variant of A's work.
+  static_assert(C::BNK == 2 * C::BMQ && C::KW == 32 && C::NP == 4, "masked block at i_lo or i_lo + 1");
+  constexpr int NS3 = C::NSLOT;
+  int i = i_lo;
+  for (; i <= n_qblk && i < i_lo + 2; ++i) {
+    const int sa = i % NS3, sb = (i + NS3 - 1) % NS3, sn = (i + 1) % NS3;
+    iter(i, q_lds[sa], do_lds[sa], lse_lds[sa], dl_lds[sa], q_lds[sb], do_lds[sb], dl_lds[sb], q_lds[sn],
+         do_lds[sn], lse_lds[sn], dl_lds[sn], std::true_type{});
+  }
+  for (; i <= n_qblk; ++i) {
+    const int sa = i % NS3, sb = (i + NS3 - 1) % NS3, sn = (i + 1) % NS3;
+    iter(i, q_lds[sa], do_lds[sa], lse_lds[sa], dl_lds[sa], q_lds[sb], do_lds[sb], dl_lds[sb], q_lds[sn],
+         do_lds[sn], lse_lds[sn], dl_lds[sn], std::false_type{});
   }
 
   // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
