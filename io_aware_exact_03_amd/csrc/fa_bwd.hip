@@ -423,17 +423,26 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.  Workgroup = 8 waves x 32 queries (two waves per SIMD); inner loop
-// over 64-key blocks, each taken as two 32-key sub-blocks.  K and V sit
-// row-major (swizzled) in LDS: rows feed S^T = K Q^T and dP^T = V dO^T,
-// transposing reads give K^T for dQ^T += K^T dS^T.
+// 3. dQ.  Workgroup = 8 waves x 32 queries (two waves per SIMD), the same
+// organisation as the forward: K and V tiles of BN keys go from global
+// memory straight into LDS (swizzled row-major) through four buffers, three
+// tiles ahead; rows feed S^T = K Q^T and dP^T = V dO^T, transposing reads
+// give K^T for dQ^T += K^T dS^T.  Each lane owns one query, so its LSE and
+// Delta are two registers.  Per 32-key sub-block u a wave issues the score
+// and dP products of sub-block u+1 in slots, each followed by its share of
+// u's vector work (P and dS), then the dQ product of u.  Only a wave's last
+// sub-block (the diagonal, or the sequence tail) is masked.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QG {
-  static constexpr int NW = 8, NT = 64 * NW, BM = NW * 32, BN = 64;
-  static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32, CPR = D / 8;
-  static constexpr int LDC = BN * CPR / NT;  // 16-byte chunks of K (and of V) per thread per block
-  static_assert(LDC >= 1 && BN * CPR % NT == 0, "staging split");
+  static constexpr int NW = 8, NT = 64 * NW, BM = NW * 32;
+  static constexpr int BN = D == 128 ? 64 : 128;  // 16 KB of K and of V per tile
+  static constexpr int DS = D / 16, DB = D / 32, SUB = BN / 32, CPR = D / 8;
+  static constexpr int RPP = 64 / CPR;            // tile rows per 1 KB wave load
+  static constexpr int PPT = BN / RPP;            // 1 KB pieces per K (or V) tile
+  static constexpr int LPW = 2 * PPT / NW;        // loads per wave per tile
+  static constexpr int NBUF = 4;
+  static_assert(SUB % 2 == 0 && LPW >= 1 && LPW * NW == 2 * PPT && 2 * DB == DS, "tile shape");
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -442,10 +451,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
     float* __restrict__ dqg, int N, int n_qblk, int BH, float qk_scale, float dq_scale, uint32_t qsign) {
   using C = QG<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * D];  // swizzled row-major
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::BN * D];
+  constexpr int BN = C::BN, DS = C::DS, DB = C::DB, SUB = C::SUB, NS = C::DS;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::NBUF][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+
   // One block of BM queries of one (batch, head), start to finish.
   auto qblock = [&](int bh, int qblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -456,11 +469,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   const int query = qw0 + n;
 
   // Q and dO of this lane's query as the B operands (zero past the end).
-  uint4 qf[C::DS], dof[C::DS];
+  uint4 qf[DS], dof[DS];
   {
     const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
+    for (int s = 0; s < DS; ++s) {
       const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * g) * 2;
       uint4 a = load16(qrs, off);
       a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
@@ -471,97 +484,177 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   const float lse2 = query < N ? lseg[(size_t)bh * N + query] * kLog2e : kPosInf;
   const float dl = query < N ? deltag[(size_t)bh * N + query] : 0.f;
 
-  f32x16 dq[C::DB];  // dQ^T: rows = d, columns = queries
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) dq[db] = f32x16{};
-
-  const int n_kv = (N + C::BN - 1) / C::BN;
-  int j_end = n_kv;
-  if (CAUSAL) j_end = min(n_kv, (min(q0 + C::BM, N) - 1) / C::BN + 1);
-  int w_s1 = n_kv, w_s2 = n_kv;
+  // Key plan, as in the forward: the wave's queries see sub-blocks
+  // [0, u_last]; only u_last is masked.
+  const int n_sub = (N + 31) / 32;
   const bool wave_live = qw0 < N;
-  if (CAUSAL && wave_live) causal_stages(qw0, min(qw0 + 32, N), C::BN, &w_s1, &w_s2);
-  const int full_blocks = N / C::BN;
+  const int u_last = !wave_live ? -1 : (CAUSAL ? qw0 / 32 : n_sub - 1);
+  const int last_live = min(C::NW - 1, (N - 1 - q0) / 32);
+  const int u_end = CAUSAL ? (q0 / 32 + last_live) : (n_sub - 1);
+  const int j_end = u_end / SUB + 1;
   const int key_lim = CAUSAL ? min(query + 1, N) : N;
 
-  uint4 ks[C::LDC], vs[C::LDC];
-  auto load_block = [&](int j) {
+  // Tile loads (as in the forward): piece t = wave LPW + e holds RPP rows of
+  // K (t < PPT) or V; lane l fills LDS bytes 16 l of the piece.
+  auto issue = [&](int j, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
+    const int lrow = lane / C::CPR;
 #pragma unroll
-    for (int e = 0; e < C::LDC; ++e) {
-      const int c = tid + e * C::NT;
-      const uint32_t off = ((uint32_t)(j * C::BN + c / C::CPR) * D + 8 * (c % C::CPR)) * 2;
-      ks[e] = load16(krs, off);
-      vs[e] = load16(vrs, off);
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < C::LDC; ++e) {
-      const int c = tid + e * C::NT;
-      const int off = swz<D>(c / C::CPR, 8 * (c % C::CPR));
-      *reinterpret_cast<uint4*>(&k_lds[buf][off]) = ks[e];
-      *reinterpret_cast<uint4*>(&v_lds[buf][off]) = vs[e];
+    for (int e = 0; e < C::LPW; ++e) {
+      const int t = wave * C::LPW + e;
+      const int p = t % C::PPT;
+      const int row = p * C::RPP + lrow;
+      const int chunk = (lane % C::CPR) ^ swz_chunk<D>(row);
+      const uint32_t off = ((uint32_t)(j * BN + row) * D + 8 * chunk) * 2;
+      if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
+      else load_lds16(vrs, vd + p * C::RPP * D, off);
     }
   };
 
-  if (j_end > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  wait_vmem();  // Q, dO fragments above
-  __syncthreads();
+  // Fragment addresses in the swizzled tiles: row reads at (R ^ 16 k) +
+  // 32 sb D, transposing reads at (T ^ 32 (k % DB) [^ 16]) + rows D (see the
+  // dK/dV pass); the bases go through an empty asm so the addresses are
+  // formed next to their reads.
+  uint32_t R = (uint32_t)swz<D>(n, 8 * g);
+  uint32_t Tb = (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  asm volatile("" : "+v"(R), "+v"(Tb));
+  auto rowfrag = [&](const uint16_t* t, int sb, int k) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(t + ((R ^ (16 * k)) + 32 * sb * D));
+  };
+  auto trfrag = [&](const uint16_t* t, int sb, int k) __attribute__((always_inline)) {
+    const uint32_t r0 = (32 * sb + 16 * (k / DB)) * D;
+    const uint32_t x = Tb ^ (32 * (k % DB));
+    const uint2 lo = read_tr_b64(t + (x + r0));
+    const uint2 hi = read_tr_b64(t + ((x ^ 16) + r0 + 8 * D));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
 
-  // Blocks [0, j_unm) need no mask for this wave (every key visible to all
-  // its queries, none past the end); the rest are masked per key.  The two
-  // stages are separate loops with the mask fixed at compile time; every
-  // iteration of either ends in the same barrier, so all waves of the
-  // workgroup still meet at each block.
-  const int j_unm = min(CAUSAL ? w_s1 : n_kv, full_blocks);
-  auto block = [&](int j, auto masked) __attribute__((always_inline)) {
+  f32x16 dq[DB];  // dQ^T: rows = d, columns = queries
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  f32x16 sA, dA, sB, dB;  // S^T and dP^T of even / odd sub-blocks
+
+  // P and dS of one sub-block's elements [r0, r0 + EP): register r is key
+  // key0 + 8 (r/4) + 4 g + r%4.  A query past N has dO = 0 and Delta = 0
+  // (its LSE is +inf, so P = 0).
+  auto vec = [&](const f32x16& s, const f32x16& dp, int key0, int r0, int ep, uint32_t (&pk)[8], auto masked)
+      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int buf = j & 1;
-    const bool more = j + 1 < j_end;
-    if (more) load_block(j + 1);
-    const bool active = wave_live && (!CAUSAL || j < w_s2);
-    if (active) {
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int r = r0; r < r0 + ep; r += 2) {
+      float p0 = fast_exp2(__builtin_fmaf(s[r], qk_scale, -lse2));
+      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], qk_scale, -lse2));
+      if constexpr (MASKED) {
+        const int kr = key0 + 8 * (r / 4) + 4 * g + (r % 4);
+        p0 = kr < key_lim ? p0 : 0.f;
+        p1 = kr + 1 < key_lim ? p1 : 0.f;
+      }
+      pk[r / 2] = pack2(T{}, p0 * (dp[r] - dl), p1 * (dp[r + 1] - dl));
+    }
+  };
+  // dQ^T += K^T dS^T over sub-block sb of a K tile (two 16-key chunks).
+  auto dq_gemm = [&](const uint16_t* kt, int sb, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
+    const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+    uint4 b[3];
+    b[0] = trfrag(kt, sb, 0);
+    b[1] = trfrag(kt, sb, 1);
 #pragma unroll
-        for (int st = 0; st < C::DS; ++st) {
-          s = mma16(T{}, read_row<D>(k_lds[buf], 32 * kb + n, 16 * st + 8 * g), qf[st], s);
-          dp = mma16(T{}, read_row<D>(v_lds[buf], 32 * kb + n, 16 * st + 8 * g), dof[st], dp);
-        }
-        // Register r is key j BN + 32 kb + 8(r/4) + 4g + r%4.
+    for (int k = 0; k < NS; ++k) {
+      if (k + 2 < NS) b[(k + 2) % 3] = trfrag(kt, sb, k + 2);
+      dq[k % DB] = mma16(T{}, b[k % 3], pp[k / DB], dq[k % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // S^T and dP^T of sub-block sb of a K/V tile, not overlapped (prologue).
+  auto sdp = [&](const uint16_t* kt, const uint16_t* vt, int sb, f32x16& s, f32x16& dp)
+      __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], qk_scale, -lse2));
-          if constexpr (MASKED) {
-            const int kr = j * C::BN + 32 * kb + 8 * (r / 4) + 4 * g + (r % 4);
-            p = kr < key_lim ? p : 0.f;
-          }
-          dp[r] = p * (dp[r] - dl);
-        }
-        const uint4 ds0 = pack8(T{}, dp, 0), ds1 = pack8(T{}, dp, 1);
-        // dQ^T += K^T dS^T over this sub-block's 32 keys (two 16-key chunks).
+    for (int k = 0; k < NS; ++k) {
+      s = mma16(T{}, rowfrag(kt, sb, k), qf[k], k == 0 ? f32x16{} : s);
+      dp = mma16(T{}, rowfrag(vt, sb, k), dof[k], k == 0 ? f32x16{} : dp);
+    }
+  };
+  // One step for an unmasked sub-block u (S^T, dP^T in cur): the products
+  // of sub-block u+1 (rows 32 nsb.. of tiles kn / vn) in NS slots, each with
+  // its share of u's vector work, then u's dQ product (K tile kt, rows 32 sb..).
+  auto step = [&](const f32x16& cs, const f32x16& cd, f32x16& ns, f32x16& nd, const uint16_t* kn,
+                  const uint16_t* vn, int nsb, const uint16_t* kt, int sb) __attribute__((always_inline)) {
+    constexpr int EPS = 16 / NS;
+    uint4 a[3], c[3];
+    a[0] = rowfrag(kn, nsb, 0); c[0] = rowfrag(vn, nsb, 0);
+    a[1] = rowfrag(kn, nsb, 1); c[1] = rowfrag(vn, nsb, 1);
+    uint32_t pk[8];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dq[db] = mma16(T{}, read_tr<D>(k_lds[buf], 32 * kb, 32 * db, lane), ds0, dq[db]);
-          dq[db] = mma16(T{}, read_tr<D>(k_lds[buf], 32 * kb + 16, 32 * db, lane), ds1, dq[db]);
-        }
+    for (int k = 0; k < NS; ++k) {
+      if (k + 2 < NS) {
+        a[(k + 2) % 3] = rowfrag(kn, nsb, k + 2);
+        c[(k + 2) % 3] = rowfrag(vn, nsb, k + 2);
+      }
+      ns = mma16(T{}, a[k % 3], qf[k], k == 0 ? f32x16{} : ns);
+      nd = mma16(T{}, c[k % 3], dof[k], k == 0 ? f32x16{} : nd);
+      vec(cs, cd, 0, EPS * k, EPS, pk, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dq_gemm(kt, sb, pk);
+  };
+
+  // One tile j (buffers kc / vc, next kn / vn): this wave's steps u < u_last
+  // in it, and the loads of tile j + 3 (restrict: see the forward).
+  auto tile = [&](int j, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                  const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, uint16_t* __restrict__ kl,
+                  uint16_t* __restrict__ vl, bool load) __attribute__((always_inline)) {
+    if (load) issue(j + 3, kl, vl);
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const int u = j * SUB + i;
+      if (u < u_last) {
+        const uint16_t* kt = i + 1 < SUB ? kc : kn;
+        const uint16_t* vt = i + 1 < SUB ? vc : vn;
+        if (i % 2 == 0) step(sA, dA, sB, dB, kt, vt, (i + 1) % SUB, kc, i);
+        else step(sB, dB, sA, dA, kt, vt, (i + 1) % SUB, kc, i);
       }
     }
-    if (more) store_block(buf ^ 1);
-    __syncthreads();
   };
-  int j = 0;
-  for (; j < min(j_unm, j_end); ++j) block(j, std::false_type{});
-  for (; j < j_end; ++j) block(j, std::true_type{});
 
-  if (query < N) {
+  // ---- prologue: tiles 0..2 in flight, wait for 0 and 1 ------------------
+  wait_vmem();  // Q, dO fragments above
+  issue(0, k_lds[0], v_lds[0]);
+  if (j_end > 1) issue(1, k_lds[1], v_lds[1]);
+  if (j_end > 2) {
+    issue(2, k_lds[2], v_lds[2]);
+    lds_barrier<C::LPW>();
+  } else {
+    lds_barrier<0>();
+  }
+  if (wave_live) sdp(k_lds[0], v_lds[0], 0, sA, dA);
+
+  // ---- main loop, unrolled over the buffers (immediate LDS offsets) ------
+  for (int j0 = 0; j0 < j_end; j0 += C::NBUF) {
+#pragma unroll
+    for (int jj = 0; jj < C::NBUF; ++jj) {
+      const int j = j0 + jj;
+      if (j < j_end) {
+        const bool load = j + 3 < j_end;
+        tile(j, k_lds[jj], v_lds[jj], k_lds[(jj + 1) % C::NBUF], v_lds[(jj + 1) % C::NBUF],
+             k_lds[(jj + 3) % C::NBUF], v_lds[(jj + 3) % C::NBUF], load);
+        if (load) lds_barrier<C::LPW>();
+        else lds_barrier<0>();
+      }
+    }
+  }
+  // The wave's last (masked) sub-block; its tile is among the last four of
+  // the workgroup, still in LDS.
+  if (wave_live) {
+    const uint16_t* kt = k_lds[(u_last / SUB) % C::NBUF];
+    const f32x16 cs = (u_last % 2 == 0) ? sA : sB, cd = (u_last % 2 == 0) ? dA : dB;
+    uint32_t pk[8];
+    vec(cs, cd, 32 * u_last, 0, 16, pk, std::true_type{});
+    dq_gemm(kt, u_last % SUB, pk);
+  }
+
+  if (wave_live && query < N) {
     float* row = dqg + head + (size_t)query * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const f32x16& v = dq[db];
