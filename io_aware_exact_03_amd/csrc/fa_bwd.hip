@@ -166,26 +166,29 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   // (32 h + 16 (k / DB) [+ 8]) D, in elements.  The two bases pass through an
   // empty asm so the compiler computes each address next to its read instead
   // of keeping dozens of precomputed addresses live across the loop.
-  uint32_t R = (uint32_t)swz<D>(n, 8 * g);
-  uint32_t Tb = (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  // (Byte offsets: one XOR per fragment, the row part is the read's
+  // immediate offset.)
+  uint32_t R = 2u * (uint32_t)swz<D>(n, 8 * g);
+  uint32_t Tb = 2u * (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   asm volatile("" : "+v"(R), "+v"(Tb));
+  const char* lb = reinterpret_cast<const char*>(lhs);
+  const char* rb = reinterpret_cast<const char*>(rhs);
   auto rowf = [&](int h, int k) __attribute__((always_inline)) {
-    return *reinterpret_cast<const uint4*>(lhs + ((R ^ (16 * k)) + 32 * h * D));
+    return *reinterpret_cast<const uint4*>(lb + (R ^ (32 * k)) + 64 * h * D);
   };
   auto trf = [&](int h, int k) __attribute__((always_inline)) {
-    const uint32_t r0 = (32 * h + 16 * (k / C::DB)) * D;
-    const uint32_t t = Tb ^ (32 * (k % C::DB));
-    const uint2 x = read_tr_b64(rhs + (t + r0));
-    const uint2 y = read_tr_b64(rhs + ((t ^ 16) + r0 + 8 * D));
+    const uint32_t r0 = 2 * (32 * h + 16 * (k / C::DB)) * D;
+    const uint32_t t = Tb ^ (64 * (k % C::DB));
+    const uint2 x = read_tr_b64(reinterpret_cast<const uint16_t*>(rb + t + r0));
+    const uint2 y = read_tr_b64(reinterpret_cast<const uint16_t*>(rb + (t ^ 32) + r0 + 16 * D));
     return make_uint4(x.x, x.y, y.x, y.y);
   };
   // Per-row values (A: -LSE log2 e, B: Delta) of the elements a slot's
   // vector work touches: elements EP k .. of half h, i.e. rows 32 h +
-  // 8 (r/4) + 4 g + r%4, read EP at a time.
+  // 8 (r/4) + 4 g + r%4; one float4 covers four consecutive elements.
   typedef float fEP __attribute__((ext_vector_type(EP)));
-  auto rowv_slot = [&](int h, int k) __attribute__((always_inline)) {
-    const int r = EP * k;
-    return *reinterpret_cast<const fEP*>(&rowv[32 * h + 8 * (r / 4) + 4 * g + (r % 4)]);
+  auto rowv4 = [&](int h, int q) __attribute__((always_inline)) {
+    return *reinterpret_cast<const float4*>(&rowv[32 * h + 8 * q + 4 * g]);
   };
   // fp16 P of half h: 8 words per lane, stored / read in two 16-byte pieces.
   auto put_p = [&](int h, int piece, const uint32_t (&ph)[8]) __attribute__((always_inline)) {
@@ -203,9 +206,11 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   //     16-byte piece is complete).
   //  B: dS = P (dP - Delta) with P from the fp16 copy, packed to 16-bit for
   //     dK += dS^T Q.
-  auto vec = [&](int h, int k, const f32x16& sd, const fEP& v, uint32_t (&pk)[8], uint32_t (&ph)[8])
+  auto vec = [&](int h, int k, const f32x16& sd, const float4& v4, uint32_t (&pk)[8], uint32_t (&ph)[8])
       __attribute__((always_inline)) {
     const int r0 = EP * k;
+    const float vq[4] = {v4.x, v4.y, v4.z, v4.w};
+    const float* v = vq + (r0 % 4);
 #pragma unroll
     for (int e = 0; e < EP; e += 2) {
       const int r = r0 + e;
@@ -234,8 +239,9 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
 
   f32x16 s0, s1;
   uint4 a[3], b[3];
-  fEP vv[2];
+  float4 vv[2];  // row values: the float4 in use and the next one
   uint32_t pk0[8], pk1[8], ph0[8], ph1[8];
+  constexpr int SPQ = 4 / EP;  // slots per float4 of row values
 
   // ---- phase 1: the first half's product chain ----------------------------
   a[0] = rowf(0, 0);
@@ -244,7 +250,7 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     a[(k + 2) % 3] = k + 2 < NS ? rowf(0, k + 2) : rowf(1, k + 2 - NS);
-    if (k == NS - 1) vv[0] = rowv_slot(0, 0);
+    if (k == NS - 1) vv[0] = rowv4(0, 0);
     s0 = mma16(T{}, a[k % 3], kv[k], k == 0 ? f32x16{} : s0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -255,12 +261,12 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   for (int k = 0; k < NS; ++k) {
     if (k + 2 < NS) a[(NS + k + 2) % 3] = rowf(1, k + 2);
     else b[k + 2 - NS] = trf(0, k + 2 - NS);
-    vv[(k + 1) % 2] = k + 1 < NS ? rowv_slot(0, k + 1) : rowv_slot(1, 0);
+    if (k % SPQ == 0) vv[(k / SPQ + 1) % 2] = k + SPQ < NS ? rowv4(0, (k + SPQ) / SPQ) : rowv4(1, 0);
     if constexpr (!ROLE_A) {
       if (k == NS - 2) get_p(1, ph1);
     }
     s1 = mma16(T{}, a[(NS + k) % 3], kv[k], k == 0 ? f32x16{} : s1);
-    vec(0, k, s0, vv[k % 2], pk0, ph0);
+    vec(0, k, s0, vv[(k / SPQ) % 2], pk0, ph0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- phase 3: the first half's second product, the second half's vector work
@@ -269,9 +275,9 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       b[(k + 2) % 3] = k + 2 < NS ? trf(0, k + 2) : trf(1, k + 2 - NS);
-      if (k + 1 < NS) vv[(k + 1) % 2] = rowv_slot(1, k + 1);
+      if (k % SPQ == 0 && k + SPQ < NS) vv[(k / SPQ + 1) % 2] = rowv4(1, (k + SPQ) / SPQ);
       acc[k % C::DB] = mma16(T{}, pp[k / C::DB], b[k % 3], acc[k % C::DB]);
-      vec(1, k, s1, vv[k % 2], pk1, ph1);
+      vec(1, k, s1, vv[(k / SPQ) % 2], pk1, ph1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -388,10 +394,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     iter(i, q_lds[sa], do_lds[sa], lse_lds[sa], dl_lds[sa], q_lds[sb], do_lds[sb], dl_lds[sb], q_lds[sn],
          do_lds[sn], lse_lds[sn], dl_lds[sn], std::true_type{});
   }
-  for (; i <= n_qblk; ++i) {
-    const int sa = i % NS3, sb = (i + NS3 - 1) % NS3, sn = (i + 1) % NS3;
-    iter(i, q_lds[sa], do_lds[sa], lse_lds[sa], dl_lds[sa], q_lds[sb], do_lds[sb], dl_lds[sb], q_lds[sn],
-         do_lds[sn], lse_lds[sn], dl_lds[sn], std::false_type{});
+  // The rest, unrolled over the three slots so every LDS base is an
+  // immediate.
+  for (int i0 = i - i % NS3; i0 <= n_qblk; i0 += NS3) {
+#pragma unroll
+    for (int jj = 0; jj < NS3; ++jj) {
+      const int ii = i0 + jj;
+      if (ii >= i && ii <= n_qblk) {
+        iter(ii, q_lds[jj], do_lds[jj], lse_lds[jj], dl_lds[jj], q_lds[(jj + NS3 - 1) % NS3],
+             do_lds[(jj + NS3 - 1) % NS3], dl_lds[(jj + NS3 - 1) % NS3], q_lds[(jj + 1) % NS3],
+             do_lds[(jj + 1) % NS3], lse_lds[(jj + 1) % NS3], dl_lds[(jj + 1) % NS3], std::false_type{});
+      }
+    }
   }
 
   // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
