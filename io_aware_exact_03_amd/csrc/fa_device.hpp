@@ -154,6 +154,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its outstanding global loads and stores (lgkmcnt(0), vmcnt left free):
+// enough before another wave may overwrite LDS this wave has read.
+__device__ __forceinline__ void lds_only_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Online softmax, split so the kernel can decide on the correction once per
 // wave.  Scores are the KB 32x32 blocks S^T of one 32-query column block:

@@ -91,28 +91,33 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // One query block of one (batch, head), start to finish.
-  auto block = [&](int bh, int qblk) __attribute__((always_inline)) {
+  // ---- Q fragments of the current query block, held in registers --------
+  // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
+  // rows past N read as zeros.  A negative scale flips Q's sign bits.  The
+  // next block's fragments are loaded during the current block's tail.
+  uint4 qf[DS];
+  auto load_q = [&](int bh, int qblk) __attribute__((always_inline)) {
+    const rsrc_t rs = make_rsrc(qg + (size_t)bh * (size_t)N * D, (uint32_t)N * D * 2);
+    const int q = qblk * C::BM + 32 * wave + n;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      uint4 x = load16(rs, ((uint32_t)q * D + 16 * s + 8 * g) * 2);
+      x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
+      qf[s] = x;
+    }
+  };
+
+  // One query block of one (batch, head), start to finish; (nbh, nqblk) is
+  // the block this workgroup runs next (nbh < 0: none).
+  auto block = [&](int bh, int qblk, int nbh, int nqblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
   const rsrc_t krs = make_rsrc(kg + head, head_bytes);
   const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
 
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + 32 * wave;  // first query of this wave
   const int query = qw0 + n;       // this lane's query
-
-  // ---- Q fragments, held in registers for the whole kernel --------------
-  // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
-  // rows past N read as zeros.  A negative scale flips Q's sign bits.
-  uint4 qf[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    uint4 x = load16(qrs, ((uint32_t)query * D + 16 * s + 8 * g) * 2);
-    x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
-    qf[s] = x;
-  }
 
   // ---- key plan ------------------------------------------------------------
   // The wave's queries see the 32-key sub-blocks [0, u_last].  Every
@@ -342,6 +347,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       }
     }
   }
+  // The next block's Q: the tail below needs no Q fragments.
+  if (nbh >= 0) load_q(nbh, nqblk);
   // The wave's last two sub-blocks: the PV product of u_last - 1 and the
   // masked weights and PV product of u_last.  Their tiles are among the
   // last five of the workgroup (a wave's last sub-block is at most seven
@@ -383,14 +390,33 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // heavier query block of a causal pair goes first.
   const int per_head = items_per_head(n_qblk, CAUSAL);
   const int n_items = BH * per_head;
-  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
-    const int bh = L / per_head;
+  // Block t of item L (heavy first); false past the item's blocks.
+  auto block_at = [&](int L, int t, int* bh, int* qb) {
+    if (L >= n_items) return false;
     int lo, hi;
     const int nb = item_blocks(L % per_head, n_qblk, CAUSAL, &lo, &hi);
-    for (int t = 0; t < nb; ++t) {  // one call site: the block body is large
-      block(bh, t + 1 < nb ? hi : lo);
-      __syncthreads();  // the next block's loads reuse the LDS buffers
+    if (t >= nb) return false;
+    *bh = L / per_head;
+    *qb = t + 1 < nb ? hi : lo;
+    return true;
+  };
+  int L = xcd_remap(blockIdx.x, gridDim.x), t = 0, bh = -1, qb = -1;
+  if (block_at(L, 0, &bh, &qb)) load_q(bh, qb);
+  while (bh >= 0) {  // one call site: the block body is large
+    int nbh = -1, nqb = -1;
+    if (block_at(L, t + 1, &nbh, &nqb)) {
+      ++t;
+    } else {
+      L += gridDim.x;
+      t = 0;
+      if (!block_at(L, 0, &nbh, &nqb)) nbh = -1;
     }
+    block(bh, qb, nbh, nqb);
+    // The next block's loads reuse the LDS buffers; this block's O stores
+    // may still be in flight.
+    lds_only_barrier();
+    bh = nbh;
+    qb = nqb;
   }
 }
 // ===========================================================================
