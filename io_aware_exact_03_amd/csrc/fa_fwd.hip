@@ -161,10 +161,29 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   f32x16 sA, sB;                    // scores of even / odd sub-blocks
 
   // S^T of one sub-block (32 keys x 32 queries) from rows 32 sb .. of a K tile.
+  // In the swizzled layout every fragment sits at a per-lane base XOR a
+  // constant plus a row offset (the chunk permutation only touches the
+  // within-row address bits): row reads at (R ^ 32 k) + 64 sb D bytes,
+  // transposing reads at (T ^ 64 (k % DB) [^ 32]) + 2 rows D.  The bases go
+  // through an empty asm so each address is formed next to its read.
+  uint32_t Rb = 2u * (uint32_t)swz<D>(n, 8 * g);
+  uint32_t Tb = 2u * (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  asm volatile("" : "+v"(Rb), "+v"(Tb));
+  auto kfrag = [&](const uint16_t* kt, int sb, int k) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kt) + (Rb ^ (32 * k)) + 64 * sb * D);
+  };
+  auto vfrag = [&](const uint16_t* vt, int sb, int k) __attribute__((always_inline)) {
+    const char* base = reinterpret_cast<const char*>(vt);
+    const uint32_t r0 = 2 * (32 * sb + 16 * (k / DB)) * D;
+    const uint32_t t = Tb ^ (64 * (k % DB));
+    const uint2 lo = read_tr_b64(reinterpret_cast<const uint16_t*>(base + t + r0));
+    const uint2 hi = read_tr_b64(reinterpret_cast<const uint16_t*>(base + (t ^ 32) + r0 + 16 * D));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
   auto s_gemm = [&](const uint16_t* kt, int sb, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < DS; ++st)
-      s = mma16(T{}, read_row<D>(kt, 32 * sb + n, 16 * st + 8 * g), qf[st], st == 0 ? f32x16{} : s);
+      s = mma16(T{}, kfrag(kt, sb, st), qf[st], st == 0 ? f32x16{} : s);
   };
   // Weights of sub-block `cur` (first key key0) with the current reference,
   // packed to 16-bit as the B operand of the PV product; returns the lane sum.
@@ -213,12 +232,6 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // takes the 16 keys 16 (k / DB) .. of the sub-block, d block k % DB.
   constexpr int NS = DS;  // = 2 DB: both products of a sub-block have NS steps
   static_assert(NS == 2 * DB, "slot pairing");
-  auto kfrag = [&](const uint16_t* kt, int sb, int k) __attribute__((always_inline)) {
-    return read_row<D>(kt, 32 * sb + n, 16 * k + 8 * g);
-  };
-  auto vfrag = [&](const uint16_t* vt, int sb, int k) __attribute__((always_inline)) {
-    return read_tr<D>(vt, 32 * sb + 16 * (k / DB), 32 * (k % DB), lane);
-  };
   // O^T += V^T P^T over one sub-block, not overlapped (the wave's last ones).
   auto pv_gemm = [&](const uint16_t* vt, int sb, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
     const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
@@ -240,7 +253,9 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // and transcendental work hides under the matrix products.  LDS reads run
   // two slots ahead and cross into the next step: ka / vb carry the first
   // two K and V fragments the next step consumes.
-  uint4 ka[2], vb[2];
+  constexpr int PD = 3;  // fragments read ahead of the product that uses them
+  static_assert(PD <= NS, "prefetch distance");
+  uint4 ka[PD], vb[PD];
   uint32_t pkp[8];  // packed weights of sub-block u-1
   auto step = [&](f32x16& cur, int key0, f32x16& nxt, const uint16_t* kt, int ksb, const uint16_t* vt, int vsb,
                   const uint16_t* kt2, int ksb2, const uint16_t* vt2, int vsb2, auto with_pv)
@@ -248,20 +263,24 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     constexpr bool PV = decltype(with_pv)::value;
     constexpr int EPS = 16 / NS;  // weights per slot
     const uint4 pp[2] = {make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]), make_uint4(pkp[4], pkp[5], pkp[6], pkp[7])};
-    uint4 a[3] = {ka[0], ka[1], ka[1]};
-    uint4 b[3] = {vb[0], vb[1], vb[1]};
+    uint4 a[PD + 1], b[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      a[i] = ka[i];
+      b[i] = vb[i];
+    }
     float part[4];
     uint32_t pk[8];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      if (k + 2 < NS) {
-        a[(k + 2) % 3] = kfrag(kt, ksb, k + 2);
-        if constexpr (PV) b[(k + 2) % 3] = vfrag(vt, vsb, k + 2);
+      if (k + PD < NS) {
+        a[(k + PD) % (PD + 1)] = kfrag(kt, ksb, k + PD);
+        if constexpr (PV) b[(k + PD) % (PD + 1)] = vfrag(vt, vsb, k + PD);
       } else {
-        ka[k + 2 - NS] = kfrag(kt2, ksb2, k + 2 - NS);
-        vb[k + 2 - NS] = vfrag(vt2, vsb2, k + 2 - NS);
+        ka[k + PD - NS] = kfrag(kt2, ksb2, k + PD - NS);
+        vb[k + PD - NS] = vfrag(vt2, vsb2, k + PD - NS);
       }
-      nxt = mma16(T{}, a[k % 3], qf[k], k == 0 ? f32x16{} : nxt);
+      nxt = mma16(T{}, a[k % (PD + 1)], qf[k], k == 0 ? f32x16{} : nxt);
 #pragma unroll
       for (int e = 0; e < EPS; e += 2) {
         const int r = k * EPS + e;
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         part[(r + 1) % 4] = r < 4 ? p1 : part[(r + 1) % 4] + p1;
         pk[r / 2] = pack2(T{}, p0, p1);
       }
-      if constexpr (PV) oacc[k % DB] = mma16(T{}, b[k % 3], pp[k / DB], oacc[k % DB]);
+      if constexpr (PV) oacc[k % DB] = mma16(T{}, b[k % (PD + 1)], pp[k / DB], oacc[k % DB]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // The rare redo rebuilds pk; this use keeps the compiler from moving the
@@ -323,8 +342,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     if (u_last >= 1) {
       // step 0: scores of sub-block 1, weights of 0, no PV product yet
       const uint16_t* k2 = k_lds[2 / SUB];
-      ka[0] = kfrag(k_lds[0], 1, 0);
-      ka[1] = kfrag(k_lds[0], 1, 1);
+#pragma unroll
+      for (int i = 0; i < PD; ++i) ka[i] = kfrag(k_lds[0], 1, i);
       step(sA, 0, sB, k_lds[0], 1, v_lds[0], 0, k2, 2 % SUB, v_lds[0], 0, std::false_type{});
     }
   }
