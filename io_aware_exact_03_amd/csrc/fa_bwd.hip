@@ -83,9 +83,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // vector work of one half runs under the matrix products of the other:
 //   A: S0 | S1 + weights P0 | dV(P0) + weights P1 | dV(P1)
 //   B: dP0 | dP1 + dS0 | dK(dS0) + dS1 | dK(dS1)
-// Q, dO and Delta go from global memory straight into LDS (no registers)
-// one block ahead through three slots (A's block, B's block, the block in
-// flight); wave 0 stages -LSE log2(e) of the block in flight.  One barrier
+// Q and dO go from global memory straight into LDS (no registers) one
+// block ahead through three slots (A's block, B's block, the block in
+// flight); waves 0 and 1 stage -LSE log2(e) and -Delta of the block in
+// flight.  One barrier
 // per iteration.  A negative scale is applied by negating K, so Q lands in
 // LDS unchanged.
 // ---------------------------------------------------------------------------
@@ -112,14 +113,16 @@ struct KVWave {
 // (t % PPA) RPL .. + RPL of Q (t < PPA) or of dO, straight into LDS; lane l
 // fills LDS bytes 16 l of the piece, i.e. tile row l / CPR and stored chunk
 // l % CPR, which holds the row's logical chunk (l % CPR) ^ swz_chunk(row).
-// Wave 1 loads Delta into LDS the same way; wave 0 loads LSE into a register
-// (returned) and stores -LSE log2(e) with kv_stage_lse once it has arrived.
+// Wave 0 loads the block's LSE and wave 1 its Delta into a register
+// (returned); once it has arrived they store -LSE log2(e) and -Delta into
+// LDS (kv_stage_rows).
 template <int D>
 __device__ __forceinline__ float kv_issue(const KVWave& w, int i, uint16_t* __restrict__ q_dst,
-                                          uint16_t* __restrict__ do_dst, float* __restrict__ d_dst) {
+                                          uint16_t* __restrict__ do_dst) {
   using C = KV<D>;
-  float lse = 0.f;
-  if (w.wave == 0) lse = load4f(w.lrs, (uint32_t)(i * C::BMQ + w.lane) * 4);
+  float val = 0.f;
+  if (w.wave == 0) val = load4f(w.lrs, (uint32_t)(i * C::BMQ + w.lane) * 4);
+  if (w.wave == 1) val = load4f(w.drs, (uint32_t)(i * C::BMQ + w.lane) * 4);
   const int lrow = w.lane / C::CPR;
 #pragma unroll
   for (int e = 0; e < C::LPB; ++e) {
@@ -132,8 +135,15 @@ __device__ __forceinline__ float kv_issue(const KVWave& w, int i, uint16_t* __re
     if (is_q) load_lds16(w.qrs, q_dst + piece, off);
     else load_lds16(w.dors, do_dst + piece, off);
   }
-  if (w.wave == 1) load_lds4(w.drs, d_dst, (uint32_t)(i * C::BMQ + w.lane) * 4);
-  return lse;
+  return val;
+}
+// The per-row values of a block as the waves consume them: -LSE log2(e)
+// (added by A's weights) and -Delta (the initial accumulator of B's dP, so
+// the dP product yields dP - Delta directly).
+__device__ __forceinline__ void kv_stage_rows(const KVWave& w, float val, float* __restrict__ l_dst,
+                                              float* __restrict__ d_dst) {
+  if (w.wave == 0) l_dst[w.lane] = -val * kLog2e;
+  if (w.wave == 1) d_dst[w.lane] = -val;
 }
 
 // One iteration of a wave's work on its block: four phases over the two
@@ -186,9 +196,18 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   // Per-row values (A: -LSE log2 e, B: Delta) of the elements a slot's
   // vector work touches: elements EP k .. of half h, i.e. rows 32 h +
   // 8 (r/4) + 4 g + r%4; one float4 covers four consecutive elements.
-  typedef float fEP __attribute__((ext_vector_type(EP)));
   auto rowv4 = [&](int h, int q) __attribute__((always_inline)) {
     return *reinterpret_cast<const float4*>(&rowv[32 * h + 8 * q + 4 * g]);
+  };
+  // B: the 16 row values of half h as an accumulator (register r <-> row).
+  auto rowacc = [&](int h) __attribute__((always_inline)) {
+    f32x16 c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = rowv4(h, q);
+      c[4 * q] = x.x; c[4 * q + 1] = x.y; c[4 * q + 2] = x.z; c[4 * q + 3] = x.w;
+    }
+    return c;
   };
   // fp16 P of half h: 8 words per lane, stored / read in two 16-byte pieces.
   auto put_p = [&](int h, int piece, const uint32_t (&ph)[8]) __attribute__((always_inline)) {
@@ -225,11 +244,12 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
         pk[r / 2] = pack2(T{}, p0, p1);
         ph[r / 2] = pack2(F16{}, p0, p1);
       } else {
-        // fp16 P times an fp32 factor, one mixed-precision multiply-add each
+        // fp16 P times dP - Delta (the accumulator), one mixed-precision
+        // multiply-add each
         const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(ph[r / 2] & 0xffffu));
         const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(ph[r / 2] >> 16));
-        pk[r / 2] = pack2(T{}, __builtin_fmaf((float)h0, sd[r] - v[e], 0.f),
-                          __builtin_fmaf((float)h1, sd[r + 1] - v[e + 1], 0.f));
+        pk[r / 2] = pack2(T{}, __builtin_fmaf((float)h0, sd[r], 0.f), __builtin_fmaf((float)h1, sd[r + 1], 0.f));
+        (void)v;
       }
     }
     if constexpr (ROLE_A) {
@@ -246,12 +266,20 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   // ---- phase 1: the first half's product chain ----------------------------
   a[0] = rowf(0, 0);
   a[1] = rowf(0, 1);
-  if constexpr (!ROLE_A) get_p(0, ph0);
+  f32x16 c0 = f32x16{}, c1 = f32x16{};  // initial accumulators (B: -Delta rows)
+  if constexpr (!ROLE_A) {
+    get_p(0, ph0);
+    c0 = rowacc(0);
+  }
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     a[(k + 2) % 3] = k + 2 < NS ? rowf(0, k + 2) : rowf(1, k + 2 - NS);
-    if (k == NS - 1) vv[0] = rowv4(0, 0);
-    s0 = mma16(T{}, a[k % 3], kv[k], k == 0 ? f32x16{} : s0);
+    if constexpr (ROLE_A) {
+      if (k == NS - 1) vv[0] = rowv4(0, 0);
+    } else {
+      if (k == NS - 1) c1 = rowacc(1);
+    }
+    s0 = mma16(T{}, a[k % 3], kv[k], k == 0 ? c0 : s0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- phase 2: the second half's chain, the first half's vector work ----
@@ -261,11 +289,12 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   for (int k = 0; k < NS; ++k) {
     if (k + 2 < NS) a[(NS + k + 2) % 3] = rowf(1, k + 2);
     else b[k + 2 - NS] = trf(0, k + 2 - NS);
-    if (k % SPQ == 0) vv[(k / SPQ + 1) % 2] = k + SPQ < NS ? rowv4(0, (k + SPQ) / SPQ) : rowv4(1, 0);
-    if constexpr (!ROLE_A) {
+    if constexpr (ROLE_A) {
+      if (k % SPQ == 0) vv[(k / SPQ + 1) % 2] = k + SPQ < NS ? rowv4(0, (k + SPQ) / SPQ) : rowv4(1, 0);
+    } else {
       if (k == NS - 2) get_p(1, ph1);
     }
-    s1 = mma16(T{}, a[(NS + k) % 3], kv[k], k == 0 ? f32x16{} : s1);
+    s1 = mma16(T{}, a[(NS + k) % 3], kv[k], k == 0 ? c1 : s1);
     vec(0, k, s0, vv[(k / SPQ) % 2], pk0, ph0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -275,7 +304,9 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       b[(k + 2) % 3] = k + 2 < NS ? trf(0, k + 2) : trf(1, k + 2 - NS);
-      if (k % SPQ == 0 && k + SPQ < NS) vv[(k / SPQ + 1) % 2] = rowv4(1, (k + SPQ) / SPQ);
+      if constexpr (ROLE_A) {
+        if (k % SPQ == 0 && k + SPQ < NS) vv[(k / SPQ + 1) % 2] = rowv4(1, (k + SPQ) / SPQ);
+      }
       acc[k % C::DB] = mma16(T{}, pp[k / C::DB], b[k % 3], acc[k % C::DB]);
       vec(1, k, s1, vv[(k / SPQ) % 2], pk1, ph1);
       __builtin_amdgcn_sched_barrier(0);
@@ -304,7 +335,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::NSLOT][C::BMQ * D];
   __shared__ __attribute__((aligned(16))) uint4 x_lds[2][C::NP][4 * 64];          // fp16 P, A -> B
   __shared__ __attribute__((aligned(16))) float lse_lds[C::NSLOT][C::BMQ];        // -LSE log2(e)
-  __shared__ __attribute__((aligned(16))) float dl_lds[C::NSLOT][C::BMQ];         // Delta
+  __shared__ __attribute__((aligned(16))) float dl_lds[C::NSLOT][C::BMQ];         // -Delta
 
   KVWave w;
   w.lane = threadIdx.x & 63;
@@ -353,8 +384,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   auto block_masked = [&](int i) { return CAUSAL && i * C::BMQ < w.kw0 + C::KW - 1; };
 
   wait_vmem();  // K or V fragments above
-  float lse_in = kv_issue<D>(w, i_lo, q_lds[i_lo % C::NSLOT], do_lds[i_lo % C::NSLOT], dl_lds[i_lo % C::NSLOT]);
-  if (w.wave == 0) lse_lds[i_lo % C::NSLOT][w.lane] = -lse_in * kLog2e;
+  float row_in = kv_issue<D>(w, i_lo, q_lds[i_lo % C::NSLOT], do_lds[i_lo % C::NSLOT]);
+  kv_stage_rows(w, row_in, lse_lds[i_lo % C::NSLOT], dl_lds[i_lo % C::NSLOT]);
   lds_barrier<0>();
 
   // Iteration i: A works on block i (slot i % 3), B on block i - 1 (slot
@@ -367,7 +398,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
                   float* __restrict__ ln, float* __restrict__ dln, auto may_mask) __attribute__((always_inline)) {
     constexpr bool MAY_MASK = decltype(may_mask)::value;
     const bool ahead = i + 1 < n_qblk;
-    if (ahead) lse_in = kv_issue<D>(w, i + 1, qn, dn, dln);
+    if (ahead) row_in = kv_issue<D>(w, i + 1, qn, dn);
     if (w.role_a) {
       if (i < n_qblk && block_active(i)) {
         if (MAY_MASK && block_masked(i))
@@ -378,9 +409,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     } else if (i > i_lo && block_active(i - 1)) {
       kv_iter<T, D, false, false>(w, i - 1, kv, acc, db_, qb, dlb, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
     }
-    // Block i + 1 must be in LDS after this barrier (wave 0 first stores its
-    // -LSE log2 e, whose load has arrived by now).
-    if (ahead && w.wave == 0) ln[w.lane] = -lse_in * kLog2e;
+    // Block i + 1 must be in LDS after this barrier (waves 0 and 1 first
+    // store its row values, whose loads have arrived by now).
+    if (ahead) kv_stage_rows(w, row_in, ln, dln);
     lds_barrier<0>();
   };
   // A pair's keys start at kw0 = 128 kblk + 32 pw, so its only masked block
