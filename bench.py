@@ -423,6 +423,30 @@ def run_legs(torch, fa, fa_synth, dev):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
+    # grouped-query causal prefill: forward and backward through the grouped
+    # entry points, next to the per-head path on K/V repeated G times
+    w = fa_synth.GQA_PREFILL
+    q, k, v, do = (t.to(dev) for t in fa_synth.workload_inputs(w))
+    G = w.H // w.kv_heads
+    o, lse = fa.fwd_gqa(q, k, v, w.scale, w.causal)
+    ms_f, _ = time_reps(lambda: fa.fwd_gqa(q, k, v, w.scale, w.causal, out=o, lse=lse), 10, torch)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bufs = dict(delta=torch.empty((w.B, w.H, w.N), **f32), dq=torch.empty((w.B, w.H, w.N, w.d), **f32),
+                dk=torch.empty((w.B, w.kv_heads, w.N, w.d), **f32), dv=torch.empty((w.B, w.kv_heads, w.N, w.d), **f32))
+    ms_b, _ = time_reps(lambda: fa.bwd_gqa(q, k, v, o, do, lse, w.scale, w.causal, **bufs), 10, torch)
+    del bufs
+    kr, vr = k.repeat_interleave(G, dim=1).contiguous(), v.repeat_interleave(G, dim=1).contiguous()
+    ms_rep, _ = time_reps(lambda: fa.fwd(q, kr, vr, w.scale, w.causal, out=o, lse=lse), 10, torch)
+    tf_f = fwd_flops(w.B, w.H, w.N, w.d, w.causal) / (ms_f * 1e-3) / 1e12
+    tf_b = bwd_flops(w.B, w.H, w.N, w.d, w.causal) / (ms_b * 1e-3) / 1e12
+    entry = {"G": G, "fwd_ms": ms_f, "fwd_tflops": tf_f, "fwd_frac_mfma_peak": tf_f / PEAK_BF16_TFLOPS,
+             "bwd_ms": ms_b, "bwd_tflops": tf_b, "bwd_frac_mfma_peak": tf_b / PEAK_BF16_TFLOPS,
+             "fwd_ms_per_head_path_on_repeated_kv": ms_rep}
+    legs[w.name] = entry
+    log(f"[bench] {w.name}: {entry}")
+    del q, k, v, do, o, lse, kr, vr
+    torch.cuda.empty_cache()
+
     # non-causal fp16 sweep, fused vs naive, with the byte models
     for w in fa_synth.NONCAUSAL_SWEEP:
         q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))

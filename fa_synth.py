@@ -36,9 +36,15 @@ class Workload:
     sigma_v: float = 1.0
     passes: tuple = field(default=("fwd",))
     naive: bool = False
+    Hkv: int = 0  # K/V heads per batch; 0 = H (one K/V head per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     def describe(self) -> str:
-        return (f"{self.name}: B={self.B} H={self.H} N={self.N} d={self.d} {self.dtype} "
+        kv = f" Hkv={self.Hkv}" if self.Hkv else ""
+        return (f"{self.name}: B={self.B} H={self.H}{kv} N={self.N} d={self.d} {self.dtype} "
                 f"{'causal' if self.causal else 'non-causal'} scale={self.scale:.6g} seed={self.seed}")
 
 
@@ -63,25 +69,33 @@ TRAIN_STEP = Workload("causal_train_step_B4_H16_N4096_d128_bf16", 4, 16, 4096, 1
 
 ALL_WORKLOADS = (SINGLE_HEAD_F32,) + NONCAUSAL_SWEEP + (CAUSAL_PREFILL, LONG_CAUSAL, TRAIN_STEP)
 
+# Grouped-query causal prefill: 64 query heads sharing 8 K/V heads (the
+# head counts of the 70B-class model the serving discussion names), forward
+# and backward.
+GQA_PREFILL = Workload("gqa_causal_prefill_B1_H64_Hkv8_N8192_d128_bf16", 1, 64, 8192, 128, "bf16", True,
+                       1 / math.sqrt(128), 1006, passes=("fwd", "bwd"), Hkv=8)
+
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, sigma_qk: float = 1.0,
-                sigma_v: float = 1.0, with_dout: bool = False):
-    """Q, K, V (and dO) as CPU tensors of ``dtype`` and shape [B,H,N,d].
+                sigma_v: float = 1.0, with_dout: bool = False, Hkv: int = 0):
+    """Q, K, V (and dO) as CPU tensors of ``dtype``: Q and dO [B,H,N,d], K
+    and V [B,Hkv,N,d] (Hkv = 0 means H).
 
     Q and K are N(0, sigma_qk^2), V and dO are N(0, sigma_v^2) and N(0, 1).
     """
     g = torch.Generator(device="cpu").manual_seed(seed)
     shape = (B, H, N, d)
+    kv_shape = (B, Hkv or H, N, d)
 
-    def draw(sigma):
+    def draw(sigma, shape=shape):
         t = torch.randn(*shape, generator=g, dtype=torch.float32)
         if sigma != 1.0:
             t = t * sigma
         return t.to(DTYPES[dtype])
 
     q = draw(sigma_qk)
-    k = draw(sigma_qk)
-    v = draw(sigma_v)
+    k = draw(sigma_qk, kv_shape)
+    v = draw(sigma_v, kv_shape)
     if not with_dout:
         return q, k, v
     return q, k, v, draw(1.0)
@@ -90,7 +104,7 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, sigma_qk:
 def workload_inputs(w: Workload, with_dout: bool | None = None):
     if with_dout is None:
         with_dout = "bwd" in w.passes
-    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.sigma_qk, w.sigma_v, with_dout)
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.sigma_qk, w.sigma_v, with_dout, w.Hkv)
 
 
 def to_f64(t):

@@ -115,6 +115,45 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  void* stream);
 
 /*
+ * Grouped-query attention (GQA; MQA when Hkv = 1), the head sharing that
+ * "Flash Attention: IO-awareness principle" names in its section on serving
+ * (fewer K/V heads, hence fewer tiles of K/V work).  The H query heads of a
+ * batch share Hkv K/V heads: query head h reads K/V head h / (H / Hkv), so
+ * G = H / Hkv consecutive query heads form a group.  The result for query
+ * head h is exactly fa_fwd's with K, V replaced by that K/V head's slices.
+ * q, o: dtype [B,H,N,d]; k, v: dtype [B,Hkv,N,d]; lse: float32 [B,H,N].
+ * Requires 1 <= Hkv <= H and H % Hkv == 0, else FA_ERR_ARG; every other
+ * argument, check and error as fa_fwd.  fa_fwd(...) is
+ * fa_fwd_gqa(..., H, Hkv = H, ...).
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+               void* stream);
+
+/*
+ * Backward of fa_fwd_gqa.  q, o, dout: dtype [B,H,N,d]; k, v: dtype
+ * [B,Hkv,N,d]; lse, delta_ws: float32 [B,H,N]; dq: float32 [B,H,N,d];
+ * dk, dv: float32 [B,Hkv,N,d], each the sum over the K/V head's G query
+ * heads of what fa_bwd would give that query head (the chain rule through
+ * the shared K and V).  The dK/dV kernel walks a K/V block's G query heads
+ * in turn and accumulates on chip, so dk and dv are written once, fully
+ * overwritten, with no atomics.  Same three launches, checks and errors as
+ * fa_bwd, plus 1 <= Hkv <= H, H % Hkv == 0 (else FA_ERR_ARG).
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, float* delta_ws, float* dq, float* dk, float* dv,
+               int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+               void* stream);
+
+/*
+ * Host copy of the head map fa_fwd_gqa / fa_bwd_gqa use: the flat K/V head
+ * b * Hkv + h / (H / Hkv) that the flat query head bh = b * H + h reads.
+ * Returns -1 unless 0 <= bh, 1 <= Hkv <= H, H % Hkv == 0.  Pure host
+ * function (no HIP call).
+ */
+int fa_kv_head(int bh, int H, int Hkv);
+
+/*
  * Naive three-kernel forward ("Flash Attention -- five lessons converging
  * into 80 lines", "Two implementations"; Algorithm 0 of the FlashAttention
  * paper review): kernel 1 writes S = scale * Q K^T for all N x N into

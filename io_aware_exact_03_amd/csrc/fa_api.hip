@@ -82,28 +82,35 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
   return (size_t)B * H * (size_t)N * (size_t)N * (dtype == FA_F32 ? 4 : 2);
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-           float scale, int causal, int dtype, void* stream) {
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+               int d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
   const int st = check_shape(B, H, N, d, dtype, causal, scale);
   if (st != FA_OK) return st;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   fa::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
+  a.BH = B * H; a.G = H / Hkv; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
   a.qk_scale = fabsf(scale) * fa::kLog2eHost;
   a.neg = scale < 0.f;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(fa::launch_fwd(a));
 }
 
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
+}
+
 static int bwd_common(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d,
-                      float scale, int causal, int dtype, void* stream) {
+                      const float* lse, float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int Hkv,
+                      int N, int d, float scale, int causal, int dtype, void* stream) {
   if (stage < 0 || stage > 3) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !dout || !lse || !delta_ws || !dq || !dk || !dv) return FA_ERR_ARG;
   const int st = check_shape(B, H, N, d, dtype, causal, scale);
   if (st != FA_OK) return st;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit MFMA only
   const void* ptrs[] = {q, k, v, o, dout, lse, delta_ws, dq, dk, dv};
   for (const void* p : ptrs)
@@ -111,7 +118,8 @@ static int bwd_common(int stage, const void* q, const void* k, const void* v, co
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = delta_ws; a.dq = dq; a.dk = dk; a.dv = dv;
-  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0; a.scale = scale;
+  a.BH = B * H; a.G = H / Hkv; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
+  a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(fa::launch_bwd(a, stage));
 }
@@ -119,14 +127,26 @@ static int bwd_common(int stage, const void* q, const void* k, const void* v, co
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
            int dtype, void* stream) {
-  return bwd_common(0, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream);
+  return bwd_common(0, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, stream);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int Hkv, int N, int d, float scale,
+               int causal, int dtype, void* stream) {
+  return bwd_common(0, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, stream);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, float* delta_ws, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                  float scale, int causal, int dtype, void* stream) {
   if (stage < 1) return FA_ERR_ARG;
-  return bwd_common(stage, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream);
+  return bwd_common(stage, q, k, v, o, dout, lse, delta_ws, dq, dk, dv, B, H, H, N, d, scale, causal, dtype,
+                    stream);
+}
+
+int fa_kv_head(int bh, int H, int Hkv) {
+  if (bh < 0 || H < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0) return -1;
+  return fa::kv_head_of(bh, H / Hkv);
 }
 
 int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* s_ws, void* p_ws, int B,

@@ -324,12 +324,14 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+// GROUPED = false compiles the one-query-head-per-K/V-head case (G = 1)
+// without the loop over a group, which costs registers.
+template <typename T, int D, bool CAUSAL, bool GROUPED>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
-    float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, int BH, float qk_scale,
-    float dk_scale, uint32_t ksign) {
+    float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, int BHkv, int G,
+    float qk_scale, float dk_scale, uint32_t ksign) {
   using C = KV<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[C::NSLOT][C::BMQ * D];   // swizzled row-major
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::NSLOT][C::BMQ * D];
@@ -347,14 +349,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   w.N = N;
   w.qk_scale = qk_scale;
 
-  // One block of BNK keys of one (batch, head), start to finish.
-  auto block = [&](int bh, int kblk) __attribute__((always_inline)) {
-  const size_t head = (size_t)bh * (size_t)N * D;
+  // One block of BNK keys of one K/V head bkv, start to finish: its G query
+  // heads' contributions are accumulated one head after another.
+  auto block = [&](int bkv, int kblk) __attribute__((always_inline)) {
+  const size_t head = (size_t)bkv * (size_t)N * D;  // K, V, dK, dV
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  w.qrs = make_rsrc(qg + head, head_bytes);
-  w.dors = make_rsrc(dog + head, head_bytes);
-  w.lrs = make_rsrc(lseg + (size_t)bh * N, (uint32_t)N * 4);
-  w.drs = make_rsrc(deltag + (size_t)bh * N, (uint32_t)N * 4);
   w.kw0 = kblk * C::BNK + w.pw * C::KW;  // first key of this pair
   const bool pair_live = w.kw0 < N;
 
@@ -384,6 +383,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   auto block_masked = [&](int i) { return CAUSAL && i * C::BMQ < w.kw0 + C::KW - 1; };
 
   wait_vmem();  // K or V fragments above
+  const int n_group = GROUPED ? G : 1;
+  for (int j = 0; j < n_group; ++j) {  // the query heads sharing this K/V head
+  const size_t qhead = GROUPED ? (size_t)q_head_of(bkv, G, j) : (size_t)bkv;
+  w.qrs = make_rsrc(qg + qhead * N * D, head_bytes);
+  w.dors = make_rsrc(dog + qhead * N * D, head_bytes);
+  w.lrs = make_rsrc(lseg + qhead * N, (uint32_t)N * 4);
+  w.drs = make_rsrc(deltag + qhead * N, (uint32_t)N * 4);
   float row_in = kv_issue<D>(w, i_lo, q_lds[i_lo % C::NSLOT], do_lds[i_lo % C::NSLOT]);
   kv_stage_rows(w, row_in, lse_lds[i_lo % C::NSLOT], dl_lds[i_lo % C::NSLOT]);
   lds_barrier<0>();
@@ -439,6 +445,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     }
   }
 
+  // The last iteration ended with a barrier after every LDS read, so the
+  // next query head may refill the slots at once.
+  }
+
   // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
   float* out = (w.role_a ? dvg : dkg) + head;
   const float sc = w.role_a ? 1.f : dk_scale;
@@ -451,11 +461,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     }
   };
 
-  // Persistent loop over equal-cost items (items_per_head / item_blocks);
-  // in each round every XCD works on a contiguous range of items.  The
-  // heavier key block of a causal pair (the lower one) goes first.
+  // Persistent loop over equal-cost items (items_per_head / item_blocks) of
+  // the K/V heads; in each round every XCD works on a contiguous range of
+  // items.  The heavier key block of a causal pair (the lower one) goes
+  // first.
   const int per_head = items_per_head(n_kblk, CAUSAL);
-  const int n_items = BH * per_head;
+  const int n_items = BHkv * per_head;
   for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
     const int bh = L / per_head;
     int lo, hi;
@@ -494,7 +505,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
-    float* __restrict__ dqg, int N, int n_qblk, int BH, float qk_scale, float dq_scale, uint32_t qsign) {
+    float* __restrict__ dqg, int N, int n_qblk, int BH, int G, float qk_scale, float dq_scale,
+    uint32_t qsign) {
   using C = QG<D>;
   constexpr int BN = C::BN, DS = C::DS, DB = C::DB, SUB = C::SUB, NS = C::DS;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
@@ -507,8 +519,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   // One block of BM queries of one (batch, head), start to finish.
   auto qblock = [&](int bh, int qblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;  // shared by G query heads
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  const rsrc_t krs = make_rsrc(kg + head, head_bytes), vrs = make_rsrc(vg + head, head_bytes);
+  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes), vrs = make_rsrc(vg + kvhead, head_bytes);
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * 32;
   const int query = qw0 + n;
@@ -733,7 +746,7 @@ hipError_t run(const BwdArgs& a, int stage) {
   const long long g1 = (rows + RPB - 1) / RPB;
   const int n_kblk = (a.N + KV<D>::BNK - 1) / KV<D>::BNK;
   const int n_qblk = (a.N + QG<D>::BM - 1) / QG<D>::BM;
-  long long g2 = (long long)items_per_head(n_kblk, CAUSAL) * a.BH;
+  long long g2 = (long long)items_per_head(n_kblk, CAUSAL) * (a.BH / a.G);
   long long g3 = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // dK/dV and dQ run persistent grids of one workgroup per CU (registers
@@ -757,14 +770,18 @@ hipError_t run(const BwdArgs& a, int stage) {
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 2) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, a.BH, qk_scale, a.scale, qsign);
+    if (a.G > 1)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, true>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q, k,
+                         v, dout, a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, a.BH / a.G, a.G, qk_scale, a.scale, qsign);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, false>), dim3((unsigned)g2), dim3(KV<D>::NT), 0, a.stream, q,
+                         k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, n_kblk, a.BH, 1, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 3) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(QG<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, qk_scale, a.scale, qsign);
+                       a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, a.G, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

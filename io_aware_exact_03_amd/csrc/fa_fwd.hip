@@ -79,8 +79,8 @@ constexpr float kSumLimit = 256.f;
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, int BH, float qk_scale,
-    uint32_t qsign) {
+    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, int BH, int G,
+    float qk_scale, uint32_t qsign) {
   using C = Fwd16<T, D, BN, CAUSAL>;
   constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
@@ -111,9 +111,10 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // the block this workgroup runs next (nbh < 0: none).
   auto block = [&](int bh, int qblk, int nbh, int nqblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;  // shared by G query heads
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const rsrc_t krs = make_rsrc(kg + head, head_bytes);
-  const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
+  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
 
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + 32 * wave;  // first query of this wave
@@ -457,7 +458,7 @@ struct Fwd32 {
 template <int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
                                                         const float* __restrict__ vg, float* __restrict__ og,
-                                                        float* __restrict__ lseg, int N, int n_qblk,
+                                                        float* __restrict__ lseg, int N, int n_qblk, int G,
                                                         float qk_scale, float qsign) {
   using C = Fwd32<D, BN, NW, CAUSAL>;
   __shared__ __attribute__((aligned(16))) float k_lds[2][BN * C::KROW];
@@ -474,8 +475,9 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 4;
   const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
-  const rsrc_t krs = make_rsrc(kg + head, head_bytes);
-  const rsrc_t vrs = make_rsrc(vg + head, head_bytes);
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;
+  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * 32;
   const int query = qw0 + n;
@@ -631,7 +633,7 @@ hipError_t launch16(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk, a.BH,
-                     a.qk_scale, a.neg ? 0x80008000u : 0u);
+                     a.G, a.qk_scale, a.neg ? 0x80008000u : 0u);
   return hipGetLastError();
 }
 
@@ -644,7 +646,7 @@ hipError_t launch32(const FwdArgs& a) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd32_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-                     static_cast<float*>(a.o), a.lse, a.N, n_qblk, a.qk_scale, a.neg ? -1.f : 1.f);
+                     static_cast<float*>(a.o), a.lse, a.N, n_qblk, a.G, a.qk_scale, a.neg ? -1.f : 1.f);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int BH;          // batch * heads
+  int BH;          // batch * query heads
+  int G;           // query heads per K/V head (1: one K/V head per query head); K/V head = bh / G
   int N;
   int d;           // 64 or 128
   int dtype;       // 0 f32, 1 f16, 2 bf16
@@ -34,7 +35,8 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  int BH;
+  int BH;          // batch * query heads (dK, dV: batch * K/V heads = BH / G)
+  int G;           // query heads per K/V head
   int N;
   int d;
   int dtype;

@@ -74,6 +74,14 @@ FA_HD int item_blocks(int p, int n_blk, bool causal, int* lo, int* hi) {
   return *hi < 0 ? 1 : 2;
 }
 
+// Grouped heads (GQA; MQA when one K/V head serves all): the H query heads
+// of a batch share H / G K/V heads, G consecutive query heads per K/V head.
+// With flat indices bh = b H + h (query) and b (H / G) + h / G (K/V), and
+// G dividing H, the K/V head of bh is simply bh / G, and the query heads of
+// flat K/V head bkv are bkv G .. bkv G + G - 1.
+FA_HD int kv_head_of(int bh, int G) { return bh / G; }
+FA_HD int q_head_of(int bkv, int G, int j) { return bkv * G + j; }
+
 // Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
 struct FwdTile {
   int bm, bn, waves;

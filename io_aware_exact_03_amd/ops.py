@@ -73,6 +73,54 @@ def bwd_stage(stage: int, q, k, v, o, dout, lse, scale: float, causal: bool, del
     _lib.check(st, f"fa_bwd_stage({stage})")
 
 
+def _check_gqa(q, k, v, *qlike):
+    """q (and o, dout) [B,H,N,d]; k, v [B,Hkv,N,d] with Hkv dividing H."""
+    _check_qkv(q, *qlike)
+    _check_qkv(k, v)
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k, v must share q's dtype and device")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2:] != q.shape[2:] or H % k.shape[1] != 0:
+        raise ValueError(f"k, v shape {tuple(k.shape)} does not group q shape {tuple(q.shape)}")
+    return B, H, k.shape[1], N, d
+
+
+def fwd_gqa(q, k, v, scale: float, causal: bool, out=None, lse=None):
+    """Grouped-query forward: q [B,H,N,d], k and v [B,Hkv,N,d]; query head h
+    reads K/V head h // (H // Hkv).  Returns (O [B,H,N,d], LSE [B,H,N])."""
+    B, H, Hkv, N, d = _check_gqa(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                Hkv, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_fwd_gqa")
+    return out, lse
+
+
+def bwd_gqa(q, k, v, o, dout, lse, scale: float, causal: bool, delta=None, dq=None, dk=None, dv=None):
+    """Backward of fwd_gqa: returns (dQ [B,H,N,d], dK and dV [B,Hkv,N,d],
+    all float32, each dK/dV summed over its group, Delta [B,H,N])."""
+    B, H, Hkv, N, d = _check_gqa(q, k, v, o, dout)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, H, N), **f32) if delta is None else delta
+    dq = torch.empty((B, H, N, d), **f32) if dq is None else dq
+    dk = torch.empty((B, Hkv, N, d), **f32) if dk is None else dk
+    dv = torch.empty((B, Hkv, N, d), **f32) if dv is None else dv
+    st = _lib.load().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H,
+                                Hkv, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_bwd_gqa")
+    return dq, dk, dv, delta
+
+
+def kv_head(bh: int, H: int, Hkv: int) -> int:
+    """The flat K/V head the flat query head bh reads (host copy of the
+    kernels' map); -1 for invalid arguments."""
+    return int(_lib.load().fa_kv_head(bh, H, Hkv))
+
+
 def naive_workspace_bytes(B: int, H: int, N: int, dtype: torch.dtype) -> int:
     return int(_lib.load().fa_naive_workspace_bytes(B, H, N, DTYPE_CODES[dtype]))
 

@@ -10,7 +10,8 @@ Pages cited in this package (by title and section; the text is theirs, the code
 is ours):
 
 * [essay]  "Flash Attention: IO-awareness principle" (hrletsgo.me documents),
-  sections "Standard Attention's real bottleneck", "Tiling", "Recomputation".
+  sections "Standard Attention's real bottleneck", "Tiling", "Recomputation",
+  and the section on serving (grouped-query attention, oracle/gqa.py).
 * [lesson] "Flash Attention -- five lessons converging into 80 lines",
   CUDA training lesson 06 (brianyu43.github.io), sections "Results",
   "Lesson 1".
@@ -37,3 +38,4 @@ from .attention import (  # noqa: F401
     causal_stage_ranges,
     loss,
 )
+from .gqa import attn_bwd_gqa, attn_fwd_gqa, attn_fwd_rows_gqa  # noqa: F401

@@ -244,3 +244,101 @@ def pin_bruteforce_bwd(bwd, brute):
 
 FWD_PINS = (pin_rows_are_distributions, pin_constant_v, pin_zero_q, pin_single_key,
             pin_shift_invariance, pin_key_permutation, pin_huge_logits, pin_torch_sdpa)
+
+
+# ----------------------------------------------------------------------------
+# grouped-query attention pins ([essay], section on serving: GQA / MQA).  The
+# head map (query head h reads K/V head h // (H // Hkv)) is the reading the
+# oracle states; torch's enable_gqa uses the same one and is independent code.
+# ----------------------------------------------------------------------------
+
+GQA_SHAPES = ((2, 8, 2), (1, 4, 1), (1, 3, 3), (2, 6, 3))  # (B, H, Hkv): G = 4, MQA, G = 1, G = 2
+
+
+def _gqa_inputs(B, H, Hkv, n, d, seed):
+    q, dout = rand((B, H, n, d), seed), rand((B, H, n, d), seed + 1)
+    k, v = rand((B, Hkv, n, d), seed + 2), rand((B, Hkv, n, d), seed + 3)
+    return q, k, v, dout
+
+
+def pin_gqa_torch_sdpa(fwd_gqa):
+    """O equals torch float64 SDPA with enable_gqa; LSE equals scipy's
+    logsumexp of the explicitly masked logits of K/V head h // G."""
+    for causal in (False, True):
+        for B, H, Hkv in GQA_SHAPES:
+            q, k, v, _ = _gqa_inputs(B, H, Hkv, 23, 5, 300 + H)
+            o, lse = fwd_gqa(q, k, v, 0.6, causal)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.6,
+                enable_gqa=True).numpy()
+            _close(o, ref, 1e-12, f"gqa sdpa O {B, H, Hkv}")
+            G = H // Hkv
+            for b in range(B):
+                for h in range(H):
+                    s = 0.6 * (q[b, h] @ k[b, h // G].T)
+                    if causal:
+                        s[np.triu_indices(23, 1)] = -np.inf
+                    _close(lse[b, h], logsumexp(s, axis=1), 1e-12, "gqa LSE")
+
+
+def pin_gqa_bruteforce(fwd_gqa, brute):
+    """Brute-force MHA (explicit sums) on K/V heads repeated G times in head
+    order 0,0,..,1,1,.. gives the same O and LSE."""
+    for causal in (False, True):
+        q, k, v, _ = _gqa_inputs(1, 6, 2, 7, 3, 320)
+        o, lse = fwd_gqa(q, k, v, 0.8, causal)
+        ob, lb = brute(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.8, causal)
+        _close(o, ob, 1e-12, "gqa brute O")
+        _close(lse, lb, 1e-12, "gqa brute LSE")
+
+
+def pin_gqa_autograd(bwd_gqa):
+    """dQ, dK, dV equal torch float64 autograd through SDPA with enable_gqa
+    (which sums the shared K/V heads' gradients itself)."""
+    for causal in (False, True):
+        for B, H, Hkv in GQA_SHAPES:
+            q, k, v, g = _gqa_inputs(B, H, Hkv, 19, 4, 340 + H)
+            tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+            out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.45,
+                                                                   enable_gqa=True)
+            out.backward(torch.from_numpy(g))
+            dq, dk, dv, _ = bwd_gqa(q, k, v, g, 0.45, causal)
+            _close(dq, tq.grad.numpy(), 1e-11, f"gqa autograd dQ {B, H, Hkv}")
+            _close(dk, tk.grad.numpy(), 1e-11, f"gqa autograd dK {B, H, Hkv}")
+            _close(dv, tv.grad.numpy(), 1e-11, f"gqa autograd dV {B, H, Hkv}")
+
+
+def pin_gqa_finite_differences(fwd_gqa, bwd_gqa):
+    """Central differences of L = sum(dO * O) with respect to the shared K
+    and V (h = 1e-6) match the analytic dK, dV: a K/V head's gradient is the
+    sum over the query heads that read it."""
+    for causal in (False, True):
+        q, k, v, g = _gqa_inputs(1, 4, 2, 5, 3, 360)
+        _, dk, dv, _ = bwd_gqa(q, k, v, g, 0.9, causal)
+        h = 1e-6
+        for name, x, dx in (("K", k, dk), ("V", v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = float(np.sum(g * fwd_gqa(q, k, v, 0.9, causal)[0]))
+                x[idx] = old - h
+                lm = float(np.sum(g * fwd_gqa(q, k, v, 0.9, causal)[0]))
+                x[idx] = old
+                fd[idx] = (lp - lm) / (2 * h)
+            scale = max(1.0, float(np.max(np.abs(dx))))
+            _close(fd / scale, dx / scale, 1e-6, f"gqa finite differences d{name}")
+
+
+def pin_gqa_identical_heads(bwd_gqa):
+    """Closed form: when every query head of a group carries the same Q and dO,
+    the group's dK and dV are G times one head's, and all its dQ are equal."""
+    for causal in (False, True):
+        q1, k, v, g1 = _gqa_inputs(1, 1, 1, 11, 4, 380)
+        G = 4
+        q, g = np.repeat(q1, G, axis=1), np.repeat(g1, G, axis=1)
+        dq, dk, dv, _ = bwd_gqa(q, k, v, g, 0.7, causal)
+        dq1, dk1, dv1, _ = bwd_gqa(q1, k, v, g1, 0.7, causal)
+        _close(dk, G * dk1, 1e-12, "identical heads dK")
+        _close(dv, G * dv1, 1e-12, "identical heads dV")
+        _close(dq, np.repeat(dq1, G, axis=1), 1e-12, "identical heads dQ")

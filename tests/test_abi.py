@@ -83,6 +83,45 @@ def test_bwd_rejects(lib):
     assert call(args, N=-3) == FA_ERR_ARG
 
 
+def test_gqa_rejects(lib):
+    def f(H=8, Hkv=2, q=A, k=A, **kw):
+        p = dict(B=1, N=8, d=64, scale=1.0, causal=0, dtype=2)
+        p.update(kw)
+        return lib.fa_fwd_gqa(q, k, A, A, A, p["B"], H, Hkv, p["N"], p["d"], p["scale"], p["causal"],
+                              p["dtype"], None)
+
+    def b(H=8, Hkv=2, ptrs=None, **kw):
+        p = dict(B=1, N=8, d=64, scale=1.0, causal=0, dtype=2)
+        p.update(kw)
+        return lib.fa_bwd_gqa(*(ptrs or [A] * 10), p["B"], H, Hkv, p["N"], p["d"], p["scale"], p["causal"],
+                              p["dtype"], None)
+    for fn in (f, b):
+        for H, Hkv in ((8, 0), (8, -1), (8, 3), (4, 8), (6, 4)):
+            assert fn(H=H, Hkv=Hkv) == FA_ERR_ARG, (fn.__name__, H, Hkv)
+        assert fn(d=96) == FA_ERR_UNSUPPORTED
+        assert fn(N=0) == FA_ERR_ARG
+    assert f(q=None) == FA_ERR_ARG and f(k=A + 8) == FA_ERR_ALIGN
+    for i in range(10):
+        ptrs = [A] * 10
+        ptrs[i] = None
+        assert b(ptrs=ptrs) == FA_ERR_ARG
+        ptrs[i] = A + 4
+        assert b(ptrs=ptrs) == FA_ERR_ALIGN
+
+
+def test_kv_head_map():
+    """Query head h of batch b reads K/V head h // (H // Hkv) of batch b; the
+    kernels' flat form is bh // G."""
+    import io_aware_exact_03_amd as fa
+    for B, H, Hkv in ((1, 1, 1), (2, 8, 2), (3, 4, 1), (2, 6, 6), (2, 12, 3)):
+        G = H // Hkv
+        for bb in range(B):
+            for h in range(H):
+                assert fa.kv_head(bb * H + h, H, Hkv) == bb * Hkv + h // G
+    for bh, H, Hkv in ((0, 8, 3), (0, 4, 8), (-1, 4, 2), (0, 4, 0)):
+        assert fa.kv_head(bh, H, Hkv) == -1
+
+
 def test_naive_rejects(lib):
     args = [A] * 7
 

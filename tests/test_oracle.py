@@ -163,3 +163,33 @@ def test_nonfinite_guard_in_fa1():
     q, k, v = (P.rand((1, 1, 9, 2), 500 + s) for s in range(3))
     o, lse = oracle.online_fa1(q, k, v, 1.0, True, 9, 2)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# Grouped-query attention ([essay], section on serving: GQA / MQA).
+
+def test_gqa_forward_pins():
+    P.pin_gqa_torch_sdpa(oracle.attn_fwd_gqa)
+    P.pin_gqa_bruteforce(oracle.attn_fwd_gqa, oracle.attn_fwd_bruteforce)
+
+
+def test_gqa_backward_pins():
+    P.pin_gqa_autograd(oracle.attn_bwd_gqa)
+    P.pin_gqa_finite_differences(oracle.attn_fwd_gqa, oracle.attn_bwd_gqa)
+    P.pin_gqa_identical_heads(oracle.attn_bwd_gqa)
+
+
+def test_gqa_rows_helper():
+    q, k, v, _ = P._gqa_inputs(2, 6, 2, 17, 4, 390)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_gqa(q, k, v, 0.5, causal)
+        rows = [(0, 0, 0), (1, 5, 16), (0, 3, 8), (1, 2, 11)]
+        ro, rl = oracle.attn_fwd_rows_gqa(q, k, v, 0.5, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            np.testing.assert_allclose(ro[n], o[b, h, i], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(rl[n], lse[b, h, i], rtol=0, atol=1e-13)
+
+
+def test_gqa_rejects_bad_grouping():
+    q, k, v, _ = P._gqa_inputs(1, 6, 4, 5, 3, 395)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_gqa(q, k, v, 0.5, False)

@@ -115,3 +115,64 @@ def test_fd_alone_catches_every_backward_mutant():
         bwd = lambda q, k, v, g, s, c, mut=mut: _bwd_variant(q, k, v, g, s, c, mut)  # noqa: E731
         with pytest.raises(AssertionError):
             P.pin_finite_differences(oracle.attn_fwd, bwd)
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention: plausible mistakes in the head map or the group sum
+# ---------------------------------------------------------------------------
+
+def _gqa_variant(mut):
+    """(fwd, bwd) of grouped-query attention built on the MHA oracle, with one
+    planted mistake."""
+    def kv_of(h, H, Hkv):
+        return h % Hkv if mut == "head_map_modulo" else h // (H // Hkv)
+
+    def fwd(q, k, v, s, c):
+        B, H, N, _ = q.shape
+        o, lse = np.empty_like(q), np.empty((B, H, N))
+        for h in range(H):
+            g = kv_of(h, H, k.shape[1])
+            oh, lh = oracle.attn_fwd(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], s, c)
+            o[:, h], lse[:, h] = oh[:, 0], lh[:, 0]
+        return o, lse
+
+    def bwd(q, k, v, go, s, c):
+        B, H, N, _ = q.shape
+        dq, dk, dv, de = np.empty_like(q), np.zeros_like(k), np.zeros_like(v), np.empty((B, H, N))
+        for h in range(H):
+            g = kv_of(h, H, k.shape[1])
+            a, b, cc, e = oracle.attn_bwd(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], go[:, h:h + 1], s, c)
+            dq[:, h], de[:, h] = a[:, 0], e[:, 0]
+            if mut == "group_last_head_only":
+                dk[:, g], dv[:, g] = b[:, 0], cc[:, 0]
+            elif mut == "group_mean":
+                G = H // k.shape[1]
+                dk[:, g] += b[:, 0] / G
+                dv[:, g] += cc[:, 0] / G
+            else:
+                dk[:, g] += b[:, 0]
+                dv[:, g] += cc[:, 0]
+        return dq, dk, dv, de
+    return fwd, bwd
+
+
+GQA_MUTANTS = ["head_map_modulo", "group_last_head_only", "group_mean"]
+
+
+def test_gqa_unmutated_variant_passes():
+    fwd, bwd = _gqa_variant(None)
+    P.pin_gqa_torch_sdpa(fwd)
+    P.pin_gqa_bruteforce(fwd, oracle.attn_fwd_bruteforce)
+    P.pin_gqa_autograd(bwd)
+    P.pin_gqa_identical_heads(bwd)
+
+
+@pytest.mark.parametrize("mut", GQA_MUTANTS)
+def test_gqa_mutant_is_caught(mut):
+    fwd, bwd = _gqa_variant(mut)
+    pins = [("sdpa", lambda: P.pin_gqa_torch_sdpa(fwd)),
+            ("brute", lambda: P.pin_gqa_bruteforce(fwd, oracle.attn_fwd_bruteforce)),
+            ("autograd", lambda: P.pin_gqa_autograd(bwd)),
+            ("fd", lambda: P.pin_gqa_finite_differences(fwd, bwd)),
+            ("identical", lambda: P.pin_gqa_identical_heads(bwd))]
+    assert _fails_some(pins), f"mutant {mut} passed every GQA pin"
