@@ -11,10 +11,11 @@ is ours):
 
 * [essay]  "Flash Attention: IO-awareness principle" (hrletsgo.me documents),
   sections "Standard Attention's real bottleneck", "Tiling", "Recomputation",
-  and the section on serving (grouped-query attention, oracle/gqa.py).
+  and the section on serving (grouped-query attention, oracle/gqa.py;
+  decoding, oracle/decode.py).
 * [lesson] "Flash Attention -- five lessons converging into 80 lines",
   CUDA training lesson 06 (brianyu43.github.io), sections "Results",
-  "Lesson 1".
+  "Lesson 1", "LLM-serving translation" (decode: one query per head).
 * [triton] "Triton 06: Flash Attention v2" (wonbeomjang.kr), sections
   "Improvement 1: un-scaled accumulation", "Improvement 2: exp -> exp2",
   "Improvement 3: causal mask 2-stage", "Backward", "Forward/Backward flow".
@@ -39,3 +40,4 @@ from .attention import (  # noqa: F401
     loss,
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa, attn_fwd_rows_gqa  # noqa: F401
+from .decode import attn_decode, decode_partials, decode_split_merge, merge_partials, split_bounds  # noqa: F401

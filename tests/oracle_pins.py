@@ -342,3 +342,98 @@ def pin_gqa_identical_heads(bwd_gqa):
         _close(dk, G * dk1, 1e-12, "identical heads dK")
         _close(dv, G * dv1, 1e-12, "identical heads dV")
         _close(dq, np.repeat(dq1, G, axis=1), 1e-12, "identical heads dQ")
+
+
+# ----------------------------------------------------------------------------
+# decode pins ([lesson] "LLM-serving translation": decoding has one query per
+# head; [review]'s softmax decomposition merges the split partials)
+# ----------------------------------------------------------------------------
+
+def _decode_inputs(B, H, Hkv, nkv, d, seed, sigma=1.0):
+    q = rand((B, H, d), seed, sigma)
+    k, v = rand((B, Hkv, nkv, d), seed + 1, sigma), rand((B, Hkv, nkv, d), seed + 2)
+    return q, k, v
+
+
+def pin_decode_is_last_causal_row(decode, fwd_gqa):
+    """Decoding the newest token equals the last row of causal grouped-query
+    attention over a sequence whose last query is that token."""
+    q, k, v = _decode_inputs(3, 6, 2, 19, 4, 400)
+    lens = [19, 7, 1]
+    o, lse = decode(q, k, v, 0.7, lens)
+    for b, n in enumerate(lens):
+        qs = rand((1, 6, n, 4), 410 + b)
+        qs[0, :, n - 1] = q[b]
+        of, lf = fwd_gqa(qs, k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.7, True)
+        _close(o[b], of[0, :, n - 1], 1e-12, "decode vs last causal row O")
+        _close(lse[b], lf[0, :, n - 1], 1e-12, "decode vs last causal row LSE")
+
+
+def pin_decode_torch_sdpa(decode):
+    """Independent library: torch float64 SDPA with enable_gqa on one query
+    over each batch's valid keys; LSE from scipy's logsumexp."""
+    for (B, H, Hkv) in ((2, 8, 2), (1, 4, 1), (2, 3, 3)):
+        q, k, v = _decode_inputs(B, H, Hkv, 41, 8, 420 + H)
+        lens = [41, 13][:B]
+        o, lse = decode(q, k, v, 0.35, lens)
+        G = H // Hkv
+        for b, n in enumerate(lens):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b][:, None].copy()), torch.from_numpy(k[b, :, :n].copy()),
+                torch.from_numpy(v[b, :, :n].copy()), scale=0.35, enable_gqa=True).numpy()[:, 0]
+            _close(o[b], ref, 1e-12, f"decode sdpa O {B, H, Hkv}")
+            for h in range(H):
+                _close(lse[b, h], logsumexp(0.35 * (k[b, h // G, :n] @ q[b, h])), 1e-12, "decode LSE")
+
+
+def pin_decode_closed_forms(decode):
+    """One valid key: O = v_0 and LSE = scale q.k_0.  No valid key: O = 0 and
+    LSE = -inf (the empty sum).  Logits near 1000 stay finite."""
+    q, k, v = _decode_inputs(2, 4, 2, 5, 3, 430)
+    o, lse = decode(q, k, v, 0.9, [1, 0])
+    for h in range(4):
+        _close(o[0, h], v[0, h // 2, 0], 1e-15, "decode single key O")
+        _close(lse[0, h], 0.9 * float(q[0, h] @ k[0, h // 2, 0]), 1e-13, "decode single key LSE")
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1])), "decode with no key"
+    q, k, v = _decode_inputs(1, 2, 1, 9, 4, 440, sigma=20.0)
+    o, lse = decode(q, k, v, 1.0, None)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "decode huge logits"
+    for h in range(2):
+        _close(lse[0, h], logsumexp(k[0, 0] @ q[0, h]), 1e-9, "decode huge logits LSE")
+
+
+def pin_split_merge(split_merge, decode):
+    """The split algorithm reproduces the definition for any split count and
+    chunk that cover the cache: splits past the valid keys, splits of one
+    key, one split, ragged lengths, empty batches and huge logits."""
+    for sigma, scale in ((1.0, 0.5), (15.0, 1.0)):
+        q, k, v = _decode_inputs(3, 4, 2, 37, 5, 450, sigma)
+        lens = [37, 10, 0]
+        ref_o, ref_l = decode(q, k, v, scale, lens)
+        for n_splits, chunk in ((1, 37), (2, 19), (3, 16), (5, 8), (37, 1), (40, 1), (4, 128)):
+            o, lse = split_merge(q, k, v, scale, n_splits, chunk, lens)
+            _close(o, ref_o, 1e-12 * max(1.0, sigma), f"split/merge O S={n_splits} C={chunk}")
+            assert np.array_equal(np.isneginf(lse), np.isneginf(ref_l)), "split/merge empty rows"
+            fin = np.isfinite(ref_l)
+            _close(lse[fin], ref_l[fin], 1e-11 * max(1.0, sigma ** 2), f"split/merge LSE S={n_splits}")
+
+
+def pin_partials_torch(partials):
+    """Each split's partial is attention over that split's keys alone
+    (torch float64 SDPA), with its own LSE (scipy); empty splits are
+    (0, -inf)."""
+    q, k, v = _decode_inputs(2, 4, 4, 30, 6, 460)
+    lens = [30, 9]
+    o_s, lse_s = partials(q, k, v, 0.6, 4, 8, lens)
+    for b, n in enumerate(lens):
+        for s in range(4):
+            k0, k1 = min(8 * s, n), min(8 * s + 8, n)
+            if k1 <= k0:
+                assert np.all(o_s[b, :, s] == 0) and np.all(np.isneginf(lse_s[b, :, s])), "empty split"
+                continue
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b][:, None].copy()), torch.from_numpy(k[b, :, k0:k1].copy()),
+                torch.from_numpy(v[b, :, k0:k1].copy()), scale=0.6).numpy()[:, 0]
+            _close(o_s[b, :, s], ref, 1e-12, "partial O")
+            for h in range(4):
+                _close(lse_s[b, h, s], logsumexp(0.6 * (k[b, h, k0:k1] @ q[b, h])), 1e-12, "partial LSE")

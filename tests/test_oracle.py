@@ -193,3 +193,28 @@ def test_gqa_rejects_bad_grouping():
     q, k, v, _ = P._gqa_inputs(1, 6, 4, 5, 3, 395)
     with pytest.raises(ValueError):
         oracle.attn_fwd_gqa(q, k, v, 0.5, False)
+
+
+# Decode ([lesson] "LLM-serving translation"; split merge: [review]'s softmax
+# decomposition).
+
+def test_decode_pins():
+    P.pin_decode_is_last_causal_row(oracle.attn_decode, oracle.attn_fwd_gqa)
+    P.pin_decode_torch_sdpa(oracle.attn_decode)
+    P.pin_decode_closed_forms(oracle.attn_decode)
+
+
+def test_decode_split_pins():
+    P.pin_split_merge(oracle.decode_split_merge, oracle.attn_decode)
+    P.pin_partials_torch(oracle.decode_partials)
+
+
+def test_decode_rejects():
+    q, k, v = P._decode_inputs(1, 4, 3, 5, 3, 470)
+    with pytest.raises(ValueError):
+        oracle.attn_decode(q, k, v, 0.5)
+    q, k, v = P._decode_inputs(1, 4, 2, 5, 3, 470)
+    with pytest.raises(ValueError):
+        oracle.attn_decode(q, k, v, 0.5, [6])
+    with pytest.raises(ValueError):
+        oracle.decode_partials(q, k, v, 0.5, 2, 2)

@@ -176,3 +176,74 @@ def test_gqa_mutant_is_caught(mut):
             ("fd", lambda: P.pin_gqa_finite_differences(fwd, bwd)),
             ("identical", lambda: P.pin_gqa_identical_heads(bwd))]
     assert _fails_some(pins), f"mutant {mut} passed every GQA pin"
+
+
+# ---------------------------------------------------------------------------
+# decode and the split merge
+# ---------------------------------------------------------------------------
+
+def _decode_variant(mut):
+    from oracle import decode as D
+
+    def decode(q, k, v, scale, kv_lens=None):
+        lens = None if mut == "lens_ignored" else kv_lens
+        if mut == "head_map_modulo":
+            B, H, d = q.shape
+            Hkv = k.shape[1]
+            o, lse = np.zeros((B, H, d)), np.full((B, H), -np.inf)
+            for h in range(H):
+                oh, lh = D.attn_decode(q[:, h:h + 1], k[:, h % Hkv:h % Hkv + 1], v[:, h % Hkv:h % Hkv + 1],
+                                       scale, lens)
+                o[:, h], lse[:, h] = oh[:, 0], lh[:, 0]
+            return o, lse
+        return D.attn_decode(q, k, v, scale, lens)
+
+    def merge(o_s, lse_s):
+        B, H, S, d = o_s.shape
+        o, lse = np.zeros((B, H, d)), np.full((B, H), -np.inf)
+        for b in range(B):
+            for h in range(H):
+                live = np.isfinite(lse_s[b, h])
+                if not live.any():
+                    continue
+                if mut == "merge_unweighted":
+                    o[b, h] = o_s[b, h, live].mean(axis=0)
+                    lse[b, h] = np.log(np.exp(lse_s[b, h, live]).sum())
+                elif mut == "merge_no_max":
+                    w = np.exp(lse_s[b, h])
+                    o[b, h] = (w @ o_s[b, h]) / w.sum()
+                    lse[b, h] = np.log(w.sum())
+                elif mut == "merge_lse_is_max":
+                    m = lse_s[b, h].max()
+                    w = np.exp(lse_s[b, h] - m)
+                    o[b, h] = (w @ o_s[b, h]) / w.sum()
+                    lse[b, h] = m
+                else:
+                    return D.merge_partials(o_s, lse_s)
+        return o, lse
+
+    def split_merge(q, k, v, scale, n_splits, chunk, kv_lens=None):
+        return merge(*D.decode_partials(q, k, v, scale, n_splits, chunk, kv_lens))
+    return decode, split_merge
+
+
+DECODE_MUTANTS = ["lens_ignored", "head_map_modulo", "merge_unweighted", "merge_no_max", "merge_lse_is_max"]
+
+
+def test_decode_unmutated_variant_passes():
+    decode, split_merge = _decode_variant(None)
+    P.pin_decode_is_last_causal_row(decode, oracle.attn_fwd_gqa)
+    P.pin_decode_torch_sdpa(decode)
+    P.pin_decode_closed_forms(decode)
+    P.pin_split_merge(split_merge, oracle.attn_decode)
+
+
+@pytest.mark.parametrize("mut", DECODE_MUTANTS)
+def test_decode_mutant_is_caught(mut):
+    decode, split_merge = _decode_variant(mut)
+    pins = [("last_row", lambda: P.pin_decode_is_last_causal_row(decode, oracle.attn_fwd_gqa)),
+            ("sdpa", lambda: P.pin_decode_torch_sdpa(decode)),
+            ("closed", lambda: P.pin_decode_closed_forms(decode)),
+            ("split", lambda: P.pin_split_merge(split_merge, oracle.attn_decode))]
+    with np.errstate(over="ignore", invalid="ignore"):
+        assert _fails_some(pins), f"mutant {mut} passed every decode pin"
