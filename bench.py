@@ -447,6 +447,28 @@ def run_legs(torch, fa, fa_synth, dev):
     del q, k, v, do, o, lse, kr, vr
     torch.cuda.empty_cache()
 
+    # decode steps (one query per head against a K/V cache): HBM-bound, so
+    # reported as K/V bytes read per second against the HBM peak
+    for w in (fa_synth.GQA_DECODE, fa_synth.GQA_DECODE_RAGGED):
+        q, k, v, lens = (t.to(dev) for t in fa_synth.make_decode_inputs(
+            w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, ragged="ragged" in w.name))
+        parts = fa.decode_plan(w.B, w.H, w.kv_heads, w.N, w.d)
+        ws = torch.empty(max(1, fa.decode_workspace_bytes(w.B, w.H, w.kv_heads, w.d, parts)), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        ms, ms_min = time_reps(lambda: fa.decode(q, k, v, w.scale, kv_lens=lens, n_parts=parts, out=o, lse=lse,
+                                                 ws=ws), 30, torch)
+        kv_bytes = float(lens.sum().item()) * w.kv_heads * w.d * 2 * 2
+        alg = kv_bytes + 2 * w.B * w.H * w.d * 2 + 4 * w.B * w.H  # + q read, o written, lse written
+        gbs = alg / (ms * 1e-3) / 1e9
+        entry = {"decode_us": ms * 1e3, "decode_us_min": ms_min * 1e3, "parts": parts, "alg_bytes": alg,
+                 "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+        legs[w.name] = entry
+        log(f"[bench] {w.name}: {entry}")
+        del q, k, v, lens, ws, o, lse
+        torch.cuda.empty_cache()
+
     # non-causal fp16 sweep, fused vs naive, with the byte models
     for w in fa_synth.NONCAUSAL_SWEEP:
         q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))

@@ -72,6 +72,14 @@ ALL_WORKLOADS = (SINGLE_HEAD_F32,) + NONCAUSAL_SWEEP + (CAUSAL_PREFILL, LONG_CAU
 # Grouped-query causal prefill: 64 query heads sharing 8 K/V heads (the
 # head counts of the 70B-class model the serving discussion names), forward
 # and backward.
+# Decode steps of the same model: one new token per sequence against a K/V
+# cache.  Batch 1 with a 32K cache (the batch-1 decoding case the serving
+# discussion names), and 16 sequences of ragged length up to 8K.
+GQA_DECODE = Workload("gqa_decode_B1_H64_Hkv8_N32768_d128_bf16", 1, 64, 32768, 128, "bf16", False,
+                      1 / math.sqrt(128), 1007, passes=("decode",), Hkv=8)
+GQA_DECODE_RAGGED = Workload("gqa_decode_ragged_B16_H64_Hkv8_N8192_d128_bf16", 16, 64, 8192, 128, "bf16", False,
+                             1 / math.sqrt(128), 1008, passes=("decode",), Hkv=8)
+
 GQA_PREFILL = Workload("gqa_causal_prefill_B1_H64_Hkv8_N8192_d128_bf16", 1, 64, 8192, 128, "bf16", True,
                        1 / math.sqrt(128), 1006, passes=("fwd", "bwd"), Hkv=8)
 
@@ -99,6 +107,21 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, sigma_qk:
     if not with_dout:
         return q, k, v
     return q, k, v, draw(1.0)
+
+
+def make_decode_inputs(B: int, H: int, Hkv: int, Nkv: int, d: int, dtype: str, seed: int, ragged: bool = False):
+    """One decode step: q [B,H,d], K/V caches [B,Hkv,Nkv,d] (all N(0, 1),
+    rounded to ``dtype``) and the valid lengths, an int32 CPU tensor [B]:
+    all Nkv, or (ragged) uniform on [1, Nkv].  Draw order: q, K, V, lengths."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn(B, H, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    k = torch.randn(B, Hkv, Nkv, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    v = torch.randn(B, Hkv, Nkv, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    if ragged:
+        lens = torch.randint(1, Nkv + 1, (B,), generator=g, dtype=torch.int32)
+    else:
+        lens = torch.full((B,), Nkv, dtype=torch.int32)
+    return q, k, v, lens
 
 
 def workload_inputs(w: Workload, with_dout: bool | None = None):

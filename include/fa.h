@@ -154,6 +154,62 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
 int fa_kv_head(int bh, int H, int Hkv);
 
 /*
+ * Decoding: the newest token of every sequence attends to its K/V cache
+ * ("Flash Attention -- five lessons converging into 80 lines", "LLM-serving
+ * translation": in decoding Q has one row per head).  With few K/V heads and
+ * small batches one workgroup per head leaves most of the GPU idle ("Flash
+ * Attention: IO-awareness principle", section on serving), so the cached
+ * keys of the whole batch are shared out evenly among n_parts workgroups,
+ * and results cut between workgroups are merged with the log-sum-exp form of
+ * the softmax decomposition ("Paper review: FlashAttention ...", "Tiling").
+ *
+ * For every batch b and query head h, with L = kv_lens[b] (clamped to
+ * [0, Nkv]; all Nkv when kv_lens is NULL) and K/V head g = h / (H / Hkv):
+ *     s_j = scale * q[b,h] . k_cache[b,g,j]   for j < L
+ *     o[b,h] = sum_j softmax(s)_j v_cache[b,g,j],  lse[b,h] = ln sum_j exp(s_j)
+ * L = 0 gives o = 0 and lse = -inf (the empty sum).  Cache rows j >= L are
+ * never read, so they may hold anything.
+ *
+ * q, o: dtype [B,H,d]; k_cache, v_cache: dtype [B,Hkv,Nkv,d] (Nkv is the
+ * cache capacity, the row stride of a head); lse: float32 [B,H]; kv_lens:
+ * NULL or a device int32 [B] (4-byte aligned).  dtype f16 or bf16 (f32 ->
+ * FA_ERR_UNSUPPORTED); d in {64, 128}; Hkv divides H; 1 <= n_parts <= 1024.
+ *
+ * Partition (computed on the device from kv_lens).  A unit is one (batch,
+ * K/V head, block of 32 query heads of that head's group), numbered
+ * u = (b Hkv + g) QB + qb with QB = ceil((H / Hkv) / 32); it owns
+ * ceil(L_b / 128) tiles of 128 keys.  The units' tiles, laid end to end (T
+ * in all), are cut into n_parts ranges of P = ceil(T / n_parts) tiles: part
+ * w (one workgroup) takes tiles [w P, (w + 1) P).  A unit held whole by one
+ * part is written to o and lse directly; a unit cut between parts leaves
+ * each piece's result in workspace slot w + u and a second launch merges
+ * them.  n_parts = 1 needs no workspace (ws may be NULL) and is one launch.
+ * n_parts > 1 needs ws (16-byte aligned, caller-owned) of at least
+ * fa_decode_workspace_bytes(B, H, Hkv, d, n_parts) bytes; afterwards slot s
+ * of a cut unit holds float32 O [32][d] (query columns of the unit, each
+ * normalised within the piece) at float offset s * 32 * d, and float32 LSE
+ * [32] at byte offset ceil256((n_parts + U) * 32 * d * 4) + s * 32 * 4,
+ * U = B Hkv QB; other slots are left as they were.
+ * Errors as fa_fwd; a missing or short workspace, a bad n_parts or a bad
+ * grouping -> FA_ERR_ARG; more than 2^31 tiles -> FA_ERR_UNSUPPORTED.
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+              void* o, float* lse, void* ws, size_t ws_bytes, int B, int H, int Hkv, int Nkv,
+              int d, float scale, int n_parts, int dtype, void* stream);
+
+/* Workspace bytes fa_decode needs for n_parts (0 for n_parts = 1 and for
+ * invalid arguments). */
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int d, int n_parts);
+
+/*
+ * The part count the library suggests for a decode step on the current
+ * device: one per CU, at most the number of tiles at full length (and at
+ * most 1024).  Queries the device's CU count (a HIP call; FA_ERR_HIP if that
+ * fails).
+ */
+int fa_decode_plan(int B, int H, int Hkv, int Nkv, int d, int* n_parts);
+
+/*
  * Naive three-kernel forward ("Flash Attention -- five lessons converging
  * into 80 lines", "Two implementations"; Algorithm 0 of the FlashAttention
  * paper review): kernel 1 writes S = scale * Q K^T for all N x N into

@@ -23,6 +23,9 @@ SIGNATURES = {
     "fa_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_kv_head": (_i, [_i, _i, _i]),
+    "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "fa_decode_plan": (_i, [_i, _i, _i, _i, _i, _ip]),
     "fa_naive_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_naive_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_strerror": (ctypes.c_char_p, [_i]),

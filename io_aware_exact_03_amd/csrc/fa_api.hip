@@ -149,6 +149,70 @@ int fa_kv_head(int bh, int H, int Hkv) {
   return fa::kv_head_of(bh, H / Hkv);
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static long long decode_units(int B, int H, int Hkv) {
+  return (long long)B * Hkv * fa::decode_query_blocks(H / Hkv);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int d, int n_parts) {
+  if (B < 1 || H < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  if (n_parts < 1 || n_parts > fa::kDecodeMaxParts) return 0;
+  if (n_parts == 1) return 0;
+  const size_t slots = (size_t)n_parts + (size_t)decode_units(B, H, Hkv);
+  return align256(slots * 32 * d * 4) + align256(slots * 32 * 4);
+}
+
+int fa_decode_plan(int B, int H, int Hkv, int Nkv, int d, int* n_parts) {
+  if (!n_parts) return FA_ERR_ARG;
+  if (B < 1 || H < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0 || Nkv < 1) return FA_ERR_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  // One part per CU (a part's LDS ring fills a CU), never more parts than
+  // tiles at full length.
+  const long long tiles = decode_units(B, H, Hkv) * fa::decode_tiles(Nkv);
+  long long P = cus < 1 ? 1 : cus;
+  if (P > tiles) P = tiles;
+  if (P > fa::kDecodeMaxParts) P = fa::kDecodeMaxParts;
+  *n_parts = (int)(P < 1 ? 1 : P);
+  return FA_OK;
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens, void* o, float* lse,
+              void* ws, size_t ws_bytes, int B, int H, int Hkv, int Nkv, int d, float scale, int n_parts,
+              int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_ARG;
+  if (Hkv < 1 || H < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
+  if (n_parts < 1 || n_parts > fa::kDecodeMaxParts) return FA_ERR_ARG;
+  const int st = check_shape(B, H, Nkv, d, dtype, 0, scale);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  // tile and slot counts are int in the kernels
+  if (decode_units(B, H, Hkv) * fa::decode_tiles(Nkv) >= (1LL << 31) ||
+      (decode_units(B, H, Hkv) + n_parts) * 32 >= (1LL << 31))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_bytes(B, H, Hkv, d, n_parts);
+  if (n_parts > 1 && (!ws || ws_bytes < need)) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k_cache, v_cache, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (kv_lens && ((uintptr_t)kv_lens & 3u)) return FA_ERR_ALIGN;
+  if (n_parts > 1 && !aligned16(ws)) return FA_ERR_ALIGN;
+  fa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_lens = kv_lens; a.o = o; a.lse = lse;
+  const size_t slots = (size_t)n_parts + (size_t)decode_units(B, H, Hkv);
+  a.opart = n_parts > 1 ? static_cast<float*>(ws) : nullptr;
+  a.lpart = n_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * 32 * d * 4)) : nullptr;
+  a.B = B; a.H = H; a.G = H / Hkv; a.Nkv = Nkv; a.d = d; a.dtype = dtype;
+  a.parts = n_parts;
+  a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_decode(a));
+}
+
 int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* s_ws, void* p_ws, int B,
                  int H, int N, int d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !s_ws || !p_ws) return FA_ERR_ARG;

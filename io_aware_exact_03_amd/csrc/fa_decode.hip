@@ -1,0 +1,487 @@
+// fa_decode.hip -- decoding: the newest query of every head against its
+// K/V cache, the keys split across workgroups, the partial results merged.
+//
+// Pages cited: "Flash Attention -- five lessons converging into 80 lines"
+// (brianyu43.github.io), "LLM-serving translation" (in decoding Q has one
+// row per head); "Flash Attention: IO-awareness principle" (hrletsgo.me),
+// section on serving (with few K/V heads and batch 1 a decode step has too
+// few tiles to fill the GPU, hence kernels that split the keys); "Paper
+// review: FlashAttention ... with IO-Awareness" (osehyeon.github.io), the
+// softmax decomposition under "Tiling" (max and normaliser of a
+// concatenation from those of its parts), which merges the splits.
+//
+// Decoding reads every cached key and value once and does 4 d flops per key
+// per query head, so it is bound by HBM bandwidth, not by the matrix cores.
+// The design keeps the K/V stream as wide and deep as LDS allows and spends
+// matrix-core work freely: the G query heads that share a K/V head are the
+// 32 columns of one MFMA product (padded with zeros), so each K/V element
+// is read from HBM once for the whole group.
+//
+// Split kernel, one workgroup per (batch, K/V head, 32 query heads, split):
+//   * K and V tiles of BN = 32 NW keys go from HBM straight into LDS
+//     (buffer_load ... lds, 1 KB per wave instruction, rows swizzled as in
+//     the forward), NBUF - 1 tiles ahead; the buffer range of the head ends
+//     at its valid length, so keys past it read as zeros (never a stale or
+//     non-finite cache entry) and are masked;
+//   * wave w owns rows 32 w .. 32 w + 31 of every tile: S^T = K Q^T on
+//     v_mfma_f32_32x32x16 (lane = query head, registers = keys), an online
+//     softmax in base 2 per wave, O^T += V^T P^T with V^T from transposing
+//     LDS reads;
+//   * at the end the waves' (m, l, O) are combined through LDS and the
+//     split's O (normalised) and LSE are written: to the outputs when there
+//     is one split, else to the caller's workspace.
+// Merge kernel (more than one split), one wave per query head: with
+// M = max_s LSE_s and w_s = exp(LSE_s - M), LSE = M + ln sum w_s and
+// O = sum w_s O_s / sum w_s.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+#include "fa_plan.hpp"
+
+namespace fa {
+namespace {
+
+template <int D, int NW_, int NBUF_>
+struct Dec {
+  static constexpr int NW = NW_, NT = 64 * NW, NBUF = NBUF_;
+  static constexpr int BN = 32 * NW;            // keys per tile, 32 per wave
+  static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  static constexpr int RPP = 64 / CPR;          // tile rows per 1 KB wave load
+  static constexpr int PPT = BN / RPP;          // 1 KB pieces per K (or V) tile
+  static constexpr int LPW = 2 * PPT / NW;      // loads per wave per tile (K and V)
+  static constexpr int EPT = D / (2 * NW);      // output elements per thread in the combine
+  static constexpr int OROW = D + 1;            // padded fp32 row of a wave's O in LDS
+  static_assert(kDecodeTileKeys % BN == 0, "whole tiles per split");
+  static_assert(LPW * NW == 2 * PPT && (NBUF - 2) * LPW < 64, "load split / vmcnt range");
+  static_assert(EPT % 8 == 0, "combine vector width");
+  static_assert(NW * 32 * (OROW + 2) * 4 <= NBUF * 2 * BN * D * 2, "combine fits in the ring");
+};
+
+// Valid length of batch b, clamped to [0, Nkv].
+__device__ __forceinline__ int decode_len(const int* kv_lens, int b, int Nkv) {
+  const int l = kv_lens ? kv_lens[b] : Nkv;
+  return l < 0 ? 0 : (l > Nkv ? Nkv : l);
+}
+
+// Block-wide sums of tiles over all batches (T) and over batches < blim
+// (P), with all NT threads; `red` holds 2 NT ints.  Block-uniform.
+template <int NT>
+__device__ __forceinline__ void decode_block_sums(const int* kv_lens, int B, int Nkv, int UB, int blim, int* red,
+                                                  int* T_out, int* P_out) {
+  const int tid = threadIdx.x;
+  int sT = 0, sP = 0;
+  for (int b = tid; b < B; b += NT) {
+    const int v = decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
+    sT += v;
+    sP += b < blim ? v : 0;
+  }
+  red[tid] = sT;
+  red[NT + tid] = sP;
+  __syncthreads();
+  for (int st = NT / 2; st > 0; st >>= 1) {
+    if (tid < st) {
+      red[tid] += red[tid + st];
+      red[NT + tid] += red[NT + tid + st];
+    }
+    __syncthreads();
+  }
+  *T_out = red[0];
+  *P_out = red[NT];
+  __syncthreads();
+}
+
+// The partition, computed by every workgroup of the split kernel with all
+// its threads: the total tile count T, and the batch b holding tile
+// `target` with the first tile P_b of that batch.  Batches go NT at a time
+// through an inclusive scan in LDS (`red`, NT + 2 ints).  Block-uniform.
+template <int NT>
+__device__ __forceinline__ void decode_block_plan(const int* kv_lens, int B, int Nkv, int UB, int parts_total,
+                                                  int part, int* red, int* T_out, int* per_out, int* b_out,
+                                                  int* Pb_out) {
+  const int tid = threadIdx.x;
+  // pass 1: T
+  int sum = 0;
+  for (int b = tid; b < B; b += NT) sum += decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
+  red[tid] = sum;
+  __syncthreads();
+  for (int st = NT / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  const int T = red[0];
+  const int per = (T + parts_total - 1) / parts_total;
+  const int target = part * per;
+  __syncthreads();
+  *T_out = T;
+  *per_out = per;
+  *b_out = B;
+  *Pb_out = T;
+  if (target >= T) return;
+  // pass 2: the batch holding `target`
+  if (tid == 0) red[NT] = -1;  // published by the first barrier below
+  int base = 0;
+  for (int c0 = 0; c0 < B; c0 += NT) {
+    const int b = c0 + tid;
+    const int v = b < B ? decode_tiles(decode_len(kv_lens, b, Nkv)) * UB : 0;
+    red[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int x = tid >= off ? red[tid - off] : 0;
+      __syncthreads();
+      red[tid] += x;
+      __syncthreads();
+    }
+    const int incl = base + red[tid];
+    const int chunk_total = red[NT - 1];
+    __syncthreads();
+    if (v > 0 && incl - v <= target && target < incl) {
+      red[NT] = b;
+      red[NT + 1] = incl - v;
+    }
+    __syncthreads();
+    if (red[NT] >= 0) {
+      *b_out = red[NT];
+      *Pb_out = red[NT + 1];
+      __syncthreads();
+      return;
+    }
+    base += chunk_total;
+    __syncthreads();
+  }
+}
+
+template <typename T, int D, int NW, int NBUF>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    const int* __restrict__ kv_lens, uint16_t* __restrict__ og, float* __restrict__ lseg,
+    float* __restrict__ opart, float* __restrict__ lpart, int B, int H, int G, int Nkv, float qk_scale) {
+  using C = Dec<D, NW, NBUF>;
+  constexpr int BN = C::BN, DS = C::DS, DB = C::DB;
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NBUF][2][BN * D];  // K, V tiles, swizzled rows
+  __shared__ int plan[C::NT + 2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB;
+
+  // Batches with no valid key: O = 0, LSE = -inf (no part owns them).
+  if (blockIdx.x == 0) {
+    for (int b = 0; b < B; ++b) {
+      if (decode_len(kv_lens, b, Nkv) != 0) continue;
+      for (int i = threadIdx.x; i < H * D; i += C::NT) og[((size_t)b * H) * D + i] = 0;
+      for (int i = threadIdx.x; i < H; i += C::NT) lseg[(size_t)b * H + i] = kNegInf;
+    }
+  }
+
+  // This part's tile range; consecutive parts share an XCD (and its L2),
+  // which the query blocks of one K/V head read in turn.
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  int Ttot, per, b, P_b;
+  decode_block_plan<C::NT>(kv_lens, B, Nkv, UB, (int)gridDim.x, w, plan, &Ttot, &per, &b, &P_b);
+  int t = w * per;
+  const int t_end = min(t + per, Ttot);
+  if (t >= t_end) return;
+
+  // The unit holding tile t: batch b (first tile P_b), unit ui of the batch.
+  int nb = decode_tiles(decode_len(kv_lens, b, Nkv));
+  int ui = (t - P_b) / nb;
+  int P_u = P_b + ui * nb;
+
+  f32x16 oacc[DB];
+  float m_run, l_run;  // base-2 running max; this half's share of l
+
+  // Keys [k0, k1) of unit (b, ui), the whole unit or not.
+  auto segment = [&](int k0, int k1, int len, bool whole, int slot) __attribute__((always_inline)) {
+    const int hkv = ui / QB, qb = ui % QB;
+    const int bkv = b * Hkv + hkv;
+    const int nq = min(32, G - 32 * qb);  // live query columns
+    const int bh0 = bkv * G + 32 * qb;    // flat query head of column 0
+
+    // Q^T fragments (MFMA B operand): lane (n, g) holds query head n,
+    // elements 16 k + 8 g .. + 8; dead columns are zero.
+    uint4 qf[DS];
+#pragma unroll
+    for (int k = 0; k < DS; ++k)
+      qf[k] = n < nq ? *reinterpret_cast<const uint4*>(qg + (size_t)(bh0 + n) * D + 16 * k + 8 * g)
+                     : make_uint4(0u, 0u, 0u, 0u);
+
+    // The buffer range ends at the valid length: later rows read as zeros.
+    const uint32_t valid_bytes = (uint32_t)len * D * 2;
+    const rsrc_t krs = make_rsrc(kg + (size_t)bkv * Nkv * D, valid_bytes);
+    const rsrc_t vrs = make_rsrc(vg + (size_t)bkv * Nkv * D, valid_bytes);
+
+    // Tile j of the segment (keys k0 + BN j ..) into ring slot `sl`: LDS
+    // row r, chunk c holds global chunk c ^ swz_chunk(r) of key k0 + BN j + r.
+    auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+      const int lrow = lane / C::CPR;
+#pragma unroll
+      for (int e = 0; e < C::LPW; ++e) {
+        const int tt = wave * C::LPW + e;
+        const int p = tt % C::PPT;
+        const int row = p * C::RPP + lrow;
+        const int ch = (lane % C::CPR) ^ swz_chunk<D>(row);
+        const uint32_t off = ((uint32_t)(k0 + j * BN + row) * D + 8 * ch) * 2;
+        if (tt < C::PPT) load_lds16(krs, &ring[sl][0][p * C::RPP * D], off);
+        else load_lds16(vrs, &ring[sl][1][p * C::RPP * D], off);
+      }
+    };
+
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+
+    // One wave's 32 keys of the tile in ring slot `sl`.
+    auto sub_block = [&](int sl, int key0) __attribute__((always_inline)) {
+      const uint16_t* kt = ring[sl][0];
+      const uint16_t* vt = ring[sl][1];
+      // two independent product chains (even and odd k), summed
+      f32x16 sc = f32x16{}, sc1 = f32x16{};
+#pragma unroll
+      for (int k = 0; k < DS; k += 2) {
+        sc = mma16(T{}, read_row<D>(kt, 32 * wave + n, 16 * k + 8 * g), qf[k], sc);
+        sc1 = mma16(T{}, read_row<D>(kt, 32 * wave + n, 16 * k + 16 + 8 * g), qf[k + 1], sc1);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] += sc1[r];
+      // register r is key key0 + 8 (r / 4) + 4 g + r % 4
+      float x[16];
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
+        x[r] = key < k1 ? sc[r] * qk_scale : kNegInf;
+        mx = fmaxf(mx, x[r]);
+      }
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float base = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - base);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = fast_exp2(x[r] - base);
+        psum += x[r];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      // P^T as the B operand of O^T += V^T P^T: registers 8 h .. 8 h + 7
+      // are the keys of 16-key step h in the order read_tr delivers V^T's rows.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 pk = make_uint4(pack2(T{}, x[8 * h + 0], x[8 * h + 1]), pack2(T{}, x[8 * h + 2], x[8 * h + 3]),
+                                    pack2(T{}, x[8 * h + 4], x[8 * h + 5]), pack2(T{}, x[8 * h + 6], x[8 * h + 7]));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = mma16(T{}, read_tr<D>(vt, 32 * wave + 16 * h, 32 * db, lane), pk, oacc[db]);
+      }
+    };
+
+    const int n_tiles = (k1 - k0 + BN - 1) / BN;
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (j < n_tiles) issue(j, j);
+    for (int j = 0; j < n_tiles; ++j) {
+      // Tile j is in LDS once this wave's loads of it returned and every
+      // wave passed the barrier; the loads of later tiles may stay in flight.
+      const int ahead = min(NBUF - 2, n_tiles - 1 - j);
+      if (NBUF >= 4 && ahead >= 2) lds_barrier<(NBUF >= 4 ? 2 : 0) * C::LPW>();
+      else if (NBUF >= 3 && ahead >= 1) lds_barrier<(NBUF >= 3 ? 1 : 0) * C::LPW>();
+      else lds_barrier<0>();
+      static_assert(NBUF <= 4, "wait cases");
+      // The slot of tile j - 1 is free: every wave finished reading it
+      // before the barrier.
+      if (j + NBUF - 1 < n_tiles) issue(j + NBUF - 1, (j + NBUF - 1) % NBUF);
+      const int key0 = k0 + j * BN + 32 * wave;
+      if (key0 < k1) sub_block(j % NBUF, key0);
+    }
+
+    // Combine the waves through LDS (the ring is free after this barrier:
+    // the last tile's wait left no load in flight).
+    __syncthreads();
+    float* orow = reinterpret_cast<float*>(&ring[0][0][0]);  // [NW][32][OROW]
+    float* mrow = orow + NW * 32 * C::OROW;                   // [NW][32]
+    float* lrow = mrow + NW * 32;                             // [NW][32]
+    const float l_tot = halves_sum(l_run);
+    if (g == 0) {
+      mrow[wave * 32 + n] = m_run;
+      lrow[wave * 32 + n] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        orow[(wave * 32 + n) * C::OROW + 32 * db + 8 * (r / 4) + 4 * g + (r % 4)] = oacc[db][r];
+    __syncthreads();
+
+    const int col = threadIdx.x % 32, e0 = (threadIdx.x / 32) * C::EPT;
+    if (col < nq) {
+      // Every segment holds a valid key, so some wave's max is finite.
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mrow[ww * 32 + col]);
+      float ew[NW], Lsum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        ew[ww] = fast_exp2(mrow[ww * 32 + col] - M);
+        Lsum += ew[ww] * lrow[ww * 32 + col];
+      }
+      const float inv = 1.f / Lsum;
+      float o[C::EPT];
+#pragma unroll
+      for (int e = 0; e < C::EPT; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* src = orow + (ww * 32 + col) * C::OROW + e0;
+#pragma unroll
+        for (int e = 0; e < C::EPT; ++e) o[e] += ew[ww] * src[e];
+      }
+      const float lse = (M + __log2f(Lsum)) * kLn2;
+      if (whole) {  // the final result of these query heads
+        uint16_t* dst = og + (size_t)(bh0 + col) * D + e0;
+#pragma unroll
+        for (int e = 0; e < C::EPT; e += 8) {
+          uint4 v;
+          v.x = pack2(T{}, o[e + 0] * inv, o[e + 1] * inv);
+          v.y = pack2(T{}, o[e + 2] * inv, o[e + 3] * inv);
+          v.z = pack2(T{}, o[e + 4] * inv, o[e + 5] * inv);
+          v.w = pack2(T{}, o[e + 6] * inv, o[e + 7] * inv);
+          *reinterpret_cast<uint4*>(dst + e) = v;
+        }
+        if (e0 == 0) lseg[bh0 + col] = lse;
+      } else {  // this segment's (O normalised within it, LSE) for the merge
+        float* dst = opart + ((size_t)slot * 32 + col) * D + e0;
+#pragma unroll
+        for (int e = 0; e < C::EPT; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+        if (e0 == 0) lpart[(size_t)slot * 32 + col] = lse;
+      }
+    }
+    __syncthreads();  // the next segment refills the ring
+  };
+
+  // Walk the range unit by unit.
+  for (;;) {
+    const int seg_end = min(t_end, P_u + nb);
+    const int len = decode_len(kv_lens, b, Nkv);
+    segment((t - P_u) * kDecodeTileKeys, min((seg_end - P_u) * kDecodeTileKeys, len), len,
+            t == P_u && seg_end == P_u + nb, w + b * UB + ui);
+    t = seg_end;
+    if (t >= t_end) break;
+    P_u += nb;
+    if (++ui == UB) {  // next batch with keys
+      ui = 0;
+      do nb = decode_tiles(decode_len(kv_lens, ++b, Nkv));
+      while (nb == 0);
+    }
+  }
+}
+
+// Merge of the segments of one (unit, query column) that was cut between
+// parts: threads stride over the segments (32 column chunks x 8 segment
+// groups), then reduce through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ opart,
+                                                           const float* __restrict__ lpart,
+                                                           const int* __restrict__ kv_lens,
+                                                           uint16_t* __restrict__ og, float* __restrict__ lseg,
+                                                           int B, int H, int G, int Nkv, int n_parts) {
+  constexpr int CH = D / 32;  // floats per column chunk
+  __shared__ float red[8][D];
+  __shared__ float rs[256];
+  __shared__ int sums[512];
+  const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB;
+  const int u = blockIdx.x / 32, col = blockIdx.x % 32;
+  const int b = u / UB, ui = u % UB, qb = ui % QB;
+  if (col >= min(32, G - 32 * qb)) return;
+  const int nb = decode_tiles(decode_len(kv_lens, b, Nkv));
+  if (nb == 0) return;
+  int Ttot, P_b;
+  decode_block_sums<256>(kv_lens, B, Nkv, UB, b, sums, &Ttot, &P_b);
+  const int per = (Ttot + n_parts - 1) / n_parts;
+  const int P_u = P_b + ui * nb;
+  const int w_first = P_u / per, w_last = (P_u + nb - 1) / per;
+  if (w_first == w_last) return;  // one part held the whole unit and wrote it
+  const int np = w_last - w_first + 1;
+  const size_t slot0 = (size_t)w_first + u;
+
+  const int tid = threadIdx.x, c = tid % 32, grp = tid / 32;
+  // M = max over the segments' LSEs.
+  float m = kNegInf;
+  for (int i = tid; i < np; i += 256) m = fmaxf(m, lpart[(slot0 + i) * 32 + col]);
+  rs[tid] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) rs[tid] = fmaxf(rs[tid], rs[tid + s]);
+    __syncthreads();
+  }
+  const float M = rs[0];
+  __syncthreads();
+  // Weighted sums: w_i = exp(LSE_i - M).
+  float acc[CH] = {};
+  float wsum = 0.f;
+  for (int i = grp; i < np; i += 8) {
+    const float wi = fast_exp2((lpart[(slot0 + i) * 32 + col] - M) * kLog2e);
+    wsum += wi;
+    const float* src = opart + ((slot0 + i) * 32 + col) * D + CH * c;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] += wi * src[e];
+  }
+#pragma unroll
+  for (int e = 0; e < CH; ++e) red[grp][CH * c + e] = acc[e];
+  if (c == 0) rs[grp] = wsum;
+  __syncthreads();
+  if (grp == 0) {
+    float W = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) W += rs[q];
+    const float inv = 1.f / W;
+    float o[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v += red[q][CH * c + e];
+      o[e] = v * inv;
+    }
+    const int bh = (b * Hkv + ui / QB) * G + 32 * qb + col;
+    uint16_t* dst = og + (size_t)bh * D + CH * c;
+#pragma unroll
+    for (int e = 0; e < CH; e += 2) *reinterpret_cast<uint32_t*>(dst + e) = pack2(T{}, o[e], o[e + 1]);
+    if (c == 0) lseg[bh] = M + __log2f(W) * kLn2;
+  }
+}
+
+template <typename T, int D>
+hipError_t run(const DecodeArgs& a) {
+  constexpr int NW = 4, NBUF = D == 128 ? 2 : 4;
+  using C = Dec<D, NW, NBUF>;
+  const float qk_scale = a.scale * kLog2eHost;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, NW, NBUF>), dim3((unsigned)a.parts), dim3(C::NT), 0, a.stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.kv_lens, static_cast<uint16_t*>(a.o), a.lse, a.opart,
+                     a.lpart, a.B, a.H, a.G, a.Nkv, qk_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.parts == 1) return e;
+  const long long units = (long long)a.B * (a.H / a.G) * decode_query_blocks(a.G);
+  if (units * 32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(units * 32)), dim3(256), 0, a.stream, a.opart,
+                     a.lpart, a.kv_lens, static_cast<uint16_t*>(a.o), a.lse, a.B, a.H, a.G, a.Nkv, a.parts);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.dtype == 2) return a.d == 128 ? run<BF16, 128>(a) : run<BF16, 64>(a);
+  return a.d == 128 ? run<F16, 128>(a) : run<F16, 64>(a);
+}
+
+}  // namespace fa

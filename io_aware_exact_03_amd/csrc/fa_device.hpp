@@ -147,8 +147,10 @@ __device__ __forceinline__ void load_lds4(rsrc_t r, void* dst, uint32_t byte_off
 // after a barrier at which the loading wave waited for that load.
 template <int NCNT>
 __device__ __forceinline__ void lds_barrier() {
-  static_assert(NCNT >= 0 && NCNT < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0070 | NCNT);  // vmcnt(NCNT) lgkmcnt(0)
+  // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 (left at its
+  // maximum), lgkmcnt 11:8 (zero).
+  static_assert(NCNT >= 0 && NCNT < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NCNT & 15) | 0x0070 | ((NCNT >> 4) << 14));  // vmcnt(NCNT) lgkmcnt(0)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");

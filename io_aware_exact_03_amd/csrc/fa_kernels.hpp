@@ -62,9 +62,25 @@ struct NaiveArgs {
   hipStream_t stream;
 };
 
+struct DecodeArgs {
+  const void* q;        // [B, H, d]
+  const void* k;        // [B, Hkv, Nkv, d]
+  const void* v;
+  const int* kv_lens;   // [B] on the device, or null (all Nkv)
+  void* o;              // [B, H, d]
+  float* lse;           // [B, H]
+  float* opart;         // [parts + units][32][d] segment outputs (parts > 1)
+  float* lpart;         // [parts + units][32] segment LSEs (parts > 1)
+  int B, H, G, Nkv, d, dtype;
+  int parts;            // workgroups sharing the key tiles
+  float scale;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0 = all three launches in order; 1 = Delta, 2 = dK/dV, 3 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, int stage);
 hipError_t launch_naive(const NaiveArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
 
 }  // namespace fa

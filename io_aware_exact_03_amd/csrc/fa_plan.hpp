@@ -82,6 +82,19 @@ FA_HD int item_blocks(int p, int n_blk, bool causal, int* lo, int* hi) {
 FA_HD int kv_head_of(int bh, int G) { return bh / G; }
 FA_HD int q_head_of(int bkv, int G, int j) { return bkv * G + j; }
 
+// Decoding (one query per head over a K/V cache).  A unit is one (batch,
+// K/V head, block of 32 query heads of its group), u = (b Hkv + hkv) QB +
+// qb; it owns the ceil(len_b / kDecodeTileKeys) key tiles of its batch's
+// valid length.  The units' tiles are laid end to end (T in all) and cut
+// into n_parts ranges of per = ceil(T / n_parts) tiles, one workgroup each:
+// part w takes tiles [w per, min((w + 1) per, T)).  The piece of unit u a
+// part holds is a segment; a segment that is not the whole unit leaves its
+// result in workspace slot w + u, to be merged.
+constexpr int kDecodeTileKeys = 128;
+constexpr int kDecodeMaxParts = 1024;
+FA_HD int decode_tiles(int len) { return (len + kDecodeTileKeys - 1) / kDecodeTileKeys; }
+FA_HD int decode_query_blocks(int G) { return (G + 31) / 32; }
+
 // Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
 struct FwdTile {
   int bm, bn, waves;

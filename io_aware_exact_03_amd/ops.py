@@ -121,6 +121,69 @@ def kv_head(bh: int, H: int, Hkv: int) -> int:
     return int(_lib.load().fa_kv_head(bh, H, Hkv))
 
 
+def decode_plan(B: int, H: int, Hkv: int, Nkv: int, d: int) -> int:
+    """The part count the library suggests for a decode step on the current
+    device."""
+    n = ctypes.c_int()
+    _lib.check(_lib.load().fa_decode_plan(B, H, Hkv, Nkv, d, ctypes.byref(n)), "fa_decode_plan")
+    return n.value
+
+
+def decode_workspace_bytes(B: int, H: int, Hkv: int, d: int, n_parts: int) -> int:
+    return int(_lib.load().fa_decode_workspace_bytes(B, H, Hkv, d, n_parts))
+
+
+def decode(q, k_cache, v_cache, scale: float, kv_lens=None, n_parts=None, out=None, lse=None, ws=None):
+    """One decode step: q [B,H,d] against the caches [B,Hkv,Nkv,d]; kv_lens
+    an int32 device tensor [B] of valid cache rows (None: all Nkv).  Query
+    head h reads K/V head h // (H // Hkv).  The batch's key tiles are shared
+    among n_parts workgroups (None: the library's plan).  Returns (O [B,H,d]
+    in q.dtype, LSE float32 [B,H]); with more than one part the workspace
+    `ws` (allocated if None) holds the pieces of cut units afterwards."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H,d] and caches [B,Hkv,Nkv,d]")
+    for t in (q, k_cache, v_cache):
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q and the caches must be contiguous, on one HIP device, of one dtype")
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, d = q.shape
+    Hkv, Nkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.device != q.device
+                                or kv_lens.numel() != B or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 tensor of B values on q's device")
+    if n_parts is None:
+        n_parts = decode_plan(B, H, Hkv, Nkv, d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, Hkv, d, n_parts)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               kv_lens.data_ptr() if kv_lens is not None else None, out.data_ptr(),
+                               lse.data_ptr(), ws.data_ptr() if ws is not None else None,
+                               ws.numel() * ws.element_size() if ws is not None else 0, B, H, Hkv, Nkv, d,
+                               float(scale), int(n_parts), DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_decode")
+    return out, lse
+
+
+def decode_pieces(ws, B: int, H: int, Hkv: int, d: int, n_parts: int):
+    """Views of a decode workspace after the call: (O [slots, 32, d], LSE
+    [slots, 32]), both float32, slots = n_parts + units."""
+    units = B * Hkv * ((H // Hkv + 31) // 32)
+    slots = n_parts + units
+    off = (slots * 32 * d * 4 + 255) // 256 * 256
+    flat = ws.view(torch.uint8)
+    o = flat[:slots * 32 * d * 4].view(torch.float32).view(slots, 32, d)
+    l = flat[off:off + slots * 32 * 4].view(torch.float32).view(slots, 32)
+    return o, l
+
+
 def naive_workspace_bytes(B: int, H: int, N: int, dtype: torch.dtype) -> int:
     return int(_lib.load().fa_naive_workspace_bytes(B, H, N, DTYPE_CODES[dtype]))
 

@@ -122,6 +122,34 @@ def test_kv_head_map():
         assert fa.kv_head(bh, H, Hkv) == -1
 
 
+def test_decode_rejects(lib):
+    big = 1 << 30
+
+    def call(q=A, k=A, v=A, lens=None, o=A, lse=A, ws=A, ws_bytes=big, B=2, H=8, Hkv=2, Nkv=100, d=128,
+             scale=0.5, parts=3, dtype=2):
+        return lib.fa_decode(q, k, v, lens, o, lse, ws, ws_bytes, B, H, Hkv, Nkv, d, scale, parts, dtype, None)
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(ws=None),
+               dict(ws_bytes=16), dict(parts=0), dict(parts=1025), dict(Hkv=3), dict(Hkv=0), dict(Hkv=16),
+               dict(B=0), dict(Nkv=0), dict(scale=float("nan"))):
+        assert call(**kw) == FA_ERR_ARG, kw
+    for kw in (dict(d=96), dict(dtype=0), dict(dtype=5)):
+        assert call(**kw) == FA_ERR_UNSUPPORTED, kw
+    for kw in (dict(q=A + 2), dict(k=A + 8), dict(o=A + 4), dict(ws=A + 4), dict(lens=A + 2)):
+        assert call(**kw) == FA_ERR_ALIGN, kw
+    assert call(parts=1, ws=None, ws_bytes=0, d=96) == FA_ERR_UNSUPPORTED  # one part needs no workspace
+
+
+def test_decode_workspace_bytes(lib):
+    assert lib.fa_decode_workspace_bytes(1, 64, 8, 128, 1) == 0
+    for B, H, Hkv, d, parts in ((2, 8, 2, 64, 5), (1, 64, 8, 128, 256), (3, 96, 1, 128, 7)):
+        units = B * Hkv * ((H // Hkv + 31) // 32)
+        slots = parts + units
+        want = (slots * 32 * d * 4 + 255) // 256 * 256 + (slots * 32 * 4 + 255) // 256 * 256
+        assert lib.fa_decode_workspace_bytes(B, H, Hkv, d, parts) == want
+    for bad in ((2, 8, 3, 64, 5), (2, 8, 2, 96, 5), (2, 8, 2, 64, 0), (2, 8, 2, 64, 1025), (0, 8, 2, 64, 5)):
+        assert lib.fa_decode_workspace_bytes(*bad) == 0
+
+
 def test_naive_rejects(lib):
     args = [A] * 7
 
