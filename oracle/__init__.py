@@ -11,8 +11,9 @@ is ours):
 
 * [essay]  "Flash Attention: IO-awareness principle" (hrletsgo.me documents),
   sections "Standard Attention's real bottleneck", "Tiling", "Recomputation",
-  and the section on serving (grouped-query attention, oracle/gqa.py;
-  decoding, oracle/decode.py).
+  and the sections on serving (grouped-query attention, oracle/gqa.py;
+  decoding, oracle/decode.py) and on PagedAttention and chunked prefill
+  (oracle/chunk.py).
 * [lesson] "Flash Attention -- five lessons converging into 80 lines",
   CUDA training lesson 06 (brianyu43.github.io), sections "Results",
   "Lesson 1", "LLM-serving translation" (decode: one query per head).
@@ -40,4 +41,5 @@ from .attention import (  # noqa: F401
     loss,
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa, attn_fwd_rows_gqa  # noqa: F401
+from .chunk import attn_fwd_chunk, attn_fwd_chunk_rows  # noqa: F401
 from .decode import attn_decode, decode_partials, decode_split_merge, merge_partials, split_bounds  # noqa: F401

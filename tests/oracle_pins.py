@@ -437,3 +437,60 @@ def pin_partials_torch(partials):
             _close(o_s[b, :, s], ref, 1e-12, "partial O")
             for h in range(4):
                 _close(lse_s[b, h, s], logsumexp(0.6 * (k[b, h, k0:k1] @ q[b, h])), 1e-12, "partial LSE")
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill pins ([essay], section on PagedAttention and chunked
+# prefill): Nq queries, the last Nq of Nk positions
+# ----------------------------------------------------------------------------
+
+def _chunk_inputs(B, H, Hkv, nq, nk, d, seed):
+    return (rand((B, H, nq, d), seed), rand((B, Hkv, nk, d), seed + 1), rand((B, Hkv, nk, d), seed + 2))
+
+
+def pin_chunk_is_suffix_of_causal(chunk_fwd, fwd_gqa):
+    """A chunk's rows equal the last Nq rows of causal grouped-query attention
+    over the whole sequence (earlier query rows arbitrary)."""
+    for nq, nk in ((5, 19), (1, 7), (19, 19), (32, 70)):
+        q, k, v = _chunk_inputs(2, 4, 2, nq, nk, 3, 500 + nk)
+        qfull = rand((2, 4, nk, 3), 510 + nk)
+        qfull[:, :, nk - nq:] = q
+        of, lf = fwd_gqa(qfull, k, v, 0.6, True)
+        o, lse = chunk_fwd(q, k, v, 0.6, True)
+        _close(o, of[:, :, nk - nq:], 1e-12, f"chunk suffix O {nq}/{nk}")
+        _close(lse, lf[:, :, nk - nq:], 1e-12, f"chunk suffix LSE {nq}/{nk}")
+
+
+def pin_chunk_torch_sdpa(chunk_fwd):
+    """Independent library: torch float64 SDPA with an explicit boolean mask
+    (key j allowed for query i iff j <= i + Nk - Nq) and enable_gqa; without
+    the mask, plain SDPA.  LSE from scipy's logsumexp."""
+    for causal in (False, True):
+        for nq, nk in ((7, 23), (23, 23), (1, 9)):
+            q, k, v = _chunk_inputs(1, 6, 3, nq, nk, 5, 520 + nq)
+            o, lse = chunk_fwd(q, k, v, 0.45, causal)
+            mask = None
+            if causal:
+                mask = torch.from_numpy(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.45,
+                enable_gqa=True).numpy()
+            _close(o, ref, 1e-12, f"chunk sdpa O causal={causal} {nq}/{nk}")
+            for h in range(6):
+                s = 0.45 * (q[0, h] @ k[0, h // 2].T)
+                if causal:
+                    s[~mask.numpy()] = -np.inf
+                _close(lse[0, h], logsumexp(s, axis=1), 1e-12, "chunk LSE")
+
+
+def pin_chunked_prefill_reassembles(chunk_fwd, fwd_gqa):
+    """Prefill done chunk by chunk (each chunk against every key up to its
+    end) reassembles causal attention over the whole prompt."""
+    n = 41
+    q, k, v = _chunk_inputs(1, 2, 1, n, n, 4, 530)
+    full_o, full_l = fwd_gqa(q, k, v, 0.8, True)
+    for cuts in ((0, 16, 32, 41), (0, 1, 40, 41), (0, 41)):
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            o, lse = chunk_fwd(q[:, :, c0:c1], k[:, :, :c1], v[:, :, :c1], 0.8, True)
+            _close(o, full_o[:, :, c0:c1], 1e-12, f"chunk [{c0},{c1})")
+            _close(lse, full_l[:, :, c0:c1], 1e-12, f"chunk LSE [{c0},{c1})")

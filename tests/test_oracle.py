@@ -218,3 +218,28 @@ def test_decode_rejects():
         oracle.attn_decode(q, k, v, 0.5, [6])
     with pytest.raises(ValueError):
         oracle.decode_partials(q, k, v, 0.5, 2, 2)
+
+
+# Chunked prefill ([essay], section on PagedAttention and chunked prefill).
+
+def test_chunk_pins():
+    P.pin_chunk_is_suffix_of_causal(oracle.attn_fwd_chunk, oracle.attn_fwd_gqa)
+    P.pin_chunk_torch_sdpa(oracle.attn_fwd_chunk)
+    P.pin_chunked_prefill_reassembles(oracle.attn_fwd_chunk, oracle.attn_fwd_gqa)
+
+
+def test_chunk_rows_helper():
+    q, k, v = P._chunk_inputs(2, 4, 2, 9, 30, 4, 540)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_chunk(q, k, v, 0.5, causal)
+        rows = [(0, 0, 0), (1, 3, 8), (0, 2, 4)]
+        ro, rl = oracle.attn_fwd_chunk_rows(q, k, v, 0.5, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            np.testing.assert_allclose(ro[n], o[b, h, i], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(rl[n], lse[b, h, i], rtol=0, atol=1e-13)
+
+
+def test_chunk_rejects():
+    q, k, v = P._chunk_inputs(1, 4, 2, 9, 5, 4, 545)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_chunk(q, k, v, 0.5, True)  # causal chunk longer than its keys

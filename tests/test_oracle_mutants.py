@@ -247,3 +247,47 @@ def test_decode_mutant_is_caught(mut):
             ("split", lambda: P.pin_split_merge(split_merge, oracle.attn_decode))]
     with np.errstate(over="ignore", invalid="ignore"):
         assert _fails_some(pins), f"mutant {mut} passed every decode pin"
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill: the alignment of the causal mask
+# ---------------------------------------------------------------------------
+
+def _chunk_variant(mut):
+    def fwd(q, k, v, scale, causal):
+        B, H, Nq, _ = q.shape
+        Hkv, Nk = k.shape[1], k.shape[2]
+        off = {"top_left": 0, "offset_sign": -(Nk - Nq), "off_by_one": Nk - Nq - 1}.get(mut, Nk - Nq)
+        o, lse = np.empty(q.shape[:3] + (v.shape[3],)), np.empty(q.shape[:3])
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // Hkv)
+                s = scale * (q[b, h] @ k[b, g].T)
+                if causal:
+                    s[np.arange(Nk)[None, :] > np.arange(Nq)[:, None] + off] = -np.inf
+                m = s.max(1, keepdims=True)
+                f = np.exp(s - m)
+                o[b, h] = (f / f.sum(1, keepdims=True)) @ v[b, g]
+                lse[b, h] = (m + np.log(f.sum(1, keepdims=True)))[:, 0]
+        return o, lse
+    return fwd
+
+
+CHUNK_MUTANTS = ["top_left", "offset_sign", "off_by_one"]
+
+
+def test_chunk_unmutated_variant_passes():
+    fwd = _chunk_variant(None)
+    P.pin_chunk_is_suffix_of_causal(fwd, oracle.attn_fwd_gqa)
+    P.pin_chunk_torch_sdpa(fwd)
+    P.pin_chunked_prefill_reassembles(fwd, oracle.attn_fwd_gqa)
+
+
+@pytest.mark.parametrize("mut", CHUNK_MUTANTS)
+def test_chunk_mutant_is_caught(mut):
+    fwd = _chunk_variant(mut)
+    pins = [("suffix", lambda: P.pin_chunk_is_suffix_of_causal(fwd, oracle.attn_fwd_gqa)),
+            ("sdpa", lambda: P.pin_chunk_torch_sdpa(fwd)),
+            ("reassemble", lambda: P.pin_chunked_prefill_reassembles(fwd, oracle.attn_fwd_gqa))]
+    with np.errstate(invalid="ignore"):
+        assert _fails_some(pins), f"mutant {mut} passed every chunk pin"
