@@ -447,6 +447,22 @@ def run_legs(torch, fa, fa_synth, dev):
     del q, k, v, do, o, lse, kr, vr
     torch.cuda.empty_cache()
 
+    # chunked prefill: 2048 new queries after 14336 cached keys (bottom-right
+    # causal mask), grouped K/V heads
+    w = fa_synth.CHUNK_PREFILL
+    Nk = fa_synth.CHUNK_PREFILL_NK
+    q, k, v = (t.to(dev) for t in fa_synth.make_chunk_inputs(w.B, w.H, w.kv_heads, w.N, Nk, w.d, w.dtype, w.seed))
+    o, lse = fa.fwd_chunk(q, k, v, w.scale, w.causal)
+    ms, ms_min = time_reps(lambda: fa.fwd_chunk(q, k, v, w.scale, w.causal, out=o, lse=lse), 20, torch)
+    # visible (query, key) pairs: query i sees i + Nk - Nq + 1 keys
+    pairs = w.B * w.H * (w.N * (Nk - w.N) + w.N * (w.N + 1) / 2)
+    tf = 4.0 * pairs * w.d / (ms * 1e-3) / 1e12
+    entry = {"fwd_ms": ms, "fwd_ms_min": ms_min, "Nk": Nk, "fwd_tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS}
+    legs[w.name] = entry
+    log(f"[bench] {w.name}: {entry}")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
     # decode steps (one query per head against a K/V cache): HBM-bound, so
     # reported as K/V bytes read per second against the HBM peak
     for w in (fa_synth.GQA_DECODE, fa_synth.GQA_DECODE_RAGGED):

@@ -80,6 +80,12 @@ GQA_DECODE = Workload("gqa_decode_B1_H64_Hkv8_N32768_d128_bf16", 1, 64, 32768, 1
 GQA_DECODE_RAGGED = Workload("gqa_decode_ragged_B16_H64_Hkv8_N8192_d128_bf16", 16, 64, 8192, 128, "bf16", False,
                              1 / math.sqrt(128), 1008, passes=("decode",), Hkv=8)
 
+# A chunk of 2048 new prompt tokens after 14336 cached ones (keys 16384),
+# same model shape: the causal mask is aligned at the bottom-right corner.
+CHUNK_PREFILL = Workload("gqa_chunk_prefill_B1_H64_Hkv8_Nq2048_Nk16384_d128_bf16", 1, 64, 2048, 128, "bf16", True,
+                         1 / math.sqrt(128), 1009, passes=("fwd",), Hkv=8)
+CHUNK_PREFILL_NK = 16384
+
 GQA_PREFILL = Workload("gqa_causal_prefill_B1_H64_Hkv8_N8192_d128_bf16", 1, 64, 8192, 128, "bf16", True,
                        1 / math.sqrt(128), 1006, passes=("fwd", "bwd"), Hkv=8)
 
@@ -122,6 +128,16 @@ def make_decode_inputs(B: int, H: int, Hkv: int, Nkv: int, d: int, dtype: str, s
     else:
         lens = torch.full((B,), Nkv, dtype=torch.int32)
     return q, k, v, lens
+
+
+def make_chunk_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, seed: int):
+    """A prefill chunk: q [B,H,Nq,d] and K, V [B,Hkv,Nk,d], all N(0, 1)
+    rounded to ``dtype``.  Draw order: q, K, V."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn(B, H, Nq, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    k = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    v = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+    return q, k, v
 
 
 def workload_inputs(w: Workload, with_dout: bool | None = None):

@@ -131,6 +131,23 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                void* stream);
 
 /*
+ * Chunked prefill ("Flash Attention: IO-awareness principle", section on
+ * PagedAttention and chunked prefill: serving feeds the kernel a chunk of
+ * the prompt at a time over contiguous K/V).  Nq new queries are the last
+ * Nq of Nk positions: with causal = 1, query i (0-based in the chunk) keeps
+ * key j iff j <= i + (Nk - Nq), the square causal mask aligned at the
+ * bottom-right corner; with causal = 0 every query sees all Nk keys.  K/V
+ * heads are shared as in fa_fwd_gqa.
+ * q, o: dtype [B,H,Nq,d]; k, v: dtype [B,Hkv,Nk,d]; lse: float32 [B,H,Nq].
+ * Requires Nq <= Nk when causal (else FA_ERR_ARG); dtype f16 or bf16 when
+ * Nq != Nk (f32 -> FA_ERR_UNSUPPORTED); other checks and errors as
+ * fa_fwd_gqa.  fa_fwd_gqa(..., N, ...) is fa_fwd_chunk(..., Nq = N, Nk = N, ...).
+ */
+int fa_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                 void* stream);
+
+/*
  * Backward of fa_fwd_gqa.  q, o, dout: dtype [B,H,N,d]; k, v: dtype
  * [B,Hkv,N,d]; lse, delta_ws: float32 [B,H,N]; dq: float32 [B,H,N,d];
  * dk, dv: float32 [B,Hkv,N,d], each the sum over the K/V head's G query

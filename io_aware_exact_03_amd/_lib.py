@@ -21,6 +21,7 @@ SIGNATURES = {
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd_stage": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_fwd_chunk": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_bwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_kv_head": (_i, [_i, _i, _i]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),

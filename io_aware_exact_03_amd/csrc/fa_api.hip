@@ -82,6 +82,26 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
   return (size_t)B * H * (size_t)N * (size_t)N * (dtype == FA_F32 ? 4 : 2);
 }
 
+int fa_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                 int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
+  int st = check_shape(B, H, Nq, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  st = check_shape(B, H, Nk, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
+  if (causal && Nq > Nk) return FA_ERR_ARG;
+  if (Nq != Nk && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.G = H / Hkv; a.N = Nq; a.Nk = Nk; a.d = d; a.dtype = dtype; a.causal = causal != 0;
+  a.qk_scale = fabsf(scale) * fa::kLog2eHost;
+  a.neg = scale < 0.f;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_fwd(a));
+}
+
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
                int d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
@@ -91,7 +111,7 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   fa::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.BH = B * H; a.G = H / Hkv; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
+  a.BH = B * H; a.G = H / Hkv; a.N = N; a.Nk = N; a.d = d; a.dtype = dtype; a.causal = causal != 0;
   a.qk_scale = fabsf(scale) * fa::kLog2eHost;
   a.neg = scale < 0.f;
   a.stream = static_cast<hipStream_t>(stream);

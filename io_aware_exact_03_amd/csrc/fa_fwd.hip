@@ -79,8 +79,8 @@ constexpr float kSumLimit = 256.f;
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, int BH, int G,
-    float qk_scale, uint32_t qsign) {
+    uint16_t* __restrict__ og, float* __restrict__ lseg, int Nq, int Nk, int qshift, int koff, int n_qblk,
+    int BH, int G, float qk_scale, uint32_t qsign) {
   using C = Fwd16<T, D, BN, CAUSAL>;
   constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
@@ -93,12 +93,20 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
 
   // ---- Q fragments of the current query block, held in registers --------
   // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
-  // rows past N read as zeros.  A negative scale flips Q's sign bits.  The
-  // next block's fragments are loaded during the current block's tail.
+  // rows outside [0, Nq) read as zeros (a negative row wraps to an offset
+  // past the buffer).  A negative scale flips Q's sign bits.  The next
+  // block's fragments are loaded during the current block's tail.
+  //
+  // Query rows are indexed virtually: virtual row i' is query i' - qshift,
+  // and with the causal mask it sees keys j <= i' + koff, koff a multiple of
+  // 32.  A query offset off = Nk - Nq (the queries are the last Nq of Nk
+  // positions) becomes koff = off - off % 32 and qshift = off % 32, so the
+  // diagonal always falls on whole 32-key sub-blocks.  Square attention has
+  // qshift = koff = 0.
   uint4 qf[DS];
   auto load_q = [&](int bh, int qblk) __attribute__((always_inline)) {
-    const rsrc_t rs = make_rsrc(qg + (size_t)bh * (size_t)N * D, (uint32_t)N * D * 2);
-    const int q = qblk * C::BM + 32 * wave + n;
+    const rsrc_t rs = make_rsrc(qg + (size_t)bh * (size_t)Nq * D, (uint32_t)Nq * D * 2);
+    const int q = qblk * C::BM + 32 * wave + n - qshift;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       uint4 x = load16(rs, ((uint32_t)q * D + 16 * s + 8 * g) * 2);
@@ -110,9 +118,9 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // One query block of one (batch, head), start to finish; (nbh, nqblk) is
   // the block this workgroup runs next (nbh < 0: none).
   auto block = [&](int bh, int qblk, int nbh, int nqblk) __attribute__((always_inline)) {
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;  // shared by G query heads
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const size_t head = (size_t)bh * (size_t)Nq * D;
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)Nk * D;  // shared by G query heads
+  const uint32_t head_bytes = (uint32_t)Nk * D * 2;
   const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
   const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
 
@@ -127,20 +135,22 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // diagonal sub-block (keys qw0 .. qw0 + 31, the pages' masked stage),
   // otherwise the sub-block holding the sequence tail.  Sub-blocks after
   // u_last (the future) are never computed.  A wave whose queries all lie
-  // past N (u_last = -1) only helps load tiles.
-  const int n_sub = (N + 31) / 32;
-  const bool wave_live = qw0 < N;
-  const int u_last = !wave_live ? -1 : (CAUSAL ? qw0 / 32 : n_sub - 1);
-  const int last_live = min(C::NW - 1, (N - 1 - q0) / 32);  // q0 < N always
-  const int u_end = CAUSAL ? (q0 / 32 + last_live) : (n_sub - 1);
+  // past the last query (u_last = -1) only helps load tiles.  In virtual
+  // rows the diagonal sub-block of the wave is (qw0 + koff) / 32.
+  const int NqV = Nq + qshift;  // virtual rows
+  const int n_sub = (Nk + 31) / 32;
+  const bool wave_live = qw0 < NqV;
+  const int u_last = !wave_live ? -1 : (CAUSAL ? (qw0 + koff) / 32 : n_sub - 1);
+  const int last_live = min(C::NW - 1, (NqV - 1 - q0) / 32);  // q0 < NqV always
+  const int u_end = CAUSAL ? ((q0 + koff) / 32 + last_live) : (n_sub - 1);
   const int j_end = u_end / SUB + 1;  // tiles this workgroup reads
-  const int key_lim = CAUSAL ? min(query + 1, N) : N;
+  const int key_lim = CAUSAL ? min(query + koff + 1, Nk) : Nk;
 
   // ---- tile loads: global -> LDS ------------------------------------------
   // Piece t (0 .. 2 PPT - 1) = wave LPW + e holds RPP tile rows of K
   // (t < PPT) or V.  Lane l fills LDS bytes 16 l of the piece: row l / CPR,
   // stored chunk l % CPR, which holds the row's logical chunk
-  // (l % CPR) ^ swz_chunk(row).  Rows past N read as zeros.
+  // (l % CPR) ^ swz_chunk(row).  Rows past Nk read as zeros.
   auto issue = [&](int j, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
     const int lrow = lane / C::CPR;
 #pragma unroll
@@ -387,8 +397,9 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
-  if (wave_live && query < N) {
-    uint16_t* orow = og + head + (size_t)query * D;
+  const int qrow = query - qshift;  // the real query of this lane's virtual row
+  if (wave_live && qrow >= 0 && qrow < Nq) {
+    uint16_t* orow = og + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
       }
     }
-    if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot)) * kLn2;
+    if (g == 0) lseg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
   };
 
@@ -620,7 +631,11 @@ template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const FwdArgs& a) {
   constexpr int BN = Tile16<D>::BN;
   using C = Fwd16<T, D, BN, CAUSAL>;
-  const int n_qblk = (a.N + C::BM - 1) / C::BM;
+  // Causal queries are the last N of Nk positions: offset Nk - N, split into
+  // a multiple of 32 (koff) and a shift of the virtual query rows (qshift).
+  const int off = CAUSAL ? a.Nk - a.N : 0;
+  const int qshift = off % 32, koff = off - qshift;
+  const int n_qblk = (a.N + qshift + C::BM - 1) / C::BM;
   const long long items = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // One workgroup per CU (the LDS ring takes the whole 160 KB), never more
@@ -632,8 +647,8 @@ hipError_t launch16(const FwdArgs& a) {
   const int grid = (int)(items < cus ? items : cus);
   hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk, a.BH,
-                     a.G, a.qk_scale, a.neg ? 0x80008000u : 0u);
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, a.Nk, qshift, koff,
+                     n_qblk, a.BH, a.G, a.qk_scale, a.neg ? 0x80008000u : 0u);
   return hipGetLastError();
 }
 

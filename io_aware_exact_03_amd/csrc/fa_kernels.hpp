@@ -15,10 +15,11 @@ struct FwdArgs {
   float* lse;
   int BH;          // batch * query heads
   int G;           // query heads per K/V head (1: one K/V head per query head); K/V head = bh / G
-  int N;
+  int N;           // queries per head
+  int Nk;          // keys per head (N for square attention)
   int d;           // 64 or 128
   int dtype;       // 0 f32, 1 f16, 2 bf16
-  bool causal;
+  bool causal;     // query i sees keys j <= i + (Nk - N)
   float qk_scale;  // |scale| * log2(e)
   bool neg;        // scale < 0: the kernels negate Q on load
   hipStream_t stream;

@@ -99,6 +99,28 @@ def fwd_gqa(q, k, v, scale: float, causal: bool, out=None, lse=None):
     return out, lse
 
 
+def fwd_chunk(q, k, v, scale: float, causal: bool, out=None, lse=None):
+    """Chunked prefill: q [B,H,Nq,d] are the last Nq of Nk positions, k and v
+    [B,Hkv,Nk,d]; causal keeps key j for query i iff j <= i + Nk - Nq.
+    Returns (O [B,H,Nq,d], LSE [B,H,Nq])."""
+    _check_qkv(q)
+    _check_qkv(k, v)
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k, v must share q's dtype and device")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or H % Hkv != 0:
+        raise ValueError(f"k, v shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                  Hkv, Nq, Nk, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_fwd_chunk")
+    return out, lse
+
+
 def bwd_gqa(q, k, v, o, dout, lse, scale: float, causal: bool, delta=None, dq=None, dk=None, dv=None):
     """Backward of fwd_gqa: returns (dQ [B,H,N,d], dK and dV [B,Hkv,N,d],
     all float32, each dK/dV summed over its group, Delta [B,H,N])."""

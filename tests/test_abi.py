@@ -109,6 +109,18 @@ def test_gqa_rejects(lib):
         assert b(ptrs=ptrs) == FA_ERR_ALIGN
 
 
+def test_chunk_rejects(lib):
+    def f(Nq=8, Nk=16, causal=1, dtype=2, H=4, Hkv=2, d=64, q=A):
+        return lib.fa_fwd_chunk(q, A, A, A, A, 1, H, Hkv, Nq, Nk, d, 0.5, causal, dtype, None)
+    assert f(Nq=17, Nk=16) == FA_ERR_ARG          # causal chunk longer than its keys
+    assert f(Nq=0) == FA_ERR_ARG and f(Nk=0) == FA_ERR_ARG
+    assert f(Hkv=3) == FA_ERR_ARG and f(q=None) == FA_ERR_ARG
+    assert f(dtype=0) == FA_ERR_UNSUPPORTED        # f32 only for square attention
+    assert f(d=96) == FA_ERR_UNSUPPORTED
+    assert f(q=A + 8) == FA_ERR_ALIGN
+    assert f(Nk=(1 << 31) // (64 * 2), causal=0) == FA_ERR_UNSUPPORTED  # K/V head of 2 GiB
+
+
 def test_kv_head_map():
     """Query head h of batch b reads K/V head h // (H // Hkv) of batch b; the
     kernels' flat form is bh // G."""
