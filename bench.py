@@ -498,6 +498,33 @@ def run_legs(torch, fa, fa_synth, dev):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
+    # FA1 loop order (K/V outer, running O/l/m through global memory, one
+    # workgroup per head) against the fused FA2-order forward
+    for w in (fa_synth.NONCAUSAL_SWEEP[1], fa_synth.NONCAUSAL_SWEEP[3], fa_synth.TRAIN_STEP):
+        q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+        ws = torch.empty(fa.fa1_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fa.fwd_fa1(q, k, v, w.scale, w.causal, out=o, lse=lse, ws=ws)
+        ms1, _ = time_reps(lambda: fa.fwd_fa1(q, k, v, w.scale, w.causal, out=o, lse=lse, ws=ws), 3, torch)
+        ms2, _ = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 10, torch)
+        # FA1's compulsory traffic: K, V once; per (key block, query block)
+        # step Q_i read, O_i (fp32) read and written, m_i and l_i read and
+        # written; then O and LSE written.
+        tc, tr, br, bc = -(-w.N // 64), -(-w.N // 128), 128, 64
+        steps = sum(tr - ((j * bc) // br if w.causal else 0) for j in range(tc))
+        e = 2
+        fa1_bytes = w.B * w.H * (2 * w.N * w.d * e + steps * br * (w.d * e + 2 * w.d * 4 + 4 * 4)
+                                 + w.N * w.d * e + 4 * w.N)
+        entry = {"fa1_ms": ms1, "fa2_ms": ms2, "fa2_speedup_over_fa1": ms1 / ms2,
+                 "fa1_tflops": fwd_flops(w.B, w.H, w.N, w.d, w.causal) / (ms1 * 1e-3) / 1e12,
+                 "fa1_model_bytes": fa1_bytes, "fa2_model_bytes": fused_fwd_bytes(w.B, w.H, w.N, w.d, e),
+                 "fa1_model_gbs": fa1_bytes / (ms1 * 1e-3) / 1e9}
+        legs[f"fa1_ablation_{w.name}"] = entry
+        log(f"[bench] fa1_ablation_{w.name}: {entry}")
+        del q, k, v, ws, o, lse
+        torch.cuda.empty_cache()
+
     # fp32 single head
     w = fa_synth.SINGLE_HEAD_F32
     q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))

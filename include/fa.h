@@ -227,6 +227,27 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int d, int n_parts);
 int fa_decode_plan(int B, int H, int Hkv, int Nkv, int d, int* n_parts);
 
 /*
+ * FlashAttention-1 loop order, kept to measure what the FA2 loop swap buys
+ * ("Paper review: FlashAttention ...", Algorithm 1; "Flash Attention:
+ * IO-awareness principle", section "FA2/FA3").  Same result as fa_fwd: o
+ * (dtype [B,H,N,d]) and lse (float32 [B,H,N], natural log).  One
+ * workgroup per (batch, head); K/V blocks of 64 keys in the outer loop,
+ * query blocks of 128 rows inside, and at every step the block's running O,
+ * l, m are read from and written back to ws.  ws (16-byte aligned, caller
+ * owned, fa_fa1_workspace_bytes() bytes) holds afterwards: float32 O
+ * [B,H,N,d] (normalised), then at ceil256 offsets float32 m [B,H,N] (row
+ * max of scale * S in log2 units) and float32 l [B,H,N], with
+ * lse = (m + log2 l) ln 2.  dtype f16 or bf16 (f32 -> FA_ERR_UNSUPPORTED);
+ * other checks and errors as fa_fwd, a missing or short ws -> FA_ERR_ARG.
+ */
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+               size_t ws_bytes, int B, int H, int N, int d, float scale, int causal, int dtype,
+               void* stream);
+
+/* Workspace bytes of fa_fwd_fa1 (0 for invalid arguments). */
+size_t fa_fa1_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * Naive three-kernel forward ("Flash Attention -- five lessons converging
  * into 80 lines", "Two implementations"; Algorithm 0 of the FlashAttention
  * paper review): kernel 1 writes S = scale * Q K^T for all N x N into

@@ -233,6 +233,33 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return hip_status(fa::launch_decode(a));
 }
 
+size_t fa_fa1_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return align256(rows * d * 4) + 2 * align256(rows * 4);
+}
+
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, size_t ws_bytes, int B,
+               int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !ws) return FA_ERR_ARG;
+  const int st = check_shape(B, H, N, d, dtype, causal, scale);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (ws_bytes < fa_fa1_workspace_bytes(B, H, N, d)) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  fa::Fa1Args a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  const size_t rows = (size_t)B * H * N;
+  a.ows = static_cast<float*>(ws);
+  a.mws = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(rows * d * 4));
+  a.lws = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(rows * d * 4) + align256(rows * 4));
+  a.BH = B * H; a.N = N; a.d = d; a.dtype = dtype; a.causal = causal != 0; a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_fa1(a));
+}
+
 int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* s_ws, void* p_ws, int B,
                  int H, int N, int d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !s_ws || !p_ws) return FA_ERR_ARG;

@@ -78,10 +78,26 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+struct Fa1Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* ows;      // [BH, N, d] running O (fp32)
+  float* mws;      // [BH, N] running max, log2 units
+  float* lws;      // [BH, N] running sum
+  int BH, N, d, dtype;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0 = all three launches in order; 1 = Delta, 2 = dK/dV, 3 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, int stage);
 hipError_t launch_naive(const NaiveArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_fa1(const Fa1Args& a);
 
 }  // namespace fa

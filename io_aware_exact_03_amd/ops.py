@@ -206,6 +206,41 @@ def decode_pieces(ws, B: int, H: int, Hkv: int, d: int, n_parts: int):
     return o, l
 
 
+def fa1_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_fa1_workspace_bytes(B, H, N, d))
+
+
+def fwd_fa1(q, k, v, scale: float, causal: bool, out=None, lse=None, ws=None):
+    """The FlashAttention-1 loop order (K/V outer, running O/l/m in global
+    memory): returns (O, LSE) like fwd(); `ws` (allocated if None) holds the
+    final running state afterwards."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(fa1_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    st = _lib.load().fa_fwd_fa1(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                ws.data_ptr(), ws.numel() * ws.element_size(), B, H, N, d, float(scale),
+                                int(bool(causal)), DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_fwd_fa1")
+    return out, lse
+
+
+def fa1_state(ws, B: int, H: int, N: int, d: int):
+    """Views of an fwd_fa1 workspace: (O [B,H,N,d], m [B,H,N] log2 units, l)."""
+    rows = B * H * N
+    a = (rows * d * 4 + 255) // 256 * 256
+    b = (rows * 4 + 255) // 256 * 256
+    flat = ws.view(torch.uint8)
+    o = flat[:rows * d * 4].view(torch.float32).view(B, H, N, d)
+    m = flat[a:a + rows * 4].view(torch.float32).view(B, H, N)
+    l = flat[a + b:a + b + rows * 4].view(torch.float32).view(B, H, N)
+    return o, m, l
+
+
 def naive_workspace_bytes(B: int, H: int, N: int, dtype: torch.dtype) -> int:
     return int(_lib.load().fa_naive_workspace_bytes(B, H, N, DTYPE_CODES[dtype]))
 

@@ -121,6 +121,19 @@ def test_chunk_rejects(lib):
     assert f(Nk=(1 << 31) // (64 * 2), causal=0) == FA_ERR_UNSUPPORTED  # K/V head of 2 GiB
 
 
+def test_fa1_rejects(lib):
+    big = 1 << 30
+
+    def f(ws=A, ws_bytes=big, N=100, d=64, dtype=2, q=A):
+        return lib.fa_fwd_fa1(q, A, A, A, A, ws, ws_bytes, 2, 2, N, d, 0.5, 1, dtype, None)
+    assert f(ws=None) == FA_ERR_ARG and f(ws_bytes=100) == FA_ERR_ARG and f(q=None) == FA_ERR_ARG
+    assert f(dtype=0) == FA_ERR_UNSUPPORTED and f(d=80) == FA_ERR_UNSUPPORTED
+    assert f(ws=A + 4) == FA_ERR_ALIGN
+    rows = 2 * 3 * 50
+    assert lib.fa_fa1_workspace_bytes(2, 3, 50, 64) == (rows * 64 * 4 + 255) // 256 * 256 + 2 * ((rows * 4 + 255) // 256 * 256)
+    assert lib.fa_fa1_workspace_bytes(2, 3, 50, 96) == 0
+
+
 def test_kv_head_map():
     """Query head h of batch b reads K/V head h // (H // Hkv) of batch b; the
     kernels' flat form is bh // G."""
