@@ -11,6 +11,7 @@ is ours):
 
 * [essay]  "Flash Attention: IO-awareness principle" (hrletsgo.me documents),
   sections "Standard Attention's real bottleneck", "Tiling", "Recomputation",
+  the section "FA2/FA3" (FP8 mode, oracle/fp8.py),
   and the sections on serving (grouped-query attention, oracle/gqa.py;
   decoding, oracle/decode.py) and on PagedAttention and chunked prefill
   (oracle/chunk.py).
@@ -41,5 +42,7 @@ from .attention import (  # noqa: F401
     loss,
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa, attn_fwd_rows_gqa  # noqa: F401
+from .fp8 import (  # noqa: F401
+    attn_fwd_fp8, attn_fwd_fp8_model, dequantize, e4m3_decode, e4m3_round, p_rounding_bound)
 from .chunk import attn_fwd_chunk, attn_fwd_chunk_rows  # noqa: F401
 from .decode import attn_decode, decode_partials, decode_split_merge, merge_partials, split_bounds  # noqa: F401

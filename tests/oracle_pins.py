@@ -494,3 +494,75 @@ def pin_chunked_prefill_reassembles(chunk_fwd, fwd_gqa):
             o, lse = chunk_fwd(q[:, :, c0:c1], k[:, :, :c1], v[:, :, :c1], 0.8, True)
             _close(o, full_o[:, :, c0:c1], 1e-12, f"chunk [{c0},{c1})")
             _close(lse, full_l[:, :, c0:c1], 1e-12, f"chunk LSE [{c0},{c1})")
+
+
+# ----------------------------------------------------------------------------
+# FP8 pins ([essay] section "FA2/FA3": FA3's FP8 mode).  The code book is
+# OCP E4M3; torch's float8_e4m3fn is the independent implementation.
+# ----------------------------------------------------------------------------
+
+def pin_e4m3_codebook(decode):
+    """All 256 codes against torch.float8_e4m3fn, plus closed forms: 0x38 = 1,
+    0x7E = 448 (largest), 0x08 = 2^-6 (smallest normal), 0x01 = 2^-9
+    (smallest subnormal), 0x80 = -0, 0x7F and 0xFF = NaN."""
+    got = decode(np.arange(256))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "E4M3 NaN codes"
+    fin = ~np.isnan(ref)
+    _close(got[fin], ref[fin], 0.0, "E4M3 code book")
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0x80] == 0.0 and np.signbit(got[0x80]) and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def pin_e4m3_round(rnd, decode):
+    """Round-to-nearest-even onto the code book: random values, exact
+    midpoints between neighbouring codes (ties go to the even mantissa) and
+    subnormals, against torch's conversion."""
+    vals = decode(np.arange(0x7F))  # non-negative finite codes, ascending
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([RNG(600).standard_normal(4000) * 40, RNG(601).standard_normal(1000) * 0.01,
+                        mids, -mids, vals])
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    _close(rnd(x), ref, 0.0, "E4M3 rounding")
+
+
+def _fp8_inputs(B, H, Hkv, n, d, seed, sigma=1.0):
+    """Codes via torch's conversion after a per-tensor scale amax / 448."""
+    out, scales = [], []
+    for i, heads in enumerate((H, Hkv, Hkv)):
+        x = torch.from_numpy(rand((B, heads, n, d), seed + i, sigma))
+        ds = float(x.abs().max()) / 448.0
+        out.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        scales.append(ds)
+    return out[0], out[1], out[2], tuple(scales)
+
+
+def pin_fp8_attention(attn_fp8, fwd_gqa):
+    """The FP8 reference is grouped-query attention of the dequantised codes
+    (dequantised here with torch, independently of the oracle's decoder)."""
+    for causal in (False, True):
+        q8, k8, v8, ds = _fp8_inputs(2, 4, 2, 21, 8, 610)
+        deq = [torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy() * s for c, s in zip((q8, k8, v8), ds)]
+        o, lse = attn_fp8(q8, k8, v8, ds, 0.4, causal)
+        ro, rl = fwd_gqa(*deq, 0.4, causal)
+        _close(o, ro, 1e-13, "fp8 attention O")
+        _close(lse, rl, 1e-13, "fp8 attention LSE")
+
+
+def pin_p_rounding_bound(bound, model, attn_fp8):
+    """Simulating the rounding of P (E4M3, ties to even, relative to the
+    exact row max, with scales 2^8 and 2^5) stays within the bound, and the
+    bound is not vacuous: some element uses at least a tenth of it, and it
+    never exceeds 2^-4 max|V| + N 2^-18 max|V|."""
+    for causal in (False, True):
+        for sigma in (1.0, 3.0):
+            q8, k8, v8, ds = _fp8_inputs(1, 2, 2, 150, 16, 620 + int(sigma), sigma)
+            exact, _ = attn_fp8(q8, k8, v8, ds, 0.3, causal)
+            bnd = bound(q8, k8, v8, ds, 0.3, causal)
+            vmax = float(np.abs(torch.from_numpy(v8).view(torch.float8_e4m3fn).double().numpy()).max()) * ds[2]
+            assert bnd.max() <= (2.0 ** -4 + 150 * 2.0 ** -18) * vmax * (1 + 1e-12), "bound above its ceiling"
+            for p_scale in (256.0, 32.0):
+                err = np.abs(model(q8, k8, v8, ds, 0.3, causal, p_scale) - exact)
+                assert np.all(err <= bnd * (1 + 1e-9) + 1e-15), f"rounding exceeds the bound ({p_scale})"
+                assert (err / bnd).max() >= 0.1, "bound vacuous"

@@ -243,3 +243,12 @@ def test_chunk_rejects():
     q, k, v = P._chunk_inputs(1, 4, 2, 9, 5, 4, 545)
     with pytest.raises(ValueError):
         oracle.attn_fwd_chunk(q, k, v, 0.5, True)  # causal chunk longer than its keys
+
+
+# FP8 ([essay] section "FA2/FA3").
+
+def test_fp8_pins():
+    P.pin_e4m3_codebook(oracle.e4m3_decode)
+    P.pin_e4m3_round(oracle.e4m3_round, oracle.e4m3_decode)
+    P.pin_fp8_attention(oracle.attn_fwd_fp8, oracle.attn_fwd_gqa)
+    P.pin_p_rounding_bound(oracle.p_rounding_bound, oracle.attn_fwd_fp8_model, oracle.attn_fwd_fp8)

@@ -291,3 +291,43 @@ def test_chunk_mutant_is_caught(mut):
             ("reassemble", lambda: P.pin_chunked_prefill_reassembles(fwd, oracle.attn_fwd_gqa))]
     with np.errstate(invalid="ignore"):
         assert _fails_some(pins), f"mutant {mut} passed every chunk pin"
+
+
+# ---------------------------------------------------------------------------
+# FP8 code book and rounding
+# ---------------------------------------------------------------------------
+
+def _e4m3_variant(mut):
+    from oracle import fp8 as F
+
+    def decode(codes):
+        c = np.asarray(codes, dtype=np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> 3) & 15
+        m = (c & 7).astype(np.float64)
+        bias = 8.0 if mut == "bias_8" else 7.0
+        sub = (1.0 + m / 8.0) * 2.0 ** (1 - bias) if mut == "no_subnormal" else m / 8.0 * 2.0 ** (1 - bias)
+        val = np.where(e == 0, sub, (1.0 + m / 8.0) * np.exp2(e - bias))
+        val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+        return sign * val
+
+    def rnd(x):
+        if mut == "ties_away":
+            x = np.asarray(x, dtype=np.float64)
+            a = np.abs(x)
+            e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6.0)
+            step = np.exp2(e - 3.0)
+            return np.sign(x) * np.floor(a / step + 0.5) * step
+        return F.e4m3_round(x)
+    return decode, rnd
+
+
+E4M3_MUTANTS = ["bias_8", "no_subnormal", "ties_away"]
+
+
+@pytest.mark.parametrize("mut", E4M3_MUTANTS)
+def test_e4m3_mutant_is_caught(mut):
+    decode, rnd = _e4m3_variant(mut)
+    pins = [("codebook", lambda: P.pin_e4m3_codebook(decode)),
+            ("round", lambda: P.pin_e4m3_round(rnd, oracle.e4m3_decode))]
+    assert _fails_some(pins), f"mutant {mut} passed every E4M3 pin"
