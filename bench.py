@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16/fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA (twice the 16-bit rate)
 METRIC = "attention TFLOP/s (bf16 fwd/bwd) at N=4k-16k; % of MFMA peak; HBM bytes"
 CSRC = os.path.join(ROOT, "io_aware_exact_03_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -422,6 +423,20 @@ def run_legs(torch, fa, fa_synth, dev):
         log(f"[bench] {w.name}: {entry}")
         del q, k, v, o, lse
         torch.cuda.empty_cache()
+
+    # FP8 (E4M3) causal prefill, against the dense fp8 MFMA peak
+    w = fa_synth.FP8_PREFILL
+    q8, k8, v8, ds = fa_synth.make_fp8_inputs(w.B, w.H, w.H, w.N, w.d, seed=w.seed)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o, lse = fa.fwd_fp8(q8, k8, v8, ds, w.scale, w.causal)
+    ms, ms_min = time_reps(lambda: fa.fwd_fp8(q8, k8, v8, ds, w.scale, w.causal, out=o, lse=lse), 20, torch)
+    tf = fwd_flops(w.B, w.H, w.N, w.d, w.causal) / (ms * 1e-3) / 1e12
+    entry = {"fwd_ms": ms, "fwd_ms_min": ms_min, "fwd_tflops": tf, "frac_fp8_mfma_peak": tf / PEAK_FP8_TFLOPS,
+             "alg_bytes": w.B * w.H * (3 * w.N * w.d + 2 * w.N * w.d + 4 * w.N)}
+    legs[w.name] = entry
+    log(f"[bench] {w.name}: {entry}")
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
 
     # grouped-query causal prefill: forward and backward through the grouped
     # entry points, next to the per-head path on K/V repeated G times

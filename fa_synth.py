@@ -80,6 +80,10 @@ GQA_DECODE = Workload("gqa_decode_B1_H64_Hkv8_N32768_d128_bf16", 1, 64, 32768, 1
 GQA_DECODE_RAGGED = Workload("gqa_decode_ragged_B16_H64_Hkv8_N8192_d128_bf16", 16, 64, 8192, 128, "bf16", False,
                              1 / math.sqrt(128), 1008, passes=("decode",), Hkv=8)
 
+# FP8 causal prefill: the causal prefill shape with E4M3 Q, K, V.
+FP8_PREFILL = Workload("fp8_causal_prefill_fwd_B2_H32_N8192_d128_e4m3", 2, 32, 8192, 128, "e4m3", True,
+                       1 / math.sqrt(128), 1010)
+
 # A chunk of 2048 new prompt tokens after 14336 cached ones (keys 16384),
 # same model shape: the causal mask is aligned at the bottom-right corner.
 CHUNK_PREFILL = Workload("gqa_chunk_prefill_B1_H64_Hkv8_Nq2048_Nk16384_d128_bf16", 1, 64, 2048, 128, "bf16", True,
@@ -138,6 +142,21 @@ def make_chunk_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, dtype:
     k = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
     v = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float32).to(DTYPES[dtype])
     return q, k, v
+
+
+def make_fp8_inputs(B: int, H: int, Hkv: int, N: int, d: int, seed: int, sigma: float = 1.0):
+    """FP8 inputs: Q [B,H,N,d], K and V [B,Hkv,N,d] drawn N(0, sigma^2) in
+    fp32, each scaled by its own descale = amax / 448 and rounded to OCP
+    E4M3 codes (torch.float8_e4m3fn, round to nearest even).  Returns the
+    codes as uint8 tensors and the three descale factors.  Draw order: Q, K, V."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    codes, scales = [], []
+    for heads in (H, Hkv, Hkv):
+        x = torch.randn(B, heads, N, d, generator=g, dtype=torch.float32) * sigma
+        ds = float(x.abs().max()) / 448.0
+        codes.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8))
+        scales.append(ds)
+    return codes[0], codes[1], codes[2], tuple(scales)
 
 
 def workload_inputs(w: Workload, with_dout: bool | None = None):

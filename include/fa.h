@@ -227,6 +227,22 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int d, int n_parts);
 int fa_decode_plan(int B, int H, int Hkv, int Nkv, int d, int* n_parts);
 
 /*
+ * FP8 forward ("Flash Attention: IO-awareness principle", section
+ * "FA2/FA3": FA3's FP8 mode), on gfx950's 8-bit matrix product.  q, k, v
+ * hold OCP E4M3 codes (1 byte each; q [B,H,N,d], k and v [B,Hkv,N,d]) with
+ * one dequantisation factor per tensor: value = code value * descale.
+ * Computes fa_fwd_gqa's result for the dequantised inputs: scores and the
+ * softmax statistics in fp32; the weights P (<= 1) are multiplied by 2^8
+ * and rounded to E4M3 for the P V product, so O carries that rounding
+ * (relative 2^-4 per weight in E4M3's normal range); the row sums and lse
+ * use unrounded P.  o: bf16 [B,H,N,d]; lse: float32 [B,H,N], natural log.
+ * d in {64, 128}; descales finite; other checks and errors as fa_fwd_gqa.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, float scale, float q_descale, float k_descale,
+               float v_descale, int causal, void* stream);
+
+/*
  * FlashAttention-1 loop order, kept to measure what the FA2 loop swap buys
  * ("Paper review: FlashAttention ...", Algorithm 1; "Flash Attention:
  * IO-awareness principle", section "FA2/FA3").  Same result as fa_fwd: o

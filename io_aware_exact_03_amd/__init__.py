@@ -3,5 +3,5 @@ backward plus a naive three-kernel baseline, all hand-written HIP behind the
 C ABI of include/fa.h.  torch is used only for device memory and streams."""
 from .ops import (  # noqa: F401
     DTYPE_CODES, bwd, bwd_gqa, bwd_stage, causal_stages, decode, decode_pieces, decode_plan, decode_workspace_bytes,
-    fa1_state, fa1_workspace_bytes, fwd, fwd_chunk, fwd_fa1, fwd_gqa, fwd_tile, kv_head, naive_fwd,
+    fa1_state, fa1_workspace_bytes, fwd, fwd_chunk, fwd_fa1, fwd_fp8, fwd_gqa, fwd_tile, kv_head, naive_fwd,
     naive_workspace_bytes)

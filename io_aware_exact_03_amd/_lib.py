@@ -27,6 +27,7 @@ SIGNATURES = {
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "fa_decode_plan": (_i, [_i, _i, _i, _i, _i, _ip]),
+    "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp]),
     "fa_fwd_fa1": (_i, [_vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_fa1_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_naive_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]),

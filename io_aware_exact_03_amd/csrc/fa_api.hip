@@ -233,6 +233,22 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return hip_status(fa::launch_decode(a));
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+               int d, float scale, float q_descale, float k_descale, float v_descale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_ARG;
+  const int st = check_shape(B, H, N, d, FA_BF16, causal, scale);  // bf16 output; 1-byte inputs are smaller
+  if (st != FA_OK) return st;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
+  if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::Fp8Args a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.G = H / Hkv; a.N = N; a.d = d; a.causal = causal != 0;
+  a.scale = scale; a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_fwd_fp8(a));
+}
+
 size_t fa_fa1_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;

@@ -1,0 +1,350 @@
+// fa_fp8.hip -- forward with FP8 (OCP E4M3) Q, K, V on the gfx950 8-bit
+// matrix product v_mfma_f32_32x32x64_f8f6f4, whose dense rate is twice the
+// 16-bit one.
+//
+// Pages cited: "Flash Attention: IO-awareness principle" (hrletsgo.me),
+// section "FA2/FA3" (FA3's FP8 mode); "Triton 06: Flash Attention v2"
+// (wonbeomjang.kr), Improvements 1-3 (un-scaled accumulator, exp2 with
+// log2(e) folded into the scale, causal blocks split into unmasked and
+// masked ones).
+//
+// Inputs are FP8 codes with one dequantisation factor per tensor (value =
+// code * descale).  The algorithm is the fused forward's: per query block
+// (8 waves x 32 queries) K and V tiles of 64 keys stream through an LDS
+// ring; per tile each wave computes S^T = K Q^T (lane = query, registers =
+// keys), an exact running max, P = exp2(x - m) in fp32, the row sum of P in
+// fp32, then P * 2^8 rounded to E4M3 as the B operand of O^T += V^T P^T.
+// The 2^8 keeps weights down to 2^-17 in E4M3's range; it and the V factor
+// are divided out once at the end.
+//
+// Operand layouts of the 8-bit product (measured on the chip): lane (r, g)
+// of an operand holds row (or column) r = lane % 32 and 32 bytes whose
+// contraction index is the same for both operands at the same (g, byte).
+// So the score product reads 32 consecutive bytes of a K row (d = 64 s +
+// 32 g + byte) against the same bytes of Q; the PV product pairs byte
+// 16 b + r of lane (n, g) with key 32 b + 8 (r / 4) + 4 g + r % 4 -- the
+// keys of register r of score block b -- so the packed P needs no shuffle,
+// and V^T's matching bytes come from ds_read_b64_tr_b8: element e of lane
+// i in a 16-lane group is byte i % 8 of the 8 bytes addressed by lane
+// 2 e + i / 8 of the group.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+#include "fa_plan.hpp"
+
+namespace fa {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mma_fp8(const v8i& a, const v8i& b, const f32x16& c) {
+  // formats 0/0 = E4M3 for both operands, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D>
+struct Fp8 {
+  static constexpr int NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 64, NBUF = 4;
+  static constexpr int DS = D / 64;        // 64-byte contraction steps of the score product
+  static constexpr int DB = D / 32;        // 32-wide d blocks of O
+  static constexpr int CPR = D / 16;       // 16-byte chunks per row
+  static constexpr int RPP = 1024 / D;     // rows per 1 KB wave load
+  static constexpr int PPT = BN / RPP;     // 1 KB pieces per K (or V) tile
+  static constexpr int LPW = 2 * PPT / NW; // loads per wave per tile
+  static_assert(LPW >= 1 && LPW * NW == 2 * PPT && (NBUF - 2) * LPW < 64, "tile loads");
+};
+
+// Stored 16-byte chunk of logical chunk c in row r.  D = 128: the two low
+// bits of (r >> 1) & 7 swapped; D = 64: (r >> 2) & 3.  Both keep the 32-byte
+// row reads of K and the transposing 8-byte reads of V free of bank
+// conflicts.
+template <int D>
+__device__ __forceinline__ int fp8_swz(int r) {
+  if (D == 128) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+  }
+  return (r >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int fp8_off(int row, int chunk) {  // byte offset of (row, logical chunk)
+  return row * D + 16 * (chunk ^ fp8_swz<D>(row));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict__ qg, const uint8_t* __restrict__ kg,
+                                                      const uint8_t* __restrict__ vg, uint16_t* __restrict__ og,
+                                                      float* __restrict__ lseg, int N, int n_qblk, int BH, int G,
+                                                      float qk_scale, float o_scale, uint32_t qsign) {
+  using C = Fp8<D>;
+  constexpr int BN = C::BN, DS = C::DS, DB = C::DB;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[C::NBUF][BN * D];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[C::NBUF][BN * D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+
+  auto block = [&](int bh, int qblk) __attribute__((always_inline)) {
+    const size_t head = (size_t)bh * N * D;
+    const size_t kvhead = (size_t)kv_head_of(bh, G) * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D;
+    const rsrc_t qrs = make_rsrc(qg + head, head_bytes);
+    const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
+    const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
+    const int q0 = qblk * C::BM;
+    const int qw0 = q0 + 32 * wave;
+    const int query = qw0 + n;
+    const bool wave_live = qw0 < N;
+
+    // Q fragments: lane (n, g), step s: bytes 64 s + 32 g .. + 32 of row `query`.
+    v8i qf[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const uint4 a = load16(qrs, (uint32_t)query * D + 64 * s + 32 * g);
+      const uint4 b = load16(qrs, (uint32_t)query * D + 64 * s + 32 * g + 16);
+      // a negative score factor flips Q's sign bits, so qk_scale >= 0
+      qf[s] = v8i{(int)(a.x ^ qsign), (int)(a.y ^ qsign), (int)(a.z ^ qsign), (int)(a.w ^ qsign),
+                  (int)(b.x ^ qsign), (int)(b.y ^ qsign), (int)(b.z ^ qsign), (int)(b.w ^ qsign)};
+    }
+
+    // Tiles this workgroup reads, and the last one each wave needs.
+    const int n_tiles = (N + BN - 1) / BN;
+    const int last_row = min(q0 + C::BM, N) - 1;
+    const int j_end = CAUSAL ? min(n_tiles, last_row / BN + 1) : n_tiles;
+    const int key_lim = CAUSAL ? min(query + 1, N) : N;
+
+    // Tile j into ring slot sl: LDS row r, stored chunk c holds global chunk
+    // c ^ fp8_swz(r) of key j BN + r.  Rows past N read as zeros.
+    auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+      const int lrow = lane / C::CPR;
+#pragma unroll
+      for (int e = 0; e < C::LPW; ++e) {
+        const int t = wave * C::LPW + e;
+        const int p = t % C::PPT;
+        const int row = p * C::RPP + lrow;
+        const int ch = (lane % C::CPR) ^ fp8_swz<D>(row);
+        const uint32_t off = (uint32_t)(j * BN + row) * D + 16 * ch;
+        if (t < C::PPT) load_lds16(krs, &k_lds[sl][p * C::RPP * D], off);
+        else load_lds16(vrs, &v_lds[sl][p * C::RPP * D], off);
+      }
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;  // base-2 running max; this half's share of l
+
+    // V^T fragment of d block db (A operand of O^T += V^T P^T): four
+    // transposing reads, read t giving bytes 8 t .. 8 t + 7, i.e. keys
+    // 32 (t / 2) + 16 (t % 2) + 8 (e / 4) + 4 g + e % 4, e = 0..7.
+    const int tg = lane >> 4, tj = lane & 15;  // 16-lane group, lane in group
+    auto vfrag = [&](const uint8_t* vt, int db) __attribute__((always_inline)) {
+      v8i r;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = tj >> 1;
+        const int row = 32 * (t >> 1) + 16 * (t & 1) + 8 * (e >> 2) + 4 * g + (e & 3);
+        const int chunk = 2 * db + (tg & 1);
+        const uint8_t* p = vt + fp8_off<D>(row, chunk) + 8 * (tj & 1);
+        const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t*)(p));
+        r[2 * t] = x[0];
+        r[2 * t + 1] = x[1];
+      }
+      return r;
+    };
+
+    // Raw scores S^T (before the scale) of the two 32-key blocks of the
+    // tile in slot sl; register r of block b is key 32 b + 8 (r / 4) + 4 g
+    // + r % 4 of the tile.
+    auto s_gemm = [&](int sl, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+      const uint8_t* kt = k_lds[sl];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        sc[b] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const int row = 32 * b + n;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(kt + fp8_off<D>(row, 4 * s + 2 * g));
+          const uint4 x1 = *reinterpret_cast<const uint4*>(kt + fp8_off<D>(row, 4 * s + 2 * g + 1));
+          const v8i a = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          sc[b] = mma_fp8(a, qf[s], sc[b]);
+        }
+      }
+    };
+
+    // Softmax step of tile j: the running max (qk_scale >= 0, so the max of
+    // the raw scores gives it), a rescale when some row's max grew, the
+    // fp32 row sum, and P 2^8 in E4M3 (byte 16 b + r = register r of block
+    // b).  MASK: some key of the tile lies past some lane's limit; those
+    // weights are set to zero (not through an infinite score, which a zero
+    // qk_scale would turn into NaN).
+    auto softmax = [&](f32x16 (&sc)[2], int j, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      auto visible = [&](int b, int r) { return !MASK || j * BN + 32 * b + 8 * (r / 4) + 4 * g + (r % 4) < key_lim; };
+      float mx = kNegInf;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, visible(b, r) ? sc[b][r] : kNegInf);
+      mx = halves_max(mx);
+      mx = mx == kNegInf ? kNegInf : mx * qk_scale;
+      const float m_new = fmaxf(m_run, mx);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {  // some row's max grew: rescale
+        const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+      }
+      // P 2^8 = exp2(x qk_scale - (m - 8)): the 2^8 rides in the exponent,
+      // and l accumulates P 2^8 too.
+      const float base = (m_run == kNegInf ? 0.f : m_run) - 8.f;
+      v8i pk;
+      float psum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int b = w / 4, r = 4 * (w % 4);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = fast_exp2(__builtin_fmaf(sc[b][r + i], qk_scale, -base));
+          if (MASK && !visible(b, r + i)) p[i] = 0.f;
+        }
+        psum += (p[0] + p[1]) + (p[2] + p[3]);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        pk[w] = word;
+      }
+      l_run += psum;
+      return pk;
+    };
+
+    // Ring and pipeline.  Iteration j computes the scores of tile j + 1, the
+    // softmax of tile j (already scored) and tile j's PV product, so the
+    // score products overlap the vector work.  Its barrier makes tile j + 1
+    // visible (tile j + 2 may still load) and frees the slot of tile j - 1,
+    // which receives tile j + 3.
+    static_assert(C::NBUF == 4, "ring of four tiles, loads three ahead of the scores");
+#pragma unroll
+    for (int j = 0; j < C::NBUF - 1; ++j)
+      if (j < j_end) issue(j, j);
+    // prologue: tile 0 in LDS, its scores
+    if (j_end > 2) lds_barrier<2 * C::LPW>();
+    else if (j_end > 1) lds_barrier<C::LPW>();
+    else lds_barrier<0>();
+    f32x16 sA[2], sB[2];
+    s_gemm(0, sA);
+    // One iteration; the loop runs two per trip so the score registers
+    // alternate without copies.
+    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto mask_tag) __attribute__((always_inline)) {
+      // tile j + 1 must be in LDS: the loads still allowed in flight are
+      // those of tile j + 2
+      if (j + 1 < j_end) {
+        if (j + 2 < j_end) lds_barrier<C::LPW>();
+        else lds_barrier<0>();
+      }
+      if (j + 3 < j_end) issue(j + 3, (j + 3) % C::NBUF);
+      // Every wave runs every tile of the block: a tile wholly past a
+      // wave's causal limit is fully masked (P = 0), which costs less than
+      // branching around the accumulators.
+      if (j + 1 < j_end) s_gemm((j + 1) % C::NBUF, nxt);
+      // V^T fragments: the first PF are read before the vector work, which
+      // hides their latency (all of them would not fit in registers at
+      // d = 128), the rest behind the first PV products.
+      constexpr int PF = DB > 2 ? 2 : DB;
+      v8i vf[DB];
+      const uint8_t* vt = v_lds[j % C::NBUF];
+#pragma unroll
+      for (int db = 0; db < PF; ++db) vf[db] = vfrag(vt, db);
+      const v8i pk = softmax(cur, j, mask_tag);
+#pragma unroll
+      for (int db = PF; db < DB; ++db) vf[db] = vfrag(vt, db);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mma_fp8(vf[db], pk, oacc[db]);
+    };
+    // Tiles every key of which every query of the block sees run without
+    // the mask; the rest (the diagonal tiles, the sequence tail) with it.
+    // Each range has one code path, so the accumulators need no merging.
+    auto run = [&](int j0, int j1, auto mask_tag) __attribute__((always_inline)) {
+      int j = j0;
+      for (; j + 1 < j1; j += 2) {
+        step(j, sA, sB, mask_tag);
+        step(j + 1, sB, sA, mask_tag);
+      }
+      if (j < j1) {
+        step(j, sA, sB, mask_tag);
+        sA[0] = sB[0];
+        sA[1] = sB[1];
+      }
+    };
+    const int j_full = min(j_end, CAUSAL ? q0 / BN : N / BN);
+    run(0, j_full, std::false_type{});
+    run(j_full, j_end, std::true_type{});
+
+    // O = acc * (V descale / 2^8) / l, LSE = (m + log2 l) ln 2.
+    const float l_tot = halves_sum(l_run);  // sum of P 2^8
+    const float inv = o_scale / l_tot;
+    if (wave_live && query < N) {
+      uint16_t* orow = og + head + (size_t)query * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x16& v = oacc[db];
+          const uint2 w = make_uint2(pack2(BF16{}, v[4 * rq + 0] * inv, v[4 * rq + 1] * inv),
+                                     pack2(BF16{}, v[4 * rq + 2] * inv, v[4 * rq + 3] * inv));
+          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
+        }
+      if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot) - 8.f) * kLn2;
+    }
+  };
+
+  // Persistent loop over equal-cost items, as the 16-bit forward.
+  const int per_head = items_per_head(n_qblk, CAUSAL);
+  const int n_items = BH * per_head;
+  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
+    int lo, hi;
+    const int nb = item_blocks(L % per_head, n_qblk, CAUSAL, &lo, &hi);
+    for (int t = 0; t < nb; ++t) {
+      block(L / per_head, t + 1 < nb ? hi : lo);  // the heavier block of a causal pair first
+      __syncthreads();                            // the next block's loads reuse the ring
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const Fp8Args& a) {
+  using C = Fp8<D>;
+  const int n_qblk = (a.N + C::BM - 1) / C::BM;
+  const long long items = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = (int)(items < cus ? items : cus);
+  const float f = a.scale * a.q_descale * a.k_descale;
+  const float qk_scale = fabsf(f) * kLog2eHost;
+  const uint32_t qsign = f < 0.f ? 0x80808080u : 0u;
+  const float o_scale = a.v_descale;  // l and the PV products both carry the 2^8
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
+                     static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                     static_cast<const uint8_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblk, a.BH, a.G,
+                     qk_scale, o_scale, qsign);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Args& a) {
+  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+}
+
+}  // namespace fa

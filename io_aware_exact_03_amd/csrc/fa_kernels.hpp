@@ -93,11 +93,24 @@ struct Fa1Args {
   hipStream_t stream;
 };
 
+struct Fp8Args {
+  const void* q;   // E4M3 codes [BH, N, d]
+  const void* k;   // [BH / G, N, d]
+  const void* v;
+  void* o;         // bf16 [BH, N, d]
+  float* lse;      // [BH, N]
+  int BH, G, N, d;
+  bool causal;
+  float scale, q_descale, k_descale, v_descale;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0 = all three launches in order; 1 = Delta, 2 = dK/dV, 3 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, int stage);
 hipError_t launch_naive(const NaiveArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_fa1(const Fa1Args& a);
+hipError_t launch_fwd_fp8(const Fp8Args& a);
 
 }  // namespace fa

@@ -206,6 +206,30 @@ def decode_pieces(ws, B: int, H: int, Hkv: int, d: int, n_parts: int):
     return o, l
 
 
+def fwd_fp8(q8, k8, v8, descales, scale: float, causal: bool, out=None, lse=None):
+    """FP8 forward: q8 [B,H,N,d], k8 and v8 [B,Hkv,N,d] hold OCP E4M3 codes
+    (uint8 or torch.float8_e4m3fn), descales = (q, k, v) factors with value =
+    code * factor.  Returns (O bf16 [B,H,N,d], LSE float32 [B,H,N])."""
+    ts = [t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q8, k8, v8)]
+    for t in ts:
+        if t.dtype != torch.uint8 or t.dim() != 4 or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("fp8 inputs must be contiguous 4-d uint8 / float8_e4m3fn tensors on a HIP device")
+    q8, k8, v8 = ts
+    B, H, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if k8.shape != v8.shape or k8.shape[0] != B or k8.shape[2:] != q8.shape[2:] or H % Hkv != 0:
+        raise ValueError(f"k, v shape {tuple(k8.shape)} does not group q shape {tuple(q8.shape)}")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    dq, dk, dv = (float(x) for x in descales)
+    st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                Hkv, N, d, float(scale), dq, dk, dv, int(bool(causal)), _stream(q8))
+    _lib.check(st, "fa_fwd_fp8")
+    return out, lse
+
+
 def fa1_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.load().fa_fa1_workspace_bytes(B, H, N, d))
 

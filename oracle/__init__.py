@@ -43,6 +43,6 @@ from .attention import (  # noqa: F401
 )
 from .gqa import attn_bwd_gqa, attn_fwd_gqa, attn_fwd_rows_gqa  # noqa: F401
 from .fp8 import (  # noqa: F401
-    attn_fwd_fp8, attn_fwd_fp8_model, dequantize, e4m3_decode, e4m3_round, p_rounding_bound)
+    attn_fwd_fp8, attn_fwd_fp8_model, attn_fwd_fp8_rows, dequantize, e4m3_decode, e4m3_round, p_rounding_bound)
 from .chunk import attn_fwd_chunk, attn_fwd_chunk_rows  # noqa: F401
 from .decode import attn_decode, decode_partials, decode_split_merge, merge_partials, split_bounds  # noqa: F401

@@ -106,3 +106,29 @@ def attn_fwd_fp8_model(q8, k8, v8, descales, scale: float, causal: bool, p_scale
             pq = e4m3_round(p * p_scale) / p_scale
             out[b, h] = (pq @ v[b, g]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+def attn_fwd_fp8_rows(q8, k8, v8, descales, scale: float, causal: bool, rows):
+    """O, LSE and the P-rounding bound of selected (b, h, i) rows, one at a
+    time (full-size sampled checks); same definitions as attn_fwd_fp8 and
+    p_rounding_bound."""
+    dq, dk, dv = descales
+    H, Hkv = q8.shape[1], k8.shape[1]
+    G = H // Hkv
+    rows = list(rows)
+    d = v8.shape[3]
+    o, lse, bnd = np.empty((len(rows), d)), np.empty(len(rows)), np.empty((len(rows), d))
+    for n, (b, h, i) in enumerate(rows):
+        g = h // G
+        n_keys = i + 1 if causal else k8.shape[2]
+        q = dequantize(q8[b, h, i], dq)
+        k = dequantize(k8[b, g, :n_keys], dk)
+        v = dequantize(v8[b, g, :n_keys], dv)
+        s = scale * (k @ q)
+        m = s.max()
+        p = np.exp(s - m)
+        l = p.sum()
+        o[n] = (p @ v) / l
+        lse[n] = m + math.log(l)
+        bnd[n] = (2.0 ** -4 * (p @ np.abs(v)) + 2.0 ** -18 * np.abs(v).sum(axis=0)) / l
+    return o, lse, bnd

@@ -252,3 +252,16 @@ def test_fp8_pins():
     P.pin_e4m3_round(oracle.e4m3_round, oracle.e4m3_decode)
     P.pin_fp8_attention(oracle.attn_fwd_fp8, oracle.attn_fwd_gqa)
     P.pin_p_rounding_bound(oracle.p_rounding_bound, oracle.attn_fwd_fp8_model, oracle.attn_fwd_fp8)
+
+
+def test_fp8_rows_helper():
+    q8, k8, v8, ds = P._fp8_inputs(2, 4, 2, 19, 8, 630)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_fp8(q8, k8, v8, ds, 0.4, causal)
+        bnd = oracle.p_rounding_bound(q8, k8, v8, ds, 0.4, causal)
+        rows = [(0, 0, 0), (1, 3, 18), (0, 2, 7)]
+        ro, rl, rb = oracle.attn_fwd_fp8_rows(q8, k8, v8, ds, 0.4, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            np.testing.assert_allclose(ro[n], o[b, h, i], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(rl[n], lse[b, h, i], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(rb[n], bnd[b, h, i], rtol=1e-12, atol=1e-15)
