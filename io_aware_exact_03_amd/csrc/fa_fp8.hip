@@ -45,6 +45,12 @@ __device__ __forceinline__ f32x16 mma_fp8(const v8i& a, const v8i& b, const f32x
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Headroom of the lazy reference, log2 units: after a raise the largest
+// weight is 2^(8 - kFp8Lift), and scores may grow by kFp8Lift + log2(448 /
+// 256) before the next raise.  Weights below 2^-9 / 2^8 of the reference
+// (2^(-17 + kFp8Lift) of the row max) round to zero.
+constexpr float kFp8Lift = 2.f;
+
 template <int D>
 struct Fp8 {
   static constexpr int NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 64, NBUF = 4;
@@ -176,24 +182,55 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
       }
     };
 
-    // Softmax step of tile j: the running max (qk_scale >= 0, so the max of
-    // the raw scores gives it), a rescale when some row's max grew, the
-    // fp32 row sum, and P 2^8 in E4M3 (byte 16 b + r = register r of block
-    // b).  MASK: some key of the tile lies past some lane's limit; those
-    // weights are set to zero (not through an infinite score, which a zero
-    // qk_scale would turn into NaN).
+    // Softmax step of tile j with a lazy reference.  The weights are
+    // P 2^8 = exp2(x qk_scale - (m - 8)) against a reference m that is only
+    // raised when some weight would leave E4M3's range (> 448): the common
+    // path computes no row max and never rescales.  An overflow shows as a
+    // NaN code (E4M3 has no infinity; the conversion does not saturate) and
+    // is tested on the packed bytes.  Then (rare; always on a row's first
+    // tile, where m is -inf) m is raised to the tile's row max plus
+    // kFp8Lift, O and l are rescaled and the weights redone.  The lift keeps
+    // later, slightly larger scores in range.  qk_scale >= 0, so the max of
+    // the raw scores gives the max.  MASK: keys past a lane's limit get
+    // weight zero (set directly; an infinite score times a zero qk_scale
+    // would be NaN).
     auto softmax = [&](f32x16 (&sc)[2], int j, auto mask_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       auto visible = [&](int b, int r) { return !MASK || j * BN + 32 * b + 8 * (r / 4) + 4 * g + (r % 4) < key_lim; };
-      float mx = kNegInf;
+      v8i pk;
+      float psum = 0.f;
+      uint32_t ovf = 0;
+      auto weights = [&]() __attribute__((always_inline)) {
+        const float base = m_run - 8.f;  // -inf before the first raise: every weight overflows
+        psum = 0.f;
+        ovf = 0;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int w = 0; w < 8; ++w) {
+          const int b = w / 4, r = 4 * (w % 4);
+          float p[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, visible(b, r) ? sc[b][r] : kNegInf);
-      mx = halves_max(mx);
-      mx = mx == kNegInf ? kNegInf : mx * qk_scale;
-      const float m_new = fmaxf(m_run, mx);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {  // some row's max grew: rescale
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(__builtin_fmaf(sc[b][r + i], qk_scale, -base));
+            if (MASK && !visible(b, r + i)) p[i] = 0.f;
+          }
+          psum += (p[0] + p[1]) + (p[2] + p[3]);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+          pk[w] = word;
+          // a byte whose low seven bits are all set is a NaN code
+          ovf |= (((uint32_t)word & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+        }
+      };
+      weights();
+      if (__builtin_amdgcn_ballot_w64(ovf != 0) != 0) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, visible(b, r) ? sc[b][r] : kNegInf);
+        mx = halves_max(mx);
+        mx = mx == kNegInf ? kNegInf : mx * qk_scale;
+        const float m_new = fmaxf(m_run, mx == kNegInf ? kNegInf : mx + kFp8Lift);
         const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -201,25 +238,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         m_run = m_new;
-      }
-      // P 2^8 = exp2(x qk_scale - (m - 8)): the 2^8 rides in the exponent,
-      // and l accumulates P 2^8 too.
-      const float base = (m_run == kNegInf ? 0.f : m_run) - 8.f;
-      v8i pk;
-      float psum = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int b = w / 4, r = 4 * (w % 4);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(__builtin_fmaf(sc[b][r + i], qk_scale, -base));
-          if (MASK && !visible(b, r + i)) p[i] = 0.f;
-        }
-        psum += (p[0] + p[1]) + (p[2] + p[3]);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        pk[w] = word;
+        weights();
       }
       l_run += psum;
       return pk;

@@ -46,12 +46,13 @@ def p_rounding_bound(q8, k8, v8, descales, scale: float, causal: bool):
     """Per-element bound on |O - O_exact| from rounding each weight.
 
     Let P_j = exp(s_j - m) with m the row max and l = sum_j P_j.  A kernel
-    that rounds a * 2^8 * P_j to E4M3 for any a >= 1 (its running reference
-    may sit below the row max) and multiplies back exactly changes P_j by at
-    most 2^-4 P_j (half the 3-bit mantissa spacing) or, below the normal
-    range (2^-6), by at most 2^-10 / 2^8 = 2^-18.  With O computed as
+    that rounds a * 2^8 * P_j to E4M3 and multiplies back exactly, with a
+    reference that lies at most 2 log2 units above the row max (a >= 2^-2;
+    a reference below the max, a > 1, only helps), changes P_j by at most
+    2^-4 P_j (half the 3-bit mantissa spacing) or, below the normal range
+    (2^-6), by at most 2^-10 / (2^8 a) <= 2^-16.  With O computed as
     sum_j P~_j V_j / l, the error in column c is at most
-    (2^-4 sum_j P_j |V_jc| + 2^-18 sum_j |V_jc|) / l.  Returns that array
+    (2^-4 sum_j P_j |V_jc| + 2^-16 sum_j |V_jc|) / l.  Returns that array
     [B,H,N,d]."""
     dq, dk, dv = descales
     q, k, v = dequantize(q8, dq), dequantize(k8, dk), dequantize(v8, dv)
@@ -68,7 +69,7 @@ def p_rounding_bound(q8, k8, v8, descales, scale: float, causal: bool):
             l = p.sum(axis=1, keepdims=True)
             av = np.abs(v[b, g])
             vis = np.isfinite(s).astype(np.float64)
-            out[b, h] = (2.0 ** -4 * (p @ av) + 2.0 ** -18 * (vis @ av)) / l
+            out[b, h] = (2.0 ** -4 * (p @ av) + 2.0 ** -16 * (vis @ av)) / l
     return out
 
 
@@ -130,5 +131,5 @@ def attn_fwd_fp8_rows(q8, k8, v8, descales, scale: float, causal: bool, rows):
         l = p.sum()
         o[n] = (p @ v) / l
         lse[n] = m + math.log(l)
-        bnd[n] = (2.0 ** -4 * (p @ np.abs(v)) + 2.0 ** -18 * np.abs(v).sum(axis=0)) / l
+        bnd[n] = (2.0 ** -4 * (p @ np.abs(v)) + 2.0 ** -16 * np.abs(v).sum(axis=0)) / l
     return o, lse, bnd
