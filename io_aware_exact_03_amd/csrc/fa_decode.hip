@@ -1,5 +1,6 @@
 // fa_decode.hip -- decoding: the newest query of every head against its
-// K/V cache, the keys split across workgroups, the partial results merged.
+// K/V cache, the keys shared out evenly among workgroups, the pieces of
+// heads cut between workgroups merged.
 //
 // Pages cited: "Flash Attention -- five lessons converging into 80 lines"
 // (brianyu43.github.io), "LLM-serving translation" (in decoding Q has one
@@ -8,7 +9,7 @@
 // few tiles to fill the GPU, hence kernels that split the keys); "Paper
 // review: FlashAttention ... with IO-Awareness" (osehyeon.github.io), the
 // softmax decomposition under "Tiling" (max and normaliser of a
-// concatenation from those of its parts), which merges the splits.
+// concatenation from those of its parts), which merges the pieces.
 //
 // Decoding reads every cached key and value once and does 4 d flops per key
 // per query head, so it is bound by HBM bandwidth, not by the matrix cores.
@@ -17,7 +18,10 @@
 // 32 columns of one MFMA product (padded with zeros), so each K/V element
 // is read from HBM once for the whole group.
 //
-// Split kernel, one workgroup per (batch, K/V head, 32 query heads, split):
+// Work split (fa_plan.hpp): the key tiles of every unit (batch, K/V head,
+// block of 32 query heads) are laid end to end and cut into as many equal
+// ranges as there are workgroups, so ragged batches stay balanced.
+// Split kernel, one workgroup per range, walking its range unit by unit:
 //   * K and V tiles of BN = 32 NW keys go from HBM straight into LDS
 //     (buffer_load ... lds, 1 KB per wave instruction, rows swizzled as in
 //     the forward), NBUF - 1 tiles ahead; the buffer range of the head ends
@@ -27,12 +31,12 @@
 //     v_mfma_f32_32x32x16 (lane = query head, registers = keys), an online
 //     softmax in base 2 per wave, O^T += V^T P^T with V^T from transposing
 //     LDS reads;
-//   * at the end the waves' (m, l, O) are combined through LDS and the
-//     split's O (normalised) and LSE are written: to the outputs when there
-//     is one split, else to the caller's workspace.
-// Merge kernel (more than one split), one wave per query head: with
-// M = max_s LSE_s and w_s = exp(LSE_s - M), LSE = M + ln sum w_s and
-// O = sum w_s O_s / sum w_s.
+//   * at the end of a unit's piece the waves' (m, l, O) are combined through
+//     LDS; a whole unit is written to the outputs, a piece to its workspace
+//     slot.
+// Merge kernel (more than one range), one workgroup per (unit, query
+// column) that was cut: with M = max_s LSE_s and w_s = exp(LSE_s - M),
+// LSE = M + ln sum w_s and O = sum w_s O_s / sum w_s.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,7 +57,7 @@ struct Dec {
   static constexpr int LPW = 2 * PPT / NW;      // loads per wave per tile (K and V)
   static constexpr int EPT = D / (2 * NW);      // output elements per thread in the combine
   static constexpr int OROW = D + 1;            // padded fp32 row of a wave's O in LDS
-  static_assert(kDecodeTileKeys % BN == 0, "whole tiles per split");
+  static_assert(kDecodeTileKeys % BN == 0, "whole tiles per plan tile");
   static_assert(LPW * NW == 2 * PPT && (NBUF - 2) * LPW < 64, "load split / vmcnt range");
   static_assert(EPT % 8 == 0, "combine vector width");
   static_assert(NW * 32 * (OROW + 2) * 4 <= NBUF * 2 * BN * D * 2, "combine fits in the ring");

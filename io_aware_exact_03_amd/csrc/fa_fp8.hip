@@ -12,10 +12,10 @@
 // code * descale).  The algorithm is the fused forward's: per query block
 // (8 waves x 32 queries) K and V tiles of 64 keys stream through an LDS
 // ring; per tile each wave computes S^T = K Q^T (lane = query, registers =
-// keys), an exact running max, P = exp2(x - m) in fp32, the row sum of P in
-// fp32, then P * 2^8 rounded to E4M3 as the B operand of O^T += V^T P^T.
-// The 2^8 keeps weights down to 2^-17 in E4M3's range; it and the V factor
-// are divided out once at the end.
+// keys), P 2^8 = exp2(x - m + 8) in fp32 against a lazily raised reference
+// m, the row sum in fp32, and P 2^8 rounded to E4M3 as the B operand of
+// O^T += V^T P^T.  The 2^8 keeps small weights in E4M3's range; it cancels
+// between O's accumulator and the row sum.
 //
 // Operand layouts of the 8-bit product (measured on the chip): lane (r, g)
 // of an operand holds row (or column) r = lane % 32 and 32 bytes whose
