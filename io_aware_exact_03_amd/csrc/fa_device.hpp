@@ -66,6 +66,15 @@ __device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
   f16x2 v = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
+// acc + a + b for a softmax row sum, where w = pack2(a, b).  fp16: one dot
+// product of the packed pair with (1, 1), i.e. the sum of the rounded
+// values (relative error at most 2^-11 each, inside the LSE bound of 1e-3
+// even when one weight carries the whole row).  bf16 rounding (2^-9) would
+// not be, so there the fp32 values are added.
+__device__ __forceinline__ float add_pair(BF16, uint32_t, float a, float b, float acc) { return acc + a + b; }
+__device__ __forceinline__ float add_pair(F16, uint32_t w, float, float, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+}
 __device__ __forceinline__ float lo16(BF16, uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(BF16, uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float lo16(F16, uint32_t w) {

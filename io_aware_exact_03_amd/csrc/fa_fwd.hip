@@ -12,29 +12,29 @@
 // LSE = (m + log2 l) * ln 2 is stored for the backward pass.
 //
 // gfx950 layout choices (not from the pages, which target NVIDIA parts):
-// * Each wave owns QB column blocks of 32 queries.  Computing S^T (keys x
-//   queries) puts every lane on ONE query, so the row max and row sum are
-//   in-lane plus one exchange of the two 32-lane halves, and the softmax
-//   correction alpha is lane-local for the O^T accumulator as well.
-// * The fp32 S^T accumulator registers, converted to 16-bit, are directly
-//   the B operand of the O^T product: no LDS round trip for P.  That product
-//   needs V with keys contiguous per lane, so V is stored transposed in LDS,
-//   with the keys of each 16-key group permuted (bits 2 and 3 of the key
-//   index swapped) to match the accumulator's key order.
-// * K (row-major, 16-byte row padding) and V^T (padded rows) sit in three
-//   LDS buffers: the block being consumed, the next one (whose first
-//   S product starts inside the current block's last step), and the one
-//   after, whose global loads are in flight meanwhile; one barrier per block.
+// * Each wave owns 32 queries.  Computing S^T (keys x queries) puts every
+//   lane on ONE query, so the softmax statistics are in-lane plus one
+//   exchange of the two 32-lane halves, and the correction alpha is
+//   lane-local for the O^T accumulator as well.
+// * The fp32 S^T accumulator registers, rounded to 16 bits, are directly the
+//   B operand of O^T += V^T P^T: no LDS round trip for P.  V stays row-major
+//   in LDS and reaches that product through transposing reads
+//   (ds_read_b64_tr_b16).
+// * K and V tiles go from global memory straight into LDS (no registers),
+//   swizzled row-major, through a ring of five tile buffers, three tiles
+//   ahead; one barrier per tile.  The ring is laid out so that nearly every
+//   LDS read takes its address from a per-lane base plus an immediate.
 // * Software pipeline inside each wave, per 32-key sub-block u: the S^T
-//   product of sub-block u+1 is issued in chunks interleaved with the
-//   exponentials of sub-block u, and the PV product of u is interleaved with
-//   the row max of u+1, so the matrix cores and the vector/transcendental
-//   units overlap within one wave; eight waves (two per SIMD) cover the rest.
-// * The reference max is raised lazily (only when a sub-block's max exceeds
-//   it by more than a fixed slack), so the O rescale is rare; exact, since
-//   O, l and the LSE all use the same reference.
-// * Workgroups are renumbered so each XCD (own L2) works on whole heads,
-//   heaviest causal query blocks first.
+//   product of u+1 and the PV product of u-1 are issued slot by slot with
+//   the exponentials of u spread between them, so the matrix cores and the
+//   vector/transcendental units overlap within one wave; eight waves (two
+//   per SIMD) cover the rest.
+// * The reference max is raised lazily (only when a weight would exceed
+//   2^8), so the common path computes no row max and the O rescale is rare;
+//   exact, since O, l and the LSE all use the same reference.
+// * A persistent grid walks equal-cost work items (a causal item pairs a
+//   heavy query block with a light one of the same head); each XCD (own L2)
+//   works on a contiguous range of items, i.e. on shared heads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,9 +51,10 @@ namespace fa {
 // ===========================================================================
 // Workgroup: 8 waves x 32 queries (BM = 256, two waves per SIMD).  K/V tiles
 // of BN keys go from global memory straight into LDS (no registers), row-major
-// with the XOR chunk swizzle, into four buffers: the tile being consumed, the
-// next one (whose first score product starts in the current tile's last
-// step) and two in flight.  K feeds S^T = K Q^T with 16-byte row reads; V
+// with the XOR chunk swizzle, into five buffers: the previous tile (whose V
+// the first step still reads), the tile being consumed, the next one (whose
+// first score product starts in the current tile's last step) and two in
+// flight.  K feeds S^T = K Q^T with 16-byte row reads; V
 // feeds O^T += V^T P^T through transposing reads (ds_read_b64_tr_b16).
 template <typename T, int D, int BN, bool CAUSAL>
 struct Fwd16 {
@@ -83,8 +84,12 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     int BH, int G, float qk_scale, uint32_t qsign) {
   using C = Fwd16<T, D, BN, CAUSAL>;
   constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::NBUF][BN * D];
+  // Swizzled row-major tiles, V below K: the transposing V reads of ring
+  // slots 0-3 then reach their address with a per-lane base register and
+  // the 16-bit immediate offset alone (no address add per read).
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][C::NBUF][BN * D];
+  auto& v_lds = kv_lds[0];
+  auto& k_lds = kv_lds[1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,11 +182,16 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // within-row address bits): row reads at (R ^ 32 k) + 64 sb D bytes,
   // transposing reads at (T ^ 64 (k % DB) [^ 32]) + 2 rows D.  The bases go
   // through an empty asm so each address is formed next to its read.
-  uint32_t Rb = 2u * (uint32_t)swz<D>(n, 8 * g);
+  // The K ring lies kKOff bytes above the V ring; that distance is carried in
+  // the K base register (the XOR touches bits 5-7 only, so (Rb + kKOff) ^ x =
+  // (Rb ^ x) + kKOff), which leaves each K read's immediate offset within the
+  // 16-bit range for ring slots 0-3.
+  constexpr uint32_t kKOff = sizeof(v_lds);
+  uint32_t Rb = 2u * (uint32_t)swz<D>(n, 8 * g) + kKOff;
   uint32_t Tb = 2u * (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   asm volatile("" : "+v"(Rb), "+v"(Tb));
   auto kfrag = [&](const uint16_t* kt, int sb, int k) __attribute__((always_inline)) {
-    return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kt) + (Rb ^ (32 * k)) + 64 * sb * D);
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kt) - kKOff + (Rb ^ (32 * k)) + 64 * sb * D);
   };
   auto vfrag = [&](const uint16_t* vt, int sb, int k) __attribute__((always_inline)) {
     const char* base = reinterpret_cast<const char*>(vt);
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // packed to 16-bit as the B operand of the PV product; returns the lane sum.
   auto exp_pack = [&](const f32x16& cur, int key0, uint32_t (&pk)[8], auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part[2] = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
@@ -210,11 +220,10 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         p0 = kb < key_lim ? p0 : 0.f;
         p1 = kb + 1 < key_lim ? p1 : 0.f;
       }
-      part[r % 4] += p0;
-      part[(r + 1) % 4] += p1;
       pk[r / 2] = pack2(T{}, p0, p1);
+      part[(r / 2) % 2] = add_pair(T{}, pk[r / 2], p0, p1, part[(r / 2) % 2]);
     }
-    return (part[0] + part[1]) + (part[2] + part[3]);
+    return part[0] + part[1];
   };
   // Rare path: some lane's weights exceeded the limit.  Raise the reference
   // to the true row max of this sub-block where it is higher, rescale O and
@@ -267,10 +276,14 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   constexpr int PD = 3;  // fragments read ahead of the product that uses them
   static_assert(PD <= NS, "prefetch distance");
   uint4 ka[PD], vb[PD];
-  uint32_t pkp[8];  // packed weights of sub-block u-1
+  // Packed weights of the even and the odd sub-blocks: step u writes the
+  // array of u's parity and its PV product reads the other one (u - 1), so
+  // no copy is needed between steps.  A tile holds an even number of
+  // sub-blocks, so the parity is a compile-time fact inside the tile loop.
+  uint32_t pkA[8], pkB[8];
   auto step = [&](f32x16& cur, int key0, f32x16& nxt, const uint16_t* kt, int ksb, const uint16_t* vt, int vsb,
-                  const uint16_t* kt2, int ksb2, const uint16_t* vt2, int vsb2, auto with_pv)
-      __attribute__((always_inline)) {
+                  const uint16_t* kt2, int ksb2, const uint16_t* vt2, int vsb2, uint32_t (&pk)[8],
+                  const uint32_t (&pkp)[8], auto with_pv) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     constexpr int EPS = 16 / NS;  // weights per slot
     const uint4 pp[2] = {make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]), make_uint4(pkp[4], pkp[5], pkp[6], pkp[7])};
@@ -280,8 +293,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       a[i] = ka[i];
       b[i] = vb[i];
     }
-    float part[4];
-    uint32_t pk[8];
+    float lsum = 0.f;  // one dot-product chain: its links are a slot apart
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (k + PD < NS) {
@@ -297,9 +309,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         const int r = k * EPS + e;
         const float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
         const float p1 = fast_exp2(__builtin_fmaf(cur[r + 1], qk_scale, -m_run));
-        part[r % 4] = r < 4 ? p0 : part[r % 4] + p0;
-        part[(r + 1) % 4] = r < 4 ? p1 : part[(r + 1) % 4] + p1;
         pk[r / 2] = pack2(T{}, p0, p1);
+        lsum = add_pair(T{}, pk[r / 2], p0, p1, lsum);
       }
       if constexpr (PV) oacc[k % DB] = mma16(T{}, b[k % (PD + 1)], pp[k / DB], oacc[k % DB]);
       __builtin_amdgcn_sched_barrier(0);
@@ -308,9 +319,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     // packs into the common branch, out of the interleave.
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[i]));
-    settle(cur, key0, pk, (part[0] + part[1]) + (part[2] + part[3]), std::false_type{});
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pkp[i] = pk[i];
+    settle(cur, key0, pk, lsum, std::false_type{});
   };
 
   // One tile j (buffers: kc / vc this tile, kn the next, vp the previous):
@@ -327,11 +336,13 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       const int u = j * SUB + i;
       f32x16& cur = (i % 2 == 0) ? sA : sB;
       f32x16& nxt = (i % 2 == 0) ? sB : sA;
+      uint32_t(&pk)[8] = (i % 2 == 0) ? pkA : pkB;
+      uint32_t(&pkp)[8] = (i % 2 == 0) ? pkB : pkA;
       if (u >= 1 && u < u_last) {
         const uint16_t* kt = i + 1 < SUB ? kc : kn;        // sub-block u + 1
         const uint16_t* vt = i >= 1 ? vc : vp;             // sub-block u - 1
         const uint16_t* kt2 = i + 2 < SUB ? kc : kn;       // sub-block u + 2
-        step(cur, 32 * u, nxt, kt, (i + 1) % SUB, vt, (i + SUB - 1) % SUB, kt2, (i + 2) % SUB, vc, i,
+        step(cur, 32 * u, nxt, kt, (i + 1) % SUB, vt, (i + SUB - 1) % SUB, kt2, (i + 2) % SUB, vc, i, pk, pkp,
              std::true_type{});
       }
     }
@@ -355,7 +366,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       const uint16_t* k2 = k_lds[2 / SUB];
 #pragma unroll
       for (int i = 0; i < PD; ++i) ka[i] = kfrag(k_lds[0], 1, i);
-      step(sA, 0, sB, k_lds[0], 1, v_lds[0], 0, k2, 2 % SUB, v_lds[0], 0, std::false_type{});
+      step(sA, 0, sB, k_lds[0], 1, v_lds[0], 0, k2, 2 % SUB, v_lds[0], 0, pkA, pkB, std::false_type{});
     }
   }
 
@@ -385,7 +396,11 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // sub-blocks before the workgroup's), so they are still in LDS: no load
   // was issued after the final one.
   if (wave_live) {
-    if (u_last >= 1) pv_gemm(v_lds[((u_last - 1) / SUB) % NB5], (u_last - 1) % SUB, pkp);
+    if (u_last >= 1) {
+      const uint16_t* vt1 = v_lds[((u_last - 1) / SUB) % NB5];
+      if (u_last % 2 == 1) pv_gemm(vt1, (u_last - 1) % SUB, pkA);
+      else pv_gemm(vt1, (u_last - 1) % SUB, pkB);
+    }
     const uint16_t* vt = v_lds[(u_last / SUB) % NB5];
     const f32x16 cur = (u_last % 2 == 0) ? sA : sB;
     uint32_t pk[8];
