@@ -101,11 +101,22 @@ struct KV {
   static_assert(2 * DB == DS, "one product per slot in every phase");
 };
 
-// Uniform state of one dK/dV wave.
+// Lane index from the lane masks (no input register), so that the compiler
+// can recompute lane-derived values where they are used instead of keeping
+// them live across the whole kernel.
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// State of one dK/dV wave: uniform values, and the lane's position.
 struct KVWave {
-  int wave, lane, n, g, pw, kw0, N;
+  int wave, pw, kw0, N;
   bool role_a;
   float qk_scale;
+  __device__ __forceinline__ int lane() const { return lane_id(); }
+  __device__ __forceinline__ int n() const { return lane_id() & 31; }
+  __device__ __forceinline__ int g() const { return lane_id() >> 5; }
+};
+// Buffer resources of the query head a segment reads: Q, dO, LSE, Delta.
+struct KVSrc {
   rsrc_t qrs, dors, lrs, drs;
 };
 
@@ -117,23 +128,23 @@ struct KVWave {
 // (returned); once it has arrived they store -LSE log2(e) and -Delta into
 // LDS (kv_stage_rows).
 template <int D>
-__device__ __forceinline__ float kv_issue(const KVWave& w, int i, uint16_t* __restrict__ q_dst,
+__device__ __forceinline__ float kv_issue(const KVWave& w, const KVSrc& src, int i, uint16_t* __restrict__ q_dst,
                                           uint16_t* __restrict__ do_dst) {
   using C = KV<D>;
   float val = 0.f;
-  if (w.wave == 0) val = load4f(w.lrs, (uint32_t)(i * C::BMQ + w.lane) * 4);
-  if (w.wave == 1) val = load4f(w.drs, (uint32_t)(i * C::BMQ + w.lane) * 4);
-  const int lrow = w.lane / C::CPR;
+  if (w.wave == 0) val = load4f(src.lrs, (uint32_t)(i * C::BMQ + w.lane()) * 4);
+  if (w.wave == 1) val = load4f(src.drs, (uint32_t)(i * C::BMQ + w.lane()) * 4);
+  const int lrow = w.lane() / C::CPR;
 #pragma unroll
   for (int e = 0; e < C::LPB; ++e) {
     const int t = w.wave * C::LPB + e;
     const bool is_q = t < C::PPA;  // wave-uniform
     const int row = (t % C::PPA) * C::RPL + lrow;
-    const int chunk = (w.lane % C::CPR) ^ swz_chunk<D>(row);
+    const int chunk = (w.lane() % C::CPR) ^ swz_chunk<D>(row);
     const uint32_t off = ((uint32_t)(i * C::BMQ + row) * D + 8 * chunk) * 2;
     const int piece = (t % C::PPA) * C::RPL * D;
-    if (is_q) load_lds16(w.qrs, q_dst + piece, off);
-    else load_lds16(w.dors, do_dst + piece, off);
+    if (is_q) load_lds16(src.qrs, q_dst + piece, off);
+    else load_lds16(src.dors, do_dst + piece, off);
   }
   return val;
 }
@@ -142,8 +153,8 @@ __device__ __forceinline__ float kv_issue(const KVWave& w, int i, uint16_t* __re
 // the dP product yields dP - Delta directly).
 __device__ __forceinline__ void kv_stage_rows(const KVWave& w, float val, float* __restrict__ l_dst,
                                               float* __restrict__ d_dst) {
-  if (w.wave == 0) l_dst[w.lane] = -val * kLog2e;
-  if (w.wave == 1) d_dst[w.lane] = -val;
+  if (w.wave == 0) l_dst[w.lane()] = -val * kLog2e;
+  if (w.wave == 1) d_dst[w.lane()] = -val;
 }
 
 // One iteration of a wave's work on its block: four phases over the two
@@ -163,7 +174,7 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
   using C = KV<D>;
   constexpr int NS = C::DS;        // products per phase
   constexpr int EP = 16 / NS;      // accumulator elements of vector work per slot (2 or 4)
-  const int n = w.n, g = w.g, lane = w.lane;
+  const int n = w.n(), g = w.g(), lane = w.lane();
   const int q_first = i * C::BMQ;
   const int key = w.kw0 + n;
 
@@ -325,7 +336,19 @@ __device__ __forceinline__ void kv_iter(const KVWave& w, int i, const uint4 (&kv
 }
 
 // GROUPED = false compiles the one-query-head-per-K/V-head case (G = 1)
-// without the loop over a group, which costs registers.
+// without the query-head index, which costs registers.
+//
+// The workgroup walks a sequence of segments: one block of BNK keys of one
+// K/V head together with one query head that reads it (G segments per block
+// under GQA), i.e. the query blocks i_lo .. n_qblk - 1 of that head.  With
+// wave B one query block behind wave A, a segment takes n_qblk - i_lo + 1
+// iterations: in the first only A has products to compute, in the last only
+// B.  Segments run back to back without draining: the last iteration loads
+// the next segment's first query block, and each wave does its block-change
+// work in its idle iteration -- A in the last (store dV, load the next
+// block's K), B in the first (store the previous block's dK, load this
+// block's V).  The barrier that ends every iteration waits for all loads and
+// stores, so that work runs under the other wave's products.
 template <typename T, int D, bool CAUSAL, bool GROUPED>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
@@ -340,142 +363,228 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float dl_lds[C::NSLOT][C::BMQ];         // -Delta
 
   KVWave w;
-  w.lane = threadIdx.x & 63;
   w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform, in a scalar register
-  w.n = w.lane & 31;
-  w.g = w.lane >> 5;
   w.role_a = w.wave < C::NP;
   w.pw = w.wave % C::NP;  // key group; waves pw and pw + NP share a SIMD
   w.N = N;
   w.qk_scale = qk_scale;
 
-  // One block of BNK keys of one K/V head bkv, start to finish: its G query
-  // heads' contributions are accumulated one head after another.
-  auto block = [&](int bkv, int kblk) __attribute__((always_inline)) {
-  const size_t head = (size_t)bkv * (size_t)N * D;  // K, V, dK, dV
+  const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  w.kw0 = kblk * C::BNK + w.pw * C::KW;  // first key of this pair
-  const bool pair_live = w.kw0 < N;
+  const int n_group = GROUPED ? G : 1;
+
+  // ---- segment cursor ------------------------------------------------------
+  // Persistent walk over equal-cost items (items_per_head / item_blocks) of
+  // the K/V heads; in each round every XCD works on a contiguous range of
+  // items.  Cursor (L, t, j): item L, its block t (the heavier, lower key
+  // block of a causal pair first), query head j of the group.
+  struct Seg {
+    int bkv, kblk, j;
+  };
+  const int per_head = items_per_head(n_kblk, CAUSAL);
+  const int n_items = BHkv * per_head;
+  auto seg_at = [&](int L, int t, int j, Seg& sg) {
+    if (L >= n_items) return false;
+    int lo, hi;
+    item_blocks(L % per_head, n_kblk, CAUSAL, &lo, &hi);
+    sg.bkv = L / per_head;
+    sg.kblk = t == 0 ? lo : hi;
+    sg.j = j;
+    return true;
+  };
+  auto advance = [&](int& L, int& t, int& j) {
+    if (++j < n_group) return;
+    j = 0;
+    int lo, hi;
+    if (++t < item_blocks(L % per_head, n_kblk, CAUSAL, &lo, &hi)) return;
+    t = 0;
+    L += gridDim.x;
+  };
+  auto qhead_of = [&](const Seg& sg) { return GROUPED ? q_head_of(sg.bkv, G, sg.j) : sg.bkv; };
+  // Loads of query block i of query head qh into a ring slot (the buffer
+  // resources are rebuilt per call: scalar work, and no live registers).
+  auto issue = [&](int qh, int i, uint16_t* __restrict__ q_dst, uint16_t* __restrict__ do_dst)
+      __attribute__((always_inline)) {
+    KVSrc r;
+    r.qrs = make_rsrc(qg + (size_t)qh * N * D, head_bytes);
+    r.dors = make_rsrc(dog + (size_t)qh * N * D, head_bytes);
+    r.lrs = make_rsrc(lseg + (size_t)qh * N, (uint32_t)N * 4);
+    r.drs = make_rsrc(deltag + (size_t)qh * N, (uint32_t)N * 4);
+    return kv_issue<D>(w, r, i, q_dst, do_dst);
+  };
+  auto first_qblk = [&](const Seg& sg) { return CAUSAL ? (sg.kblk * C::BNK) / C::BMQ : 0; };
+  auto same_block = [&](const Seg& x, const Seg& y) { return x.bkv == y.bkv && x.kblk == y.kblk; };
 
   // A holds K (sign-flipped for a negative scale), B holds V, as the B
   // operand of Q K^T / dO V^T: kv[s] = row kw0 + n, columns 16 s + 8 g .. + 8.
+  // Rows past N read as zeros.
   uint4 kv[C::DS];
-  {
-    const rsrc_t rs = make_rsrc((w.role_a ? kg : vg) + head, head_bytes);
+  auto load_kv = [&](const Seg& sg) __attribute__((always_inline)) {
+    const int kw0 = sg.kblk * C::BNK + w.pw * C::KW;
+    const rsrc_t rs = make_rsrc((w.role_a ? kg : vg) + (size_t)sg.bkv * N * D, head_bytes);
     const uint32_t sgn = w.role_a ? ksign : 0u;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      const uint4 a = load16(rs, ((uint32_t)(w.kw0 + w.n) * D + 16 * s + 8 * w.g) * 2);
+      const uint4 a = load16(rs, ((uint32_t)(kw0 + w.n()) * D + 16 * s + 8 * w.g()) * 2);
       kv[s] = make_uint4(a.x ^ sgn, a.y ^ sgn, a.z ^ sgn, a.w ^ sgn);
     }
-  }
+  };
   f32x16 acc[C::DB];  // A: dV, B: dK (unscaled); rows = keys, columns = d
+  // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
+  // Buffer stores: rows past N fall outside the head's range and are dropped.
+  auto store_acc = [&](int bkv, int kblk) __attribute__((always_inline)) {
+    const int kw0 = kblk * C::BNK + w.pw * C::KW;
+    const rsrc_t rs = make_rsrc((w.role_a ? dvg : dkg) + (size_t)bkv * N * D, (uint32_t)((size_t)N * D * 4));
+    const float sc = w.role_a ? 1.f : dk_scale;
+    const uint32_t base = ((uint32_t)(kw0 + 4 * w.g()) * D + w.n()) * 4;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[db][r] * sc), rs,
+                                              base + (uint32_t)((8 * (r / 4) + (r % 4)) * D + 32 * db) * 4, 0, 0);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  };
+
+  // ---- first segment: A's K, the first query block ------------------------
+  int cL = xcd_remap(blockIdx.x, gridDim.x), ct = 0, cj = 0;
+  Seg cur;
+  if (!seg_at(cL, ct, cj, cur)) return;  // uniform: the grid never exceeds the items
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-
-  const int n_qblk = (N + C::BMQ - 1) / C::BMQ;
-  const int i_lo = CAUSAL ? (kblk * C::BNK) / C::BMQ : 0;
-  auto block_active = [&](int i) {
-    return pair_live && (!CAUSAL || min((i + 1) * C::BMQ, N) - 1 >= w.kw0);
-  };
-  // A block needs the causal mask when its first query is left of the
-  // pair's last key (only the diagonal block of the pair).
-  auto block_masked = [&](int i) { return CAUSAL && i * C::BMQ < w.kw0 + C::KW - 1; };
-
-  wait_vmem();  // K or V fragments above
-  const int n_group = GROUPED ? G : 1;
-  for (int j = 0; j < n_group; ++j) {  // the query heads sharing this K/V head
-  const size_t qhead = GROUPED ? (size_t)q_head_of(bkv, G, j) : (size_t)bkv;
-  w.qrs = make_rsrc(qg + qhead * N * D, head_bytes);
-  w.dors = make_rsrc(dog + qhead * N * D, head_bytes);
-  w.lrs = make_rsrc(lseg + qhead * N, (uint32_t)N * 4);
-  w.drs = make_rsrc(deltag + qhead * N, (uint32_t)N * 4);
-  float row_in = kv_issue<D>(w, i_lo, q_lds[i_lo % C::NSLOT], do_lds[i_lo % C::NSLOT]);
-  kv_stage_rows(w, row_in, lse_lds[i_lo % C::NSLOT], dl_lds[i_lo % C::NSLOT]);
+  if (w.role_a) load_kv(cur);
+  int qh = qhead_of(cur);
+  float row_in = issue(qh, first_qblk(cur), q_lds[0], do_lds[0]);
+  kv_stage_rows(w, row_in, lse_lds[0], dl_lds[0]);
   lds_barrier<0>();
 
-  // Iteration i: A works on block i (slot i % 3), B on block i - 1 (slot
-  // (i - 1) % 3); block i + 1 is loaded into slot (i + 1) % 3, whose last
-  // reader (B, block i - 2) finished before the previous barrier.  MAY_MASK
-  // marks the call sites that can meet A's masked block.
-  auto iter = [&](int i, uint16_t* __restrict__ qa, uint16_t* __restrict__ da, float* __restrict__ la,
-                  float* __restrict__ dla, uint16_t* __restrict__ qb, uint16_t* __restrict__ db_,
-                  float* __restrict__ dlb, uint16_t* __restrict__ qn, uint16_t* __restrict__ dn,
-                  float* __restrict__ ln, float* __restrict__ dln, auto may_mask) __attribute__((always_inline)) {
-    constexpr bool MAY_MASK = decltype(may_mask)::value;
-    const bool ahead = i + 1 < n_qblk;
-    if (ahead) row_in = kv_issue<D>(w, i + 1, qn, dn);
-    if (w.role_a) {
-      if (i < n_qblk && block_active(i)) {
-        if (MAY_MASK && block_masked(i))
-          kv_iter<T, D, true, true>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
-        else
-          kv_iter<T, D, true, false>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+  // Element (query block) i of the current segment sits in ring slot
+  // (sb + i - i_lo) % 3.
+  int sb = 0;
+  // A block change leaves the finished block's dV in A's accumulators and its
+  // dK in B's; each wave stores them just before its first product of the
+  // new segment (A: iteration i_lo, B: iteration i_lo + 1), so the stores
+  // drain under full-rate products.
+  int prev_bkv = -1, prev_kblk = 0;  // the block whose dV / dK is still in the accumulators (-1: none)
+  bool b_change = true;  // B: new block at this segment; a previous block's dK to store
+  while (true) {
+    int nL = cL, nt = ct, nj = cj;
+    advance(nL, nt, nj);
+    Seg nxt;
+    const bool has_next = seg_at(nL, nt, nj, nxt);
+    const bool a_change = !has_next || !same_block(cur, nxt);
+    w.kw0 = cur.kblk * C::BNK + w.pw * C::KW;  // first key of this pair
+    const bool pair_live = w.kw0 < N;
+    const int i_lo = first_qblk(cur);
+    auto block_active = [&](int i) {
+      return pair_live && (!CAUSAL || min((i + 1) * C::BMQ, N) - 1 >= w.kw0);
+    };
+    // A block needs the causal mask when its first query is left of the
+    // pair's last key (only the diagonal block of the pair).
+    auto block_masked = [&](int i) { return CAUSAL && i * C::BMQ < w.kw0 + C::KW - 1; };
+    auto a_work = [&](int i, const uint16_t* __restrict__ qa, const uint16_t* __restrict__ da,
+                      const float* __restrict__ la, auto may_mask, auto first) __attribute__((always_inline)) {
+      constexpr bool MAY_MASK = decltype(may_mask)::value;
+      if (decltype(first)::value && prev_bkv >= 0) store_acc(prev_bkv, prev_kblk);  // first product of a new block
+      if (!block_active(i)) return;
+      if (MAY_MASK && block_masked(i))
+        kv_iter<T, D, true, true>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+      else
+        kv_iter<T, D, true, false>(w, i, kv, acc, qa, da, la, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+    };
+    // B's work on element i - 1 in iteration i.
+    auto b_work = [&](int i, const uint16_t* __restrict__ qb, const uint16_t* __restrict__ db_,
+                      const float* __restrict__ dlb, auto first) __attribute__((always_inline)) {
+      if (decltype(first)::value && prev_bkv >= 0) store_acc(prev_bkv, prev_kblk);  // first product of a new block
+      if (block_active(i - 1))
+        kv_iter<T, D, false, false>(w, i - 1, kv, acc, db_, qb, dlb, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+    };
+
+    // ---- iteration i_lo: A's first block; B changes block if needed -------
+    {
+      const int sa = sb, sn = (sb + 1) % 3;
+      const bool ahead = i_lo + 1 < n_qblk;
+      if (ahead) row_in = issue(qh, i_lo + 1, q_lds[sn], do_lds[sn]);
+      if (w.role_a) {
+        a_work(i_lo, q_lds[sa], do_lds[sa], lse_lds[sa], std::true_type{}, std::true_type{});
+      } else if (b_change) {
+        load_kv(cur);
       }
-    } else if (i > i_lo && block_active(i - 1)) {
-      kv_iter<T, D, false, false>(w, i - 1, kv, acc, db_, qb, dlb, x_lds[i & 1][w.pw], x_lds[(i + 1) & 1][w.pw]);
+      if (ahead) kv_stage_rows(w, row_in, lse_lds[sn], dl_lds[sn]);
+      lds_barrier<0>();
     }
-    // Block i + 1 must be in LDS after this barrier (waves 0 and 1 first
-    // store its row values, whose loads have arrived by now).
-    if (ahead) kv_stage_rows(w, row_in, ln, dln);
-    lds_barrier<0>();
-  };
-  // A pair's keys start at kw0 = 128 kblk + 32 pw, so its only masked block
-  // (the one holding query kw0) is block 2 kblk + pw / 2: i_lo or i_lo + 1.
-  // Only those two iterations carry the masked variant of A's work.
-  static_assert(C::BNK == 2 * C::BMQ && C::KW == 32 && C::NP == 4, "masked block at i_lo or i_lo + 1");
-  constexpr int NS3 = C::NSLOT;
-  int i = i_lo;
-  for (; i <= n_qblk && i < i_lo + 2; ++i) {
-    const int sa = i % NS3, sb = (i + NS3 - 1) % NS3, sn = (i + 1) % NS3;
-    iter(i, q_lds[sa], do_lds[sa], lse_lds[sa], dl_lds[sa], q_lds[sb], do_lds[sb], dl_lds[sb], q_lds[sn],
-         do_lds[sn], lse_lds[sn], dl_lds[sn], std::true_type{});
-  }
-  // The rest, unrolled over the three slots so every LDS base is an
-  // immediate.
-  for (int i0 = i - i % NS3; i0 <= n_qblk; i0 += NS3) {
+    // ---- iterations i_lo + 1 .. n_qblk - 1: both waves --------------------
+    // Iteration i: A on block i (slot sa), B on block i - 1 (slot sa - 1),
+    // block i + 1 loaded into slot sa + 1, whose last reader (B, block i - 2)
+    // finished before the previous barrier.
+    auto mid = [&](int i, uint16_t* __restrict__ qa, uint16_t* __restrict__ da, float* __restrict__ la,
+                   uint16_t* __restrict__ qb, uint16_t* __restrict__ db_, float* __restrict__ dlb,
+                   uint16_t* __restrict__ qn, uint16_t* __restrict__ dn, float* __restrict__ ln,
+                   float* __restrict__ dln, auto may_mask) __attribute__((always_inline)) {
+      const bool ahead = i + 1 < n_qblk;
+      if (ahead) row_in = issue(qh, i + 1, qn, dn);
+      // may_mask marks iteration i_lo + 1: A's block may be masked there, and
+      // it is B's first product of the segment.
+      if (w.role_a) a_work(i, qa, da, la, may_mask, std::false_type{});
+      else b_work(i, qb, db_, dlb, may_mask);
+      // Block i + 1 must be in LDS after this barrier (waves 0 and 1 first
+      // store its row values, whose loads have arrived by now).
+      if (ahead) kv_stage_rows(w, row_in, ln, dln);
+      lds_barrier<0>();
+    };
+    // A pair's keys start at kw0 = 128 kblk + 32 pw, so its only masked block
+    // (the one holding query kw0) is block 2 kblk + pw / 2: i_lo or i_lo + 1.
+    static_assert(C::BNK == 2 * C::BMQ && C::KW == 32 && C::NP == 4, "masked block at i_lo or i_lo + 1");
+    if (i_lo + 1 < n_qblk) {
+      const int sa = (sb + 1) % 3, sp = sb, sn = (sb + 2) % 3;
+      mid(i_lo + 1, q_lds[sa], do_lds[sa], lse_lds[sa], q_lds[sp], do_lds[sp], dl_lds[sp], q_lds[sn], do_lds[sn],
+          lse_lds[sn], dl_lds[sn], std::true_type{});
+    }
+    // The rest, unrolled over the three slots so every LDS base is an
+    // immediate: stream position c = sb + i - i_lo, slot c % 3.
+    {
+      const int c_beg = sb + 2, c_end = sb + n_qblk - 1 - i_lo;  // i from i_lo + 2 to n_qblk - 1
+      for (int c0 = c_beg - c_beg % 3; c0 <= c_end; c0 += 3) {
 #pragma unroll
-    for (int jj = 0; jj < NS3; ++jj) {
-      const int ii = i0 + jj;
-      if (ii >= i && ii <= n_qblk) {
-        iter(ii, q_lds[jj], do_lds[jj], lse_lds[jj], dl_lds[jj], q_lds[(jj + NS3 - 1) % NS3],
-             do_lds[(jj + NS3 - 1) % NS3], dl_lds[(jj + NS3 - 1) % NS3], q_lds[(jj + 1) % NS3],
-             do_lds[(jj + 1) % NS3], lse_lds[(jj + 1) % NS3], dl_lds[(jj + 1) % NS3], std::false_type{});
+        for (int jj = 0; jj < 3; ++jj) {
+          const int c = c0 + jj;
+          if (c >= c_beg && c <= c_end) {
+            mid(c - sb + i_lo, q_lds[jj], do_lds[jj], lse_lds[jj], q_lds[(jj + 2) % 3], do_lds[(jj + 2) % 3],
+                dl_lds[(jj + 2) % 3], q_lds[(jj + 1) % 3], do_lds[(jj + 1) % 3], lse_lds[(jj + 1) % 3],
+                dl_lds[(jj + 1) % 3], std::false_type{});
+          }
+        }
       }
     }
-  }
-
-  // The last iteration ended with a barrier after every LDS read, so the
-  // next query head may refill the slots at once.
-  }
-
-  // Register r of d block db is key kw0 + 8(r/4) + 4g + r%4, column 32 db + n.
-  float* out = (w.role_a ? dvg : dkg) + head;
-  const float sc = w.role_a ? 1.f : dk_scale;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = w.kw0 + 8 * (r / 4) + 4 * w.g + (r % 4);
-      if (kr < N) out[(size_t)kr * D + 32 * db + w.n] = acc[db][r] * sc;
+    // ---- iteration n_qblk: B's last block; A changes block if needed ------
+    // The next segment's first block goes into the slot after B's.
+    const int s_b = (sb + n_qblk - 1 - i_lo) % 3, s_n = (s_b + 1) % 3;
+    {
+      if (has_next) row_in = issue(qhead_of(nxt), first_qblk(nxt), q_lds[s_n], do_lds[s_n]);
+      if (w.role_a) {
+        if (a_change && has_next) load_kv(nxt);  // A's K is dead; its dV waits in acc
+      } else if (i_lo + 1 == n_qblk) {
+        b_work(n_qblk, q_lds[s_b], do_lds[s_b], dl_lds[s_b], std::true_type{});
+      } else {
+        b_work(n_qblk, q_lds[s_b], do_lds[s_b], dl_lds[s_b], std::false_type{});
+      }
+      if (has_next) kv_stage_rows(w, row_in, lse_lds[s_n], dl_lds[s_n]);
+      lds_barrier<0>();
     }
-  };
-
-  // Persistent loop over equal-cost items (items_per_head / item_blocks) of
-  // the K/V heads; in each round every XCD works on a contiguous range of
-  // items.  The heavier key block of a causal pair (the lower one) goes
-  // first.
-  const int per_head = items_per_head(n_kblk, CAUSAL);
-  const int n_items = BHkv * per_head;
-  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
-    const int bh = L / per_head;
-    int lo, hi;
-    const int nb = item_blocks(L % per_head, n_kblk, CAUSAL, &lo, &hi);
-    for (int t = 0; t < nb; ++t) {
-      block(bh, t == 0 ? lo : hi);
-      __syncthreads();  // the next block reuses the LDS buffers
-    }
+    if (!has_next) break;
+    b_change = a_change;
+    prev_bkv = a_change ? cur.bkv : -1;
+    prev_kblk = cur.kblk;
+    cur = nxt;
+    cL = nL;
+    ct = nt;
+    cj = nj;
+    qh = qhead_of(cur);
+    sb = s_n;
   }
+  // The last block's dV (A) and dK (B).
+  store_acc(cur.bkv, cur.kblk);
 }
 
 // ---------------------------------------------------------------------------
