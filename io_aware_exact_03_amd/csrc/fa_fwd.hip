@@ -99,8 +99,10 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // ---- Q fragments of the current query block, held in registers --------
   // B operand of S^T = K Q^T: lane supplies Q[query][16 s + 8 g + 0..7];
   // rows outside [0, Nq) read as zeros (a negative row wraps to an offset
-  // past the buffer).  A negative scale flips Q's sign bits.  The next
-  // block's fragments are loaded during the current block's tail.
+  // past the buffer).  A negative scale flips Q's sign bits, at the block's
+  // first use rather than at the load, so that nothing waits for the data
+  // early: the next block's fragments are loaded at the end of the current
+  // block and arrive under its epilogue.
   //
   // Query rows are indexed virtually: virtual row i' is query i' - qshift,
   // and with the causal mask it sees keys j <= i' + koff, koff a multiple of
@@ -113,11 +115,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     const rsrc_t rs = make_rsrc(qg + (size_t)bh * (size_t)Nq * D, (uint32_t)Nq * D * 2);
     const int q = qblk * C::BM + 32 * wave + n - qshift;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      uint4 x = load16(rs, ((uint32_t)q * D + 16 * s + 8 * g) * 2);
-      x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
-      qf[s] = x;
-    }
+    for (int s = 0; s < DS; ++s) qf[s] = load16(rs, ((uint32_t)q * D + 16 * s + 8 * g) * 2);
   };
 
   // One query block of one (batch, head), start to finish; (nbh, nqblk) is
@@ -357,6 +355,12 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   } else {
     lds_barrier<0>();
   }
+  if (qsign != 0) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s].x ^= qsign; qf[s].y ^= qsign; qf[s].z ^= qsign; qf[s].w ^= qsign;
+    }
+  }
   if (wave_live) {
     s_gemm(k_lds[0], 0, sA);
     f32x16 s1[1] = {sA};
@@ -388,8 +392,6 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       }
     }
   }
-  // The next block's Q: the tail below needs no Q fragments.
-  if (nbh >= 0) load_q(nbh, nqblk);
   // The wave's last two sub-blocks: the PV product of u_last - 1 and the
   // masked weights and PV product of u_last.  Their tiles are among the
   // last five of the workgroup (a wave's last sub-block is at most seven
@@ -397,9 +399,10 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   // was issued after the final one.
   if (wave_live) {
     if (u_last >= 1) {
-      const uint16_t* vt1 = v_lds[((u_last - 1) / SUB) % NB5];
-      if (u_last % 2 == 1) pv_gemm(vt1, (u_last - 1) % SUB, pkA);
-      else pv_gemm(vt1, (u_last - 1) % SUB, pkB);
+      uint32_t pkl[8];  // weights of sub-block u_last - 1, from the array of its parity
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pkl[i] = (u_last & 1) ? pkA[i] : pkB[i];
+      pv_gemm(v_lds[((u_last - 1) / SUB) % NB5], (u_last - 1) % SUB, pkl);
     }
     const uint16_t* vt = v_lds[(u_last / SUB) % NB5];
     const f32x16 cur = (u_last % 2 == 0) ? sA : sB;
@@ -408,6 +411,12 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     settle(cur, 32 * u_last, pk, lsum, std::true_type{});
     pv_gemm(vt, u_last % SUB, pk);
   }
+
+  // The next block's Q (the tail above was the last use of this block's).
+  // Issued after the tail, whose LDS reads the compiler makes wait for every
+  // outstanding load, so they arrive under the epilogue and the next
+  // block's tile wait.
+  if (nbh >= 0) load_q(nbh, nqblk);
 
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
   const float l_tot = halves_sum(l_run);
