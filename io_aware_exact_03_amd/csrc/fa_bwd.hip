@@ -624,32 +624,41 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
 
-  // One block of BM queries of one (batch, head), start to finish.
-  auto qblock = [&](int bh, int qblk) __attribute__((always_inline)) {
+  // Q and dO of this lane's query as the B operands, and its LSE and Delta
+  // (zeros past the end; the LSE and Delta loads are range-checked too, and
+  // a query past N is made harmless by LSE = +inf below).  The next
+  // block's values are loaded at the end of the current block, after the
+  // last use of these registers, and arrive under its epilogue; a negative
+  // scale flips Q's sign bits at the block's first use, so nothing waits
+  // for the data at the load.
+  uint4 qf[DS], dof[DS];
+  float lse_in, dl;
+  auto load_rows = [&](int bh, int qblk) __attribute__((always_inline)) {
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
+    const int query = qblk * C::BM + wave * 32 + n;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * g) * 2;
+      qf[s] = load16(qrs, off);
+      dof[s] = load16(dors, off);
+    }
+    lse_in = load4f(make_rsrc(lseg + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)query * 4);
+    dl = load4f(make_rsrc(deltag + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)query * 4);
+  };
+
+  // One block of BM queries of one (batch, head), start to finish; the
+  // block (nbh, nqblk) comes next (nbh < 0: none).
+  auto qblock = [&](int bh, int qblk, int nbh, int nqblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;  // shared by G query heads
-  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes), vrs = make_rsrc(vg + kvhead, head_bytes);
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + wave * 32;
   const int query = qw0 + n;
-
-  // Q and dO of this lane's query as the B operands (zero past the end).
-  uint4 qf[DS], dof[DS];
-  {
-    const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * g) * 2;
-      uint4 a = load16(qrs, off);
-      a.x ^= qsign; a.y ^= qsign; a.z ^= qsign; a.w ^= qsign;
-      qf[s] = a;
-      dof[s] = load16(dors, off);
-    }
-  }
-  const float lse2 = query < N ? lseg[(size_t)bh * N + query] * kLog2e : kPosInf;
-  const float dl = query < N ? deltag[(size_t)bh * N + query] : 0.f;
+  float lse2;  // LSE log2(e), set once the rows have arrived (prologue)
 
   // Key plan, as in the forward: the wave's queries see sub-blocks
   // [0, u_last]; only u_last is masked.
@@ -783,7 +792,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   };
 
   // ---- prologue: tiles 0..2 in flight, wait for 0 and 1 ------------------
-  wait_vmem();  // Q, dO fragments above
   issue(0, k_lds[0], v_lds[0]);
   if (j_end > 1) issue(1, k_lds[1], v_lds[1]);
   if (j_end > 2) {
@@ -792,6 +800,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   } else {
     lds_barrier<0>();
   }
+  if (qsign != 0) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s].x ^= qsign; qf[s].y ^= qsign; qf[s].z ^= qsign; qf[s].w ^= qsign;
+    }
+  }
+  lse2 = query < N ? lse_in * kLog2e : kPosInf;
   if (wave_live) sdp(k_lds[0], v_lds[0], 0, sA, dA);
 
   // ---- main loop, unrolled over the buffers (immediate LDS offsets) ------
@@ -817,6 +832,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     vec(cs, cd, 32 * u_last, 0, 16, pk, std::true_type{});
     dq_gemm(kt, u_last % SUB, pk);
   }
+  // The next block's rows (the tail above was the last use of these).
+  if (nbh >= 0) load_rows(nbh, nqblk);
 
   if (wave_live && query < N) {
     float* row = dqg + head + (size_t)query * D;
@@ -836,14 +853,33 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   // heavier query block of a causal pair (the higher one) goes first.
   const int per_head = items_per_head(n_qblk, CAUSAL);
   const int n_items = BH * per_head;
-  for (int L = xcd_remap(blockIdx.x, gridDim.x); L < n_items; L += gridDim.x) {
-    const int bh = L / per_head;
+  // Block t of item L (heavy first); false past the item's blocks.
+  auto block_at = [&](int L, int t, int* bh, int* qb) {
+    if (L >= n_items) return false;
     int lo, hi;
     const int nb = item_blocks(L % per_head, n_qblk, CAUSAL, &lo, &hi);
-    for (int t = 0; t < nb; ++t) {
-      qblock(bh, t + 1 < nb ? hi : lo);
-      __syncthreads();  // the next block reuses the LDS buffers
+    if (t >= nb) return false;
+    *bh = L / per_head;
+    *qb = t + 1 < nb ? hi : lo;
+    return true;
+  };
+  int L = xcd_remap(blockIdx.x, gridDim.x), t = 0, bh = -1, qb = -1;
+  if (block_at(L, 0, &bh, &qb)) load_rows(bh, qb);
+  while (bh >= 0) {  // one call site: the block body is large
+    int nbh = -1, nqb = -1;
+    if (block_at(L, t + 1, &nbh, &nqb)) {
+      ++t;
+    } else {
+      L += gridDim.x;
+      t = 0;
+      if (!block_at(L, 0, &nbh, &nqb)) nbh = -1;
     }
+    qblock(bh, qb, nbh, nqb);
+    // The next block's loads reuse the LDS buffers; this block's dQ stores
+    // may still be in flight.
+    lds_only_barrier();
+    bh = nbh;
+    qb = nqb;
   }
 }
 
