@@ -518,15 +518,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     // Iteration i: A on block i (slot sa), B on block i - 1 (slot sa - 1),
     // block i + 1 loaded into slot sa + 1, whose last reader (B, block i - 2)
     // finished before the previous barrier.
+    // role: 0 = this wave's role decided at run time, 1 = A, 2 = B (the
+    // unrolled loop below runs one copy per role, so that A's and B's
+    // accumulators never meet in a join, which would cost a register copy
+    // of the whole accumulator per iteration).
     auto mid = [&](int i, uint16_t* __restrict__ qa, uint16_t* __restrict__ da, float* __restrict__ la,
                    uint16_t* __restrict__ qb, uint16_t* __restrict__ db_, float* __restrict__ dlb,
                    uint16_t* __restrict__ qn, uint16_t* __restrict__ dn, float* __restrict__ ln,
-                   float* __restrict__ dln, auto may_mask) __attribute__((always_inline)) {
+                   float* __restrict__ dln, auto may_mask, auto role) __attribute__((always_inline)) {
+      constexpr int ROLE = decltype(role)::value;
       const bool ahead = i + 1 < n_qblk;
       if (ahead) row_in = issue(qh, i + 1, qn, dn);
       // may_mask marks iteration i_lo + 1: A's block may be masked there, and
       // it is B's first product of the segment.
-      if (w.role_a) a_work(i, qa, da, la, may_mask, std::false_type{});
+      if (ROLE == 1 || (ROLE == 0 && w.role_a)) a_work(i, qa, da, la, may_mask, std::false_type{});
       else b_work(i, qb, db_, dlb, may_mask);
       // Block i + 1 must be in LDS after this barrier (waves 0 and 1 first
       // store its row values, whose loads have arrived by now).
@@ -539,11 +544,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     if (i_lo + 1 < n_qblk) {
       const int sa = (sb + 1) % 3, sp = sb, sn = (sb + 2) % 3;
       mid(i_lo + 1, q_lds[sa], do_lds[sa], lse_lds[sa], q_lds[sp], do_lds[sp], dl_lds[sp], q_lds[sn], do_lds[sn],
-          lse_lds[sn], dl_lds[sn], std::true_type{});
+          lse_lds[sn], dl_lds[sn], std::true_type{}, std::integral_constant<int, 0>{});
     }
     // The rest, unrolled over the three slots so every LDS base is an
     // immediate: stream position c = sb + i - i_lo, slot c % 3.
-    {
+    auto rest = [&](auto role) __attribute__((always_inline)) {
       const int c_beg = sb + 2, c_end = sb + n_qblk - 1 - i_lo;  // i from i_lo + 2 to n_qblk - 1
       for (int c0 = c_beg - c_beg % 3; c0 <= c_end; c0 += 3) {
 #pragma unroll
@@ -552,11 +557,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
           if (c >= c_beg && c <= c_end) {
             mid(c - sb + i_lo, q_lds[jj], do_lds[jj], lse_lds[jj], q_lds[(jj + 2) % 3], do_lds[(jj + 2) % 3],
                 dl_lds[(jj + 2) % 3], q_lds[(jj + 1) % 3], do_lds[(jj + 1) % 3], lse_lds[(jj + 1) % 3],
-                dl_lds[(jj + 1) % 3], std::false_type{});
+                dl_lds[(jj + 1) % 3], std::false_type{}, role);
           }
         }
       }
-    }
+    };
+    if (w.role_a) rest(std::integral_constant<int, 1>{});
+    else rest(std::integral_constant<int, 2>{});
     // ---- iteration n_qblk: B's last block; A changes block if needed ------
     // The next segment's first block goes into the slot after B's.
     const int s_b = (sb + n_qblk - 1 - i_lo) % 3, s_n = (s_b + 1) % 3;
