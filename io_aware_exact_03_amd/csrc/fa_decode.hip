@@ -22,15 +22,18 @@
 // block of 32 query heads) are laid end to end and cut into as many equal
 // ranges as there are workgroups, so ragged batches stay balanced.
 // Split kernel, one workgroup per range, walking its range unit by unit:
-//   * K and V tiles of BN = 32 NW keys go from HBM straight into LDS
-//     (buffer_load ... lds, 1 KB per wave instruction, rows swizzled as in
-//     the forward), NBUF - 1 tiles ahead; the buffer range of the head ends
-//     at its valid length, so keys past it read as zeros (never a stale or
-//     non-finite cache entry) and are masked;
-//   * wave w owns rows 32 w .. 32 w + 31 of every tile: S^T = K Q^T on
-//     v_mfma_f32_32x32x16 (lane = query head, registers = keys), an online
-//     softmax in base 2 per wave, O^T += V^T P^T with V^T from transposing
-//     LDS reads;
+//   * a unit's piece is cut into 32-key sub-tiles and wave w takes sub-tiles
+//     w, w + NW, w + 2 NW, ...: every wave streams its own keys, with no
+//     workgroup barrier, and keeps NSLOT - 1 sub-tiles in flight -- K
+//     fragments straight into registers (the A operand of S^T = K Q^T), V
+//     straight into the wave's own NSLOT-slot LDS ring (buffer_load ... lds,
+//     rows swizzled as in the forward) -- so each CU has many loads
+//     outstanding, which a bandwidth-bound stream needs;
+//   * the buffer range of the head ends at its valid length, so keys past it
+//     read as zeros (never a stale or non-finite cache entry) and are masked;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (lane = query head, registers =
+//     keys), an online softmax in base 2 per wave, O^T += V^T P^T with V^T
+//     from transposing LDS reads;
 //   * at the end of a unit's piece the waves' (m, l, O) are combined through
 //     LDS; a whole unit is written to the outputs, a piece to its workspace
 //     slot.
@@ -47,20 +50,17 @@
 namespace fa {
 namespace {
 
-template <int D, int NW_, int NBUF_>
+template <int D, int NW_, int NSLOT_>
 struct Dec {
-  static constexpr int NW = NW_, NT = 64 * NW, NBUF = NBUF_;
-  static constexpr int BN = 32 * NW;            // keys per tile, 32 per wave
+  static constexpr int NW = NW_, NT = 64 * NW, NSLOT = NSLOT_;
   static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  static constexpr int RPP = 64 / CPR;          // tile rows per 1 KB wave load
-  static constexpr int PPT = BN / RPP;          // 1 KB pieces per K (or V) tile
-  static constexpr int LPW = 2 * PPT / NW;      // loads per wave per tile (K and V)
+  static constexpr int RPP = 64 / CPR;          // sub-tile rows per 1 KB wave load
+  static constexpr int VL = 32 / RPP;           // 1 KB loads per 32-key V sub-tile
   static constexpr int EPT = D / (2 * NW);      // output elements per thread in the combine
   static constexpr int OROW = D + 1;            // padded fp32 row of a wave's O in LDS
-  static_assert(kDecodeTileKeys % BN == 0, "whole tiles per plan tile");
-  static_assert(LPW * NW == 2 * PPT && (NBUF - 2) * LPW < 64, "load split / vmcnt range");
+  static_assert(2 * VL + DS < 64, "vmcnt range");
   static_assert(EPT % 8 == 0, "combine vector width");
-  static_assert(NW * 32 * (OROW + 2) * 4 <= NBUF * 2 * BN * D * 2, "combine fits in the ring");
+  static_assert(NW * 32 * (OROW + 2) * 4 <= NW * NSLOT * 32 * D * 2, "combine fits in the ring");
 };
 
 // Valid length of batch b, clamped to [0, Nkv].
@@ -156,14 +156,15 @@ __device__ __forceinline__ void decode_block_plan(const int* kv_lens, int B, int
   }
 }
 
-template <typename T, int D, int NW, int NBUF>
+template <typename T, int D, int NW, int NSLOT>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ og, float* __restrict__ lseg,
     float* __restrict__ opart, float* __restrict__ lpart, int B, int H, int G, int Nkv, float qk_scale) {
-  using C = Dec<D, NW, NBUF>;
-  constexpr int BN = C::BN, DS = C::DS, DB = C::DB;
-  __shared__ __attribute__((aligned(16))) uint16_t ring[NBUF][2][BN * D];  // K, V tiles, swizzled rows
+  using C = Dec<D, NW, NSLOT>;
+  constexpr int DS = C::DS, DB = C::DB;
+  // Each wave's V ring: NSLOT sub-tiles of 32 swizzled rows.
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NW][NSLOT][32 * D];
   __shared__ int plan[C::NT + 2];
 
   const int lane = threadIdx.x & 63;
@@ -217,19 +218,28 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const rsrc_t krs = make_rsrc(kg + (size_t)bkv * Nkv * D, valid_bytes);
     const rsrc_t vrs = make_rsrc(vg + (size_t)bkv * Nkv * D, valid_bytes);
 
-    // Tile j of the segment (keys k0 + BN j ..) into ring slot `sl`: LDS
-    // row r, chunk c holds global chunk c ^ swz_chunk(r) of key k0 + BN j + r.
-    auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+    // This wave's sub-tiles: s = wave + NW i for i < n_mine, keys
+    // k0 + 32 s .. + 31.
+    const int n_sub = (k1 - k0 + 31) / 32;
+    const int n_mine = n_sub > wave ? (n_sub - 1 - wave) / NW + 1 : 0;
+
+    // Loads of the wave's i-th sub-tile: K fragments into a register set
+    // (lane (n, g): key n, elements 16 k + 8 g .. + 8) and V rows into a
+    // ring slot (row r, stored chunk c holds global chunk c ^ swz_chunk(r)).
+    uint4 kf[2][DS];
+    auto issue_k = [&](int i, uint4 (&kd)[DS]) __attribute__((always_inline)) {
+      const int key0 = k0 + 32 * (wave + NW * i);
+#pragma unroll
+      for (int k = 0; k < DS; ++k) kd[k] = load16(krs, ((uint32_t)(key0 + n) * D + 16 * k + 8 * g) * 2);
+    };
+    auto issue_v = [&](int i, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
+      const int key0 = k0 + 32 * (wave + NW * i);
       const int lrow = lane / C::CPR;
 #pragma unroll
-      for (int e = 0; e < C::LPW; ++e) {
-        const int tt = wave * C::LPW + e;
-        const int p = tt % C::PPT;
-        const int row = p * C::RPP + lrow;
+      for (int e = 0; e < C::VL; ++e) {
+        const int row = e * C::RPP + lrow;
         const int ch = (lane % C::CPR) ^ swz_chunk<D>(row);
-        const uint32_t off = ((uint32_t)(k0 + j * BN + row) * D + 8 * ch) * 2;
-        if (tt < C::PPT) load_lds16(krs, &ring[sl][0][p * C::RPP * D], off);
-        else load_lds16(vrs, &ring[sl][1][p * C::RPP * D], off);
+        load_lds16(vrs, vd + e * C::RPP * D, ((uint32_t)(key0 + row) * D + 8 * ch) * 2);
       }
     };
 
@@ -238,44 +248,56 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     m_run = kNegInf;
     l_run = 0.f;
 
-    // One wave's 32 keys of the tile in ring slot `sl`.
-    auto sub_block = [&](int sl, int key0) __attribute__((always_inline)) {
-      const uint16_t* kt = ring[sl][0];
-      const uint16_t* vt = ring[sl][1];
+    // One 32-key sub-tile: K fragments kd, V rows in vt, first key key0.
+    auto sub_block = [&](const uint4 (&kd)[DS], const uint16_t* __restrict__ vt, int key0)
+        __attribute__((always_inline)) {
       // two independent product chains (even and odd k), summed
       f32x16 sc = f32x16{}, sc1 = f32x16{};
 #pragma unroll
       for (int k = 0; k < DS; k += 2) {
-        sc = mma16(T{}, read_row<D>(kt, 32 * wave + n, 16 * k + 8 * g), qf[k], sc);
-        sc1 = mma16(T{}, read_row<D>(kt, 32 * wave + n, 16 * k + 16 + 8 * g), qf[k + 1], sc1);
+        sc = mma16(T{}, kd[k], qf[k], sc);
+        sc1 = mma16(T{}, kd[k + 1], qf[k + 1], sc1);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] += sc1[r];
       // register r is key key0 + 8 (r / 4) + 4 g + r % 4
       float x[16];
-      float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
         x[r] = key < k1 ? sc[r] * qk_scale : kNegInf;
-        mx = fmaxf(mx, x[r]);
       }
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float base = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
+      // Lazy reference max, as in the forward: the wave's first sub-tile sets
+      // the reference to its row max (some key of it is valid); later
+      // weights are accepted while each lane's sum of its 16 weights stays
+      // at or below 2^8, otherwise (rare) the reference is raised to the row
+      // max and O, l rescaled.  Exact: O, l and the LSE share the reference.
+      auto row_max = [&]() __attribute__((always_inline)) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        return halves_max(mx);
+      };
+      if (__builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0) m_run = fmaxf(m_run, row_max());
       float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = fast_exp2(x[r] - base);
-        psum += x[r];
+      for (int r = 0; r < 16; ++r) psum += fast_exp2(x[r] - m_run);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
+        const float m_new = fmaxf(m_run, row_max());
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+        psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) psum += fast_exp2(x[r] - m_run);
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - m_run);
       // P^T as the B operand of O^T += V^T P^T: registers 8 h .. 8 h + 7
       // are the keys of 16-key step h in the order read_tr delivers V^T's rows.
 #pragma unroll
@@ -284,31 +306,48 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
                                     pack2(T{}, x[8 * h + 4], x[8 * h + 5]), pack2(T{}, x[8 * h + 6], x[8 * h + 7]));
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          oacc[db] = mma16(T{}, read_tr<D>(vt, 32 * wave + 16 * h, 32 * db, lane), pk, oacc[db]);
+          oacc[db] = mma16(T{}, read_tr<D>(vt, 16 * h, 32 * db, lane), pk, oacc[db]);
       }
     };
 
-    const int n_tiles = (k1 - k0 + BN - 1) / BN;
+    // The wave's stream: the K fragments of sub-tile i go into register set
+    // i % 2 one sub-tile ahead, its V rows into ring slot i % NSLOT two
+    // sub-tiles ahead; step i issues K(i+1) and then V(i+2), so waiting until
+    // only the DS + 2 VL loads issued after K(i) are outstanding (in-order
+    // counter) means K(i) and V(i) have arrived while V(i+1), K(i+1) and
+    // V(i+2) stay in flight.  Only this wave reads its slots, so no barrier.
+    // The loop is unrolled over six steps so every register set and LDS
+    // offset is fixed; the slots go in as distinct __restrict__ pointers
+    // (loads into one do not alias reads of another, so the compiler does
+    // not wait for them).
+    static_assert(NSLOT == 3, "two V sub-tiles ahead");
+    uint16_t* const myring = ring[wave][0];
+    if (n_mine > 0) {
+      issue_k(0, kf[0]);
+      issue_v(0, myring);
+    }
+    if (n_mine > 1) issue_v(1, myring + 32 * D);
+    auto step = [&](int i, const uint4 (&kd)[DS], uint4 (&kn)[DS], const uint16_t* __restrict__ vt,
+                    uint16_t* __restrict__ vn2) __attribute__((always_inline)) {
+      if (i + 1 < n_mine) issue_k(i + 1, kn);
+      if (i + 2 < n_mine) issue_v(i + 2, vn2);
+      const int later = (i + 1 < n_mine ? C::VL + DS : 0) + (i + 2 < n_mine ? C::VL : 0);
+      if (later == C::VL + DS + C::VL) vm_wait<2 * C::VL + DS>();
+      else if (later == C::VL + DS) vm_wait<C::VL + DS>();
+      else vm_wait<0>();
+      sub_block(kd, vt, k0 + 32 * (wave + NW * i));
+    };
+    for (int i0 = 0; i0 < n_mine; i0 += 6) {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j)
-      if (j < n_tiles) issue(j, j);
-    for (int j = 0; j < n_tiles; ++j) {
-      // Tile j is in LDS once this wave's loads of it returned and every
-      // wave passed the barrier; the loads of later tiles may stay in flight.
-      const int ahead = min(NBUF - 2, n_tiles - 1 - j);
-      if (NBUF >= 4 && ahead >= 2) lds_barrier<(NBUF >= 4 ? 2 : 0) * C::LPW>();
-      else if (NBUF >= 3 && ahead >= 1) lds_barrier<(NBUF >= 3 ? 1 : 0) * C::LPW>();
-      else lds_barrier<0>();
-      static_assert(NBUF <= 4, "wait cases");
-      // The slot of tile j - 1 is free: every wave finished reading it
-      // before the barrier.
-      if (j + NBUF - 1 < n_tiles) issue(j + NBUF - 1, (j + NBUF - 1) % NBUF);
-      const int key0 = k0 + j * BN + 32 * wave;
-      if (key0 < k1) sub_block(j % NBUF, key0);
+      for (int jj = 0; jj < 6; ++jj) {
+        const int i = i0 + jj;
+        if (i < n_mine)
+          step(i, kf[jj % 2], kf[(jj + 1) % 2], myring + (jj % 3) * 32 * D, myring + ((jj + 2) % 3) * 32 * D);
+      }
     }
 
-    // Combine the waves through LDS (the ring is free after this barrier:
-    // the last tile's wait left no load in flight).
+    // Combine the waves through LDS (the rings are free after this barrier:
+    // every wave's last wait left no load in flight).
     __syncthreads();
     float* orow = reinterpret_cast<float*>(&ring[0][0][0]);  // [NW][32][OROW]
     float* mrow = orow + NW * 32 * C::OROW;                   // [NW][32]
@@ -327,7 +366,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
 
     const int col = threadIdx.x % 32, e0 = (threadIdx.x / 32) * C::EPT;
     if (col < nq) {
-      // Every segment holds a valid key, so some wave's max is finite.
+      // Wave 0's first sub-tile holds the segment's first key, so some
+      // wave's max is finite; a wave without keys has m = -inf, weight 0.
       float M = kNegInf;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mrow[ww * 32 + col]);
@@ -368,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
         if (e0 == 0) lpart[(size_t)slot * 32 + col] = lse;
       }
     }
-    __syncthreads();  // the next segment refills the ring
+    __syncthreads();  // the next segment refills the rings
   };
 
   // Walk the range unit by unit.
@@ -465,10 +505,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 template <typename T, int D>
 hipError_t run(const DecodeArgs& a) {
-  constexpr int NW = 4, NBUF = D == 128 ? 2 : 4;
-  using C = Dec<D, NW, NBUF>;
+  constexpr int NW = 4, NSLOT = 3;
+  using C = Dec<D, NW, NSLOT>;
   const float qk_scale = a.scale * kLog2eHost;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, NW, NBUF>), dim3((unsigned)a.parts), dim3(C::NT), 0, a.stream,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, NW, NSLOT>), dim3((unsigned)a.parts), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.kv_lens, static_cast<uint16_t*>(a.o), a.lse, a.opart,
                      a.lpart, a.B, a.H, a.G, a.Nkv, qk_scale);
