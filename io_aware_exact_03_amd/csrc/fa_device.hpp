@@ -124,6 +124,7 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 

@@ -419,11 +419,18 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   if (nbh >= 0) load_q(nbh, nqblk);
 
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
+  // A lane holds 4-element pieces of its own query's row, so storing from
+  // registers would make every store instruction touch 32 rows.  Instead
+  // each wave stages its 32 x D tile of O in its own part of the (now idle)
+  // LDS ring, swizzled row-major, and reads it back so that every store
+  // instruction writes whole rows (64 lanes x 16 bytes).
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
   const int qrow = query - qshift;  // the real query of this lane's virtual row
-  if (wave_live && qrow >= 0 && qrow < Nq) {
-    uint16_t* orow = og + head + (size_t)qrow * D;
+  if (wave_live && g == 0 && qrow >= 0 && qrow < Nq) lseg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  lds_only_barrier();  // every wave's tail has finished reading the ring
+  uint16_t* stage = &kv_lds[0][0][0] + wave * 32 * D;
+  if (wave_live) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -431,10 +438,26 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         const f32x16& v = oacc[db];
         const uint2 w = make_uint2(pack2(T{}, v[4 * rq + 0] * inv, v[4 * rq + 1] * inv),
                                    pack2(T{}, v[4 * rq + 2] * inv, v[4 * rq + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
+        *reinterpret_cast<uint2*>(stage + swz<D>(n, 32 * db + 8 * rq + 4 * g)) = w;
       }
     }
-    if (g == 0) lseg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    // Store instruction i writes rows 64 i / CPR .. of the tile: lane l takes
+    // row (64 i + l) / CPR, 16-byte chunk l % CPR.  Buffer stores: rows past
+    // Nq, or before 0 (virtual rows, whose offset wraps), fall outside the
+    // head's range and are dropped.  The lane index goes through an empty asm
+    // so the addresses are formed here, not hoisted and kept live.
+    constexpr int CPR = D / 8, ROWS = 64 / CPR;
+    const int q_first = qw0 - qshift;  // the real query of the wave's row 0
+    const rsrc_t ors = make_rsrc(og + head, (uint32_t)Nq * D * 2);
+    int li = lane;
+    asm volatile("" : "+v"(li));
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int r = ROWS * i + li / CPR, c = li % CPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + swz<D>(r, 8 * c));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), ors,
+                                             ((uint32_t)(q_first + r) * D + 8 * c) * 2, 0, 0);
+    }
   }
   };
 
