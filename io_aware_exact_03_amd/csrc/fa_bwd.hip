@@ -645,10 +645,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   auto load_rows = [&](int bh, int qblk) __attribute__((always_inline)) {
     const size_t head = (size_t)bh * (size_t)N * D;
     const rsrc_t qrs = make_rsrc(qg + head, head_bytes), dors = make_rsrc(dog + head, head_bytes);
-    const int query = qblk * C::BM + wave * 32 + n;
+    int nn = n, gg = g;  // through an empty asm: offsets formed here, not hoisted and spilled
+    asm volatile("" : "+v"(nn), "+v"(gg));
+    const int query = qblk * C::BM + wave * 32 + nn;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * g) * 2;
+      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * gg) * 2;
       qf[s] = load16(qrs, off);
       dof[s] = load16(dors, off);
     }
@@ -839,20 +841,47 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     vec(cs, cd, 32 * u_last, 0, 16, pk, std::true_type{});
     dq_gemm(kt, u_last % SUB, pk);
   }
-  // The next block's rows (the tail above was the last use of these).
-  if (nbh >= 0) load_rows(nbh, nqblk);
 
-  if (wave_live && query < N) {
-    float* row = dqg + head + (size_t)query * D;
+  // dQ through LDS, as the forward's O: each wave stages its 32 x D fp32
+  // tile in its own part of the idle ring (16-byte chunk c of row r at chunk
+  // c ^ (r mod chunks per row)), then every store instruction writes whole
+  // rows (64 lanes x 16 bytes); range-checked buffer stores drop rows past N.
+  lds_only_barrier();  // every wave's tail has finished reading the ring
+  if (wave_live) {
+    constexpr int CH = D / 4;  // 16-byte chunks per fp32 row
+    float* stage = reinterpret_cast<float*>(wave < C::NW / 2 ? &k_lds[0][0] : &v_lds[0][0]) +
+                   (wave % (C::NW / 2)) * 32 * D;
+    static_assert((C::NW / 2) * 32 * D * 4 <= C::NBUF * BN * D * 2, "dQ staging fits in half the ring");
+    // Lane values through an empty asm: the addresses are formed here
+    // rather than hoisted out of the persistent loop and kept live.
+    int nn = n, gg = g;
+    asm volatile("" : "+v"(nn), "+v"(gg));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const f32x16& v = dq[db];
-        *reinterpret_cast<float4*>(row + 32 * db + 8 * rq + 4 * g) =
+        const int c = 8 * db + 2 * rq + gg;
+        *reinterpret_cast<float4*>(stage + nn * D + 4 * (c ^ (nn % CH))) =
             make_float4(v[4 * rq] * dq_scale, v[4 * rq + 1] * dq_scale, v[4 * rq + 2] * dq_scale,
                         v[4 * rq + 3] * dq_scale);
       }
+    // The next block's rows (the tail above was the last use of the rows,
+    // and the accumulator is in LDS now).
+    if (nbh >= 0) load_rows(nbh, nqblk);
+    const rsrc_t drs = make_rsrc(dqg + head, (uint32_t)((size_t)N * D * 4));
+    int li = lane;  // through an empty asm: addresses formed here, not hoisted
+    asm volatile("" : "+v"(li));
+    constexpr int ROWS = 64 / CH;
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int r = ROWS * i + li / CH, c = li % CH;
+      const float4 x = *reinterpret_cast<const float4*>(stage + r * D + 4 * (c ^ (r % CH)));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), drs,
+                                             ((uint32_t)(qw0 + r) * D + 4 * c) * 4, 0, 0);
+    }
+  } else if (nbh >= 0) {
+    load_rows(nbh, nqblk);
   }
   };
 
