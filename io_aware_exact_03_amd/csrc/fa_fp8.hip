@@ -306,11 +306,19 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
     run(0, j_full, std::false_type{});
     run(j_full, j_end, std::true_type{});
 
-    // O = acc * (V descale / 2^8) / l, LSE = (m + log2 l) ln 2.
+    // O = acc * (V descale / 2^8) / l, LSE = (m + log2 l) ln 2.  O goes
+    // through LDS as in the 16-bit forward: each wave stages its 32 x D bf16
+    // tile in the idle ring and writes whole rows per store instruction.
     const float l_tot = halves_sum(l_run);  // sum of P 2^8
     const float inv = o_scale / l_tot;
-    if (wave_live && query < N) {
-      uint16_t* orow = og + head + (size_t)query * D;
+    if (wave_live && g == 0 && query < N) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot) - 8.f) * kLn2;
+    lds_only_barrier();  // every wave has finished reading the ring
+    if (wave_live) {
+      static_assert(C::NW * 32 * D * 2 <= 2 * C::NBUF * BN * D, "O staging fits in the ring");
+      uint16_t* stage = reinterpret_cast<uint16_t*>(wave < C::NW / 2 ? &k_lds[0][0] : &v_lds[0][0]) +
+                        (wave % (C::NW / 2)) * 32 * D;
+      int nn = n, gg = g;  // through an empty asm: addresses formed here, not hoisted
+      asm volatile("" : "+v"(nn), "+v"(gg));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -318,9 +326,21 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
           const f32x16& v = oacc[db];
           const uint2 w = make_uint2(pack2(BF16{}, v[4 * rq + 0] * inv, v[4 * rq + 1] * inv),
                                      pack2(BF16{}, v[4 * rq + 2] * inv, v[4 * rq + 3] * inv));
-          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * rq + 4 * g) = w;
+          *reinterpret_cast<uint2*>(stage + swz<D>(nn, 32 * db + 8 * rq + 4 * gg)) = w;
         }
-      if (g == 0) lseg[(size_t)bh * N + query] = (m_run + __log2f(l_tot) - 8.f) * kLn2;
+      // Store instruction i: lane l writes row (64 i + l) / CPR, chunk l % CPR;
+      // rows past N fall outside the range of the buffer stores.
+      constexpr int CPR = D / 8, ROWS = 64 / CPR;
+      const rsrc_t ors = make_rsrc(og + head, (uint32_t)N * D * 2);
+      int li = lane;
+      asm volatile("" : "+v"(li));
+#pragma unroll
+      for (int i = 0; i < 32 / ROWS; ++i) {
+        const int r = ROWS * i + li / CPR, c = li % CPR;
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + swz<D>(r, 8 * c));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), ors,
+                                               ((uint32_t)(qw0 + r) * D + 8 * c) * 2, 0, 0);
+      }
     }
   };
 
