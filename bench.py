@@ -54,11 +54,36 @@ def log(*a):
 STEP_SOURCES = ("fa_bwd.hip", "fa_device.hpp", "fa_fwd.hip", "fa_plan.hpp")
 
 
+def _code_only(text: str) -> str:
+    """The source with comments and whitespace removed: what the traffic
+    depends on (a comment edit leaves the kernels, and their traffic, as
+    they were)."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':  # string literal, kept whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for f in STEP_SOURCES:
         h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(_code_only(open(os.path.join(CSRC, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,14 +16,17 @@
 // * dK/dV computes S = Q K^T (queries x keys) so each lane owns one key:
 //   the fp32 accumulators of P and dS, packed to 16-bit, are directly the A
 //   operand of the dV and dK products, whose B operands (dO and Q with the
-//   queries as contraction index) come from transposed LDS copies whose
-//   query order matches the accumulator registers.
+//   queries as contraction index) come from transposing reads of the
+//   row-major Q and dO tiles in LDS.
 // * dQ computes S^T (keys x queries) like the forward, so each lane owns one
-//   query; dS^T is the B operand of dQ^T = K^T dS^T with K^T in LDS.
+//   query; dS^T is the B operand of dQ^T = K^T dS^T, K^T from transposing
+//   reads of the row-major K tile.
 // * Per-query LSE and Delta are lane-local in dQ and read from LDS (four
 //   16-byte broadcast reads per 32 queries) in dK/dV.
-// * The next query/key block is loaded into registers while the current one
-//   computes; LDS is double-buffered with one barrier per block.
+// * Every tile goes from global memory straight into LDS (buffer_load ...
+//   lds) through a ring of slots loaded ahead of use: Q/dO blocks in dK/dV
+//   (three slots, one block ahead, continuing across blocks), K/V tiles in
+//   dQ (four slots, three tiles ahead); both grids are persistent.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
