@@ -359,11 +359,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     float* __restrict__ dkg, float* __restrict__ dvg, int N, int n_kblk, int BHkv, int G,
     float qk_scale, float dk_scale, uint32_t ksign) {
   using C = KV<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[C::NSLOT][C::BMQ * D];   // swizzled row-major
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::NSLOT][C::BMQ * D];
-  __shared__ __attribute__((aligned(16))) uint4 x_lds[2][C::NP][4 * 64];          // fp16 P, A -> B
-  __shared__ __attribute__((aligned(16))) float lse_lds[C::NSLOT][C::BMQ];        // -LSE log2(e)
-  __shared__ __attribute__((aligned(16))) float dl_lds[C::NSLOT][C::BMQ];         // -Delta
+  // All of LDS is one variable.  The compiler matches loads into LDS
+  // against later LDS reads per variable: with the ring slots of Q in an
+  // array of their own, every read of one slot would wait for the loads
+  // just issued into the next.  The barriers' explicit waits order the
+  // loads and the reads.
+  struct Lds {
+    uint16_t q[C::NSLOT][C::BMQ * D];   // swizzled row-major
+    uint16_t dO[C::NSLOT][C::BMQ * D];
+    uint4 x[2][C::NP][4 * 64];          // fp16 P, A -> B
+    float lse[C::NSLOT][C::BMQ];        // -LSE log2(e)
+    float dl[C::NSLOT][C::BMQ];         // -Delta
+  };
+  __shared__ __attribute__((aligned(16))) Lds lds;
+  auto& q_lds = lds.q;
+  auto& do_lds = lds.dO;
+  auto& x_lds = lds.x;
+  auto& lse_lds = lds.lse;
+  auto& dl_lds = lds.dl;
 
   KVWave w;
   w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform, in a scalar register
@@ -628,7 +641,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     uint32_t qsign) {
   using C = QG<D>;
   constexpr int BN = C::BN, DS = C::DS, DB = C::DB, SUB = C::SUB, NS = C::DS;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];  // swizzled row-major
+  // Swizzled row-major tiles, one LDS variable (loads into one ring slot
+  // then do not make the compiler wait before reads of another).
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::NBUF][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::NBUF][BN * D];
 
   const int lane = threadIdx.x & 63;
@@ -835,6 +850,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
       }
     }
   }
+  // No load is in flight here (the loop's last barrier waited for all of
+  // them); saying so spares the tail and the dQ staging below a wait for
+  // loads the compiler would otherwise take as pending.
+  vm_wait<0>();
   // The wave's last (masked) sub-block; its tile is among the last four of
   // the workgroup, still in LDS.
   if (wave_live) {

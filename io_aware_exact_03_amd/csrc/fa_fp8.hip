@@ -87,8 +87,13 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
                                                       float qk_scale, float o_scale, uint32_t qsign) {
   using C = Fp8<D>;
   constexpr int BN = C::BN, DS = C::DS, DB = C::DB;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[C::NBUF][BN * D];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[C::NBUF][BN * D];
+  // One LDS variable for both rings: the compiler matches loads into LDS
+  // against later LDS reads per variable, and would make the reads of one
+  // slot wait for the loads just issued into another.  The barriers' explicit
+  // waits order loads and reads.
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][C::NBUF][BN * D];
+  auto& k_lds = kv_lds[0];
+  auto& v_lds = kv_lds[1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
 
     // Tile j into ring slot sl: LDS row r, stored chunk c holds global chunk
     // c ^ fp8_swz(r) of key j BN + r.  Rows past N read as zeros.
-    auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+    auto issue = [&](int j, uint8_t* __restrict__ kd, uint8_t* __restrict__ vd) __attribute__((always_inline)) {
       const int lrow = lane / C::CPR;
 #pragma unroll
       for (int e = 0; e < C::LPW; ++e) {
@@ -134,8 +139,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
         const int row = p * C::RPP + lrow;
         const int ch = (lane % C::CPR) ^ fp8_swz<D>(row);
         const uint32_t off = (uint32_t)(j * BN + row) * D + 16 * ch;
-        if (t < C::PPT) load_lds16(krs, &k_lds[sl][p * C::RPP * D], off);
-        else load_lds16(vrs, &v_lds[sl][p * C::RPP * D], off);
+        if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
+        else load_lds16(vrs, vd + p * C::RPP * D, off);
       }
     };
 
@@ -163,11 +168,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
       return r;
     };
 
-    // Raw scores S^T (before the scale) of the two 32-key blocks of the
-    // tile in slot sl; register r of block b is key 32 b + 8 (r / 4) + 4 g
-    // + r % 4 of the tile.
-    auto s_gemm = [&](int sl, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-      const uint8_t* kt = k_lds[sl];
+    // Raw scores S^T (before the scale) of the two 32-key blocks of the K
+    // tile kt; register r of block b is key 32 b + 8 (r / 4) + 4 g + r % 4
+    // of the tile.
+    auto s_gemm = [&](const uint8_t* __restrict__ kt, f32x16 (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         sc[b] = f32x16{};
@@ -252,33 +256,37 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
     static_assert(C::NBUF == 4, "ring of four tiles, loads three ahead of the scores");
 #pragma unroll
     for (int j = 0; j < C::NBUF - 1; ++j)
-      if (j < j_end) issue(j, j);
+      if (j < j_end) issue(j, k_lds[j], v_lds[j]);
     // prologue: tile 0 in LDS, its scores
     if (j_end > 2) lds_barrier<2 * C::LPW>();
     else if (j_end > 1) lds_barrier<C::LPW>();
     else lds_barrier<0>();
     f32x16 sA[2], sB[2];
-    s_gemm(0, sA);
+    s_gemm(k_lds[0], sA);
     // One iteration; the loop runs two per trip so the score registers
     // alternate without copies.
-    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto mask_tag) __attribute__((always_inline)) {
+    // The ring slots arrive as distinct __restrict__ pointers: with that, the
+    // compiler does not make the reads of one slot wait for the loads just
+    // issued into another.
+    auto step_in = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint8_t* __restrict__ kn,
+                       const uint8_t* __restrict__ vt, uint8_t* __restrict__ kl, uint8_t* __restrict__ vl,
+                       auto mask_tag) __attribute__((always_inline)) {
       // tile j + 1 must be in LDS: the loads still allowed in flight are
       // those of tile j + 2
       if (j + 1 < j_end) {
         if (j + 2 < j_end) lds_barrier<C::LPW>();
         else lds_barrier<0>();
       }
-      if (j + 3 < j_end) issue(j + 3, (j + 3) % C::NBUF);
+      if (j + 3 < j_end) issue(j + 3, kl, vl);
       // Every wave runs every tile of the block: a tile wholly past a
       // wave's causal limit is fully masked (P = 0), which costs less than
       // branching around the accumulators.
-      if (j + 1 < j_end) s_gemm((j + 1) % C::NBUF, nxt);
+      if (j + 1 < j_end) s_gemm(kn, nxt);
       // V^T fragments: the first PF are read before the vector work, which
       // hides their latency (all of them would not fit in registers at
       // d = 128), the rest behind the first PV products.
       constexpr int PF = DB > 2 ? 2 : DB;
       v8i vf[DB];
-      const uint8_t* vt = v_lds[j % C::NBUF];
 #pragma unroll
       for (int db = 0; db < PF; ++db) vf[db] = vfrag(vt, db);
       const v8i pk = softmax(cur, j, mask_tag);
@@ -286,6 +294,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
       for (int db = PF; db < DB; ++db) vf[db] = vfrag(vt, db);
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = mma_fp8(vf[db], pk, oacc[db]);
+    };
+    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto mask_tag) __attribute__((always_inline)) {
+      step_in(j, cur, nxt, k_lds[(j + 1) % C::NBUF], v_lds[j % C::NBUF], k_lds[(j + 3) % C::NBUF],
+              v_lds[(j + 3) % C::NBUF], mask_tag);
     };
     // Tiles every key of which every query of the block sees run without
     // the mask; the rest (the diagonal tiles, the sequence tail) with it.
@@ -305,6 +317,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
     const int j_full = min(j_end, CAUSAL ? q0 / BN : N / BN);
     run(0, j_full, std::false_type{});
     run(j_full, j_end, std::true_type{});
+    // No tile load is in flight (none is issued for the last three tiles, and
+    // the last barrier waited for all); saying so spares the O staging below
+    // a wait for loads the compiler would otherwise take as pending.
+    vm_wait<0>();
 
     // O = acc * (V descale / 2^8) / l, LSE = (m + log2 l) ln 2.  O goes
     // through LDS as in the 16-bit forward: each wave stages its 32 x D bf16

@@ -118,14 +118,58 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     for (int s = 0; s < DS; ++s) qf[s] = load16(rs, ((uint32_t)q * D + 16 * s + 8 * g) * 2);
   };
 
+  // ---- tile loads: global -> LDS ------------------------------------------
+  // Piece t (0 .. 2 PPT - 1) = wave LPW + e holds RPP tile rows of K
+  // (t < PPT) or V.  Lane l fills LDS bytes 16 l of the piece: row l / CPR,
+  // stored chunk l % CPR, which holds the row's logical chunk
+  // (l % CPR) ^ swz_chunk(row).  Rows past Nk read as zeros.
+  auto issue_tile = [&](const rsrc_t& krs, const rsrc_t& vrs, int j, uint16_t* __restrict__ kd,
+                        uint16_t* __restrict__ vd) __attribute__((always_inline)) {
+    const int lrow = lane / C::CPR;
+#pragma unroll
+    for (int e = 0; e < C::LPW; ++e) {
+      const int t = wave * C::LPW + e;
+      const int p = t % C::PPT;
+      const int row = p * C::RPP + lrow;
+      const int chunk = (lane % C::CPR) ^ swz_chunk<D>(row);
+      const uint32_t off = ((uint32_t)(j * BN + row) * D + 8 * chunk) * 2;
+      if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
+      else load_lds16(vrs, vd + p * C::RPP * D, off);
+    }
+  };
+  auto kv_rsrc = [&](int bh, rsrc_t* krs, rsrc_t* vrs) __attribute__((always_inline)) {
+    const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)Nk * D;  // shared by G query heads
+    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
+    *krs = make_rsrc(kg + kvhead, head_bytes);
+    *vrs = make_rsrc(vg + kvhead, head_bytes);
+  };
+  // Tiles query block qblk reads: up to the diagonal sub-block of its last
+  // wave with live queries (causal), else to the key tail.
+  auto tiles_of = [&](int qblk) __attribute__((always_inline)) {
+    const int q0 = qblk * C::BM;
+    const int last_live = min(C::NW - 1, (Nq + qshift - 1 - q0) / 32);  // q0 < Nq + qshift always
+    const int u_end = CAUSAL ? ((q0 + koff) / 32 + last_live) : ((Nk + 31) / 32 - 1);
+    return u_end / SUB + 1;
+  };
+  // A block's first three tiles go to ring slots 0-2.  They are issued
+  // before the block starts: by the block before it, as soon as its last
+  // tile reads are done, so they arrive under its epilogue.
+  auto issue_first = [&](int bh, int qblk) __attribute__((always_inline)) {
+    rsrc_t krs, vrs;
+    kv_rsrc(bh, &krs, &vrs);
+    const int je = tiles_of(qblk);
+    issue_tile(krs, vrs, 0, k_lds[0], v_lds[0]);
+    if (je > 1) issue_tile(krs, vrs, 1, k_lds[1], v_lds[1]);
+    if (je > 2) issue_tile(krs, vrs, 2, k_lds[2], v_lds[2]);
+  };
+
   // One query block of one (batch, head), start to finish; (nbh, nqblk) is
-  // the block this workgroup runs next (nbh < 0: none).
+  // the block this workgroup runs next (nbh < 0: none).  Its first three
+  // tiles and its Q fragments are in flight when it starts.
   auto block = [&](int bh, int qblk, int nbh, int nqblk) __attribute__((always_inline)) {
   const size_t head = (size_t)bh * (size_t)Nq * D;
-  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)Nk * D;  // shared by G query heads
-  const uint32_t head_bytes = (uint32_t)Nk * D * 2;
-  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
-  const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
+  rsrc_t krs, vrs;
+  kv_rsrc(bh, &krs, &vrs);
 
   const int q0 = qblk * C::BM;
   const int qw0 = q0 + 32 * wave;  // first query of this wave
@@ -144,28 +188,11 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   const int n_sub = (Nk + 31) / 32;
   const bool wave_live = qw0 < NqV;
   const int u_last = !wave_live ? -1 : (CAUSAL ? (qw0 + koff) / 32 : n_sub - 1);
-  const int last_live = min(C::NW - 1, (NqV - 1 - q0) / 32);  // q0 < NqV always
-  const int u_end = CAUSAL ? ((q0 + koff) / 32 + last_live) : (n_sub - 1);
-  const int j_end = u_end / SUB + 1;  // tiles this workgroup reads
+  const int j_end = tiles_of(qblk);  // tiles this workgroup reads
   const int key_lim = CAUSAL ? min(query + koff + 1, Nk) : Nk;
 
-  // ---- tile loads: global -> LDS ------------------------------------------
-  // Piece t (0 .. 2 PPT - 1) = wave LPW + e holds RPP tile rows of K
-  // (t < PPT) or V.  Lane l fills LDS bytes 16 l of the piece: row l / CPR,
-  // stored chunk l % CPR, which holds the row's logical chunk
-  // (l % CPR) ^ swz_chunk(row).  Rows past Nk read as zeros.
-  auto issue = [&](int j, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
-    const int lrow = lane / C::CPR;
-#pragma unroll
-    for (int e = 0; e < C::LPW; ++e) {
-      const int t = wave * C::LPW + e;
-      const int p = t % C::PPT;
-      const int row = p * C::RPP + lrow;
-      const int chunk = (lane % C::CPR) ^ swz_chunk<D>(row);
-      const uint32_t off = ((uint32_t)(j * BN + row) * D + 8 * chunk) * 2;
-      if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
-      else load_lds16(vrs, vd + p * C::RPP * D, off);
-    }
+  auto issue = [&](int j, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+    issue_tile(krs, vrs, j, kd, vd);
   };
 
   f32x16 oacc[DB];
@@ -346,15 +373,9 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     }
   };
 
-  // ---- prologue: tiles 0..2 in flight, wait for 0 and 1 ------------------
-  issue(0, k_lds[0], v_lds[0]);
-  if (j_end > 1) issue(1, k_lds[1], v_lds[1]);
-  if (j_end > 2) {
-    issue(2, k_lds[2], v_lds[2]);
-    lds_barrier<C::LPW>();
-  } else {
-    lds_barrier<0>();
-  }
+  // ---- prologue: tiles 0..2 and Q were issued before the block; wait for
+  // all of them (and for the previous block's O stores, issued after them).
+  lds_barrier<0>();
   if (qsign != 0) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -392,6 +413,11 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       }
     }
   }
+  // The loop's last barrier waited for every load (no tile load follows the
+  // final three tiles), so this wait costs nothing; it tells the compiler
+  // that no tile load is pending, which spares the LDS accesses below a
+  // wait for the global loads issued after them.
+  vm_wait<0>();
   // The wave's last two sub-blocks: the PV product of u_last - 1 and the
   // masked weights and PV product of u_last.  Their tiles are among the
   // last five of the workgroup (a wave's last sub-block is at most seven
@@ -412,24 +438,33 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     pv_gemm(vt, u_last % SUB, pk);
   }
 
-  // The next block's Q (the tail above was the last use of this block's).
-  // Issued after the tail, whose LDS reads the compiler makes wait for every
-  // outstanding load, so they arrive under the epilogue and the next
-  // block's tile wait.
+  // The next block's Q (the tail above was the last use of this block's),
+  // in flight during the epilogue.
   if (nbh >= 0) load_q(nbh, nqblk);
 
   // ---- epilogue: one divide per row, store O and the natural-log LSE ------
   // A lane holds 4-element pieces of its own query's row, so storing from
   // registers would make every store instruction touch 32 rows.  Instead
-  // each wave stages its 32 x D tile of O in its own part of the (now idle)
-  // LDS ring, swizzled row-major, and reads it back so that every store
-  // instruction writes whole rows (64 lanes x 16 bytes).
+  // each wave stages its 32 x D tile of O in its own part of ring slots 3
+  // and 4 (idle now: the next block's first tiles go to slots 0-2 as soon
+  // as every wave's tail has read the ring), swizzled row-major, and reads
+  // it back so that every store instruction writes whole rows (64 lanes x
+  // 16 bytes).
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
   const int qrow = query - qshift;  // the real query of this lane's virtual row
   if (wave_live && g == 0 && qrow >= 0 && qrow < Nq) lseg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   lds_only_barrier();  // every wave's tail has finished reading the ring
-  uint16_t* stage = &kv_lds[0][0][0] + wave * 32 * D;
+  static_assert(4 * 32 * D <= 2 * BN * D, "four waves' O tiles fit in two ring slots");
+  uint16_t* stage = (wave < 4 ? v_lds[3] : k_lds[3]) + (wave % 4) * 32 * D;
+  // Read-back instruction i covers rows 64 i / CPR .. of the tile: lane l
+  // takes row (64 i + l) / CPR, 16-byte chunk l % CPR.  A wave reads back
+  // only its own tile, so no barrier sits between its writes and reads.
+  // Both come before the next block's tile loads, which the compiler would
+  // otherwise make them wait for (it cannot tell the LDS ranges apart).
+  constexpr int CPR = D / 8, ROWS = 64 / CPR;
+  uint4 ox[32 / ROWS];
+  int li = lane;
   if (wave_live) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -441,21 +476,26 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         *reinterpret_cast<uint2*>(stage + swz<D>(n, 32 * db + 8 * rq + 4 * g)) = w;
       }
     }
-    // Store instruction i writes rows 64 i / CPR .. of the tile: lane l takes
-    // row (64 i + l) / CPR, 16-byte chunk l % CPR.  Buffer stores: rows past
-    // Nq, or before 0 (virtual rows, whose offset wraps), fall outside the
-    // head's range and are dropped.  The lane index goes through an empty asm
-    // so the addresses are formed here, not hoisted and kept live.
-    constexpr int CPR = D / 8, ROWS = 64 / CPR;
-    const int q_first = qw0 - qshift;  // the real query of the wave's row 0
-    const rsrc_t ors = make_rsrc(og + head, (uint32_t)Nq * D * 2);
-    int li = lane;
+    // The lane index goes through an empty asm so the addresses are formed
+    // here, not hoisted and kept live.
     asm volatile("" : "+v"(li));
 #pragma unroll
     for (int i = 0; i < 32 / ROWS; ++i) {
       const int r = ROWS * i + li / CPR, c = li % CPR;
-      const uint4 x = *reinterpret_cast<const uint4*>(stage + swz<D>(r, 8 * c));
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), ors,
+      ox[i] = *reinterpret_cast<const uint4*>(stage + swz<D>(r, 8 * c));
+    }
+  }
+  if (nbh >= 0) issue_first(nbh, nqblk);
+  if (wave_live) {
+    // Buffer stores, whole rows per instruction: rows past Nq, or before 0
+    // (virtual rows, whose offset wraps), fall outside the head's range and
+    // are dropped.
+    const int q_first = qw0 - qshift;  // the real query of the wave's row 0
+    const rsrc_t ors = make_rsrc(og + head, (uint32_t)Nq * D * 2);
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int r = ROWS * i + li / CPR, c = li % CPR;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, ox[i]), ors,
                                              ((uint32_t)(q_first + r) * D + 8 * c) * 2, 0, 0);
     }
   }
@@ -479,7 +519,10 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     return true;
   };
   int L = xcd_remap(blockIdx.x, gridDim.x), t = 0, bh = -1, qb = -1;
-  if (block_at(L, 0, &bh, &qb)) load_q(bh, qb);
+  if (block_at(L, 0, &bh, &qb)) {
+    load_q(bh, qb);
+    issue_first(bh, qb);
+  }
   while (bh >= 0) {  // one call site: the block body is large
     int nbh = -1, nqb = -1;
     if (block_at(L, t + 1, &nbh, &nqb)) {
@@ -490,8 +533,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       if (!block_at(L, 0, &nbh, &nqb)) nbh = -1;
     }
     block(bh, qb, nbh, nqb);
-    // The next block's loads reuse the LDS buffers; this block's O stores
-    // may still be in flight.
+    // Every wave has read its staged O before the next block's tile loads
+    // reach slots 3 and 4; the O stores may still be in flight.
     lds_only_barrier();
     bh = nbh;
     qb = nqb;
