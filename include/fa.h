@@ -96,7 +96,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   3. per Q block:  dQ += scale * dS K                      -> dq
  * dq, dk, dv are float32 [B,H,N,d] and are fully overwritten (no zeroing
  * needed).  delta_ws is caller-owned scratch that holds Delta afterwards.
- * dtype f16 and bf16 are supported; f32 returns FA_ERR_UNSUPPORTED.
+ * dtype f16 and bf16 are supported; f32 returns FA_ERR_UNSUPPORTED.  The
+ * fp32 gradients of one head must stay below 2 GiB including the last
+ * block's padding, (N + 255) * d * 4 < 2^31 (N <= 4,194,048 at d = 128),
+ * else FA_ERR_UNSUPPORTED.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, float* delta_ws, float* dq, float* dk, float* dv,
@@ -302,6 +305,34 @@ int fa_causal_stages(int row0, int row_end, int bn, int n, int* s1_end, int* s2_
  * Pure host function; FA_ERR_UNSUPPORTED for unsupported d/dtype.
  */
 int fa_fwd_tile(int d, int dtype, int* bm, int* bn, int* waves);
+
+/*
+ * Measured ceilings of the chip, for reporting attention kernels against what
+ * the hardware sustains as well as against its published peaks ("Flash
+ * Attention -- five lessons converging into 80 lines", brianyu43.github.io,
+ * Lesson 3: bandwidth as a fraction of what the memory delivers).  They
+ * compute nothing of attention.
+ *
+ * fa_ceiling_mfma: `workgroups` workgroups of `waves` (4 or 8) wavefronts;
+ * every wave issues iters x 8 independent v_mfma_f32_32x32x16_bf16 products
+ * (32768 flops each), so the launch performs
+ * workgroups * waves * iters * 8 * 32768 flops.  sink: caller-owned float
+ * [workgroups * waves * 64] (one value per lane, so no product is dead).
+ * clocks: NULL or caller-owned uint64 [2 * workgroups]; per workgroup, the
+ * shader-clock counter (s_memtime) and the 100 MHz constant clock
+ * (s_memrealtime) elapsed over its loop.  FA_ERR_ARG for null sink, sizes
+ * < 1 or waves not 4/8; FA_ERR_ALIGN for unaligned pointers.
+ *
+ * fa_ceiling_copy: copies `bytes` (a multiple of 16, > 0) from src to dst
+ * with 16-byte accesses over a fixed grid (8 workgroups per CU); HBM traffic
+ * 2 * bytes.  fa_ceiling_read: reads `bytes` once and writes
+ * fa_ceiling_read_sink_bytes() bytes of per-lane results to sink.  Both
+ * return FA_ERR_ARG / FA_ERR_ALIGN like the attention entry points.
+ */
+int fa_ceiling_mfma(float* sink, unsigned long long* clocks, int workgroups, int waves, int iters, void* stream);
+int fa_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
+int fa_ceiling_read(const void* src, size_t bytes, void* sink, void* stream);
+size_t fa_ceiling_read_sink_bytes(void);
 
 #ifdef __cplusplus
 }

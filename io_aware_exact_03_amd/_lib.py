@@ -36,6 +36,10 @@ SIGNATURES = {
     "fa_last_hip_error": (_i, []),
     "fa_causal_stages": (_i, [_i, _i, _i, _i, _ip, _ip]),
     "fa_fwd_tile": (_i, [_i, _i, _ip, _ip, _ip]),
+    "fa_ceiling_mfma": (_i, [_vp, _vp, _i, _i, _i, _vp]),
+    "fa_ceiling_copy": (_i, [_vp, _vp, ctypes.c_size_t, _vp]),
+    "fa_ceiling_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
+    "fa_ceiling_read_sink_bytes": (ctypes.c_size_t, []),
 }
 
 _lib = None

@@ -42,6 +42,10 @@ int check_shape(int B, int H, int N, int d, int dtype, int causal, float scale) 
 
 }  // namespace
 
+namespace fa {
+void record_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace fa
+
 extern "C" {
 
 const char* fa_strerror(int status) {
@@ -132,6 +136,10 @@ static int bwd_common(int stage, const void* q, const void* k, const void* v, co
   if (st != FA_OK) return st;
   if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit MFMA only
+  // dQ, dK, dV are fp32: one head of them is twice the bytes of a 16-bit
+  // head, and the kernels' 32-bit buffer offsets also cover the padded rows
+  // of the last block (up to 255 past N) before the range check drops them.
+  if ((long long)(N + 255) * d * 4 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, o, dout, lse, delta_ws, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;

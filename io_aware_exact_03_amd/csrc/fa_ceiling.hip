@@ -1,0 +1,135 @@
+// fa_ceiling.hip -- what the chip itself sustains, measured by the same
+// library the attention kernels live in: a matrix-core-only loop (the
+// ceiling a dense bf16 contraction can reach) and streaming copy / read
+// loops (the ceiling an HBM-bound kernel can reach).  Attention kernels are
+// reported as a fraction of the published peaks and of these measured ones
+// ("Flash Attention -- five lessons converging into 80 lines",
+// brianyu43.github.io, Lesson 3: effective bandwidth as a fraction of what
+// the memory can deliver).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// Matrix cores alone: every wave keeps NACC independent 32x32 fp32
+// accumulators and issues v_mfma_f32_32x32x16_bf16 into them round-robin, so
+// no product waits for the one before it.  The operands are built from the
+// lane index (nothing for the compiler to fold) and every accumulator feeds
+// the value written at the end, so no product is dead.  Wave 0 of each
+// workgroup also records the shader-clock and constant-clock (100 MHz)
+// counters at its start and end.  At most eight waves per workgroup (two
+// per SIMD), which leaves 256 registers per lane: no spills.
+template <int NACC>
+__global__ __launch_bounds__(512) void ceiling_mfma_kernel(float* __restrict__ sink, unsigned long long* __restrict__ clocks, int iters) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t w = 0x3F803F80u ^ (lane << 3);  // bf16 pairs near 1.0
+  const uint4 a = make_uint4(w, w ^ 0x10001u, w ^ 0x20002u, w ^ 0x30003u);
+  const uint4 b = make_uint4(w ^ 0x40004u, w, w ^ 0x50005u, w ^ 0x60006u);
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = f32x16{};
+  const bool timer = threadIdx.x == 0;
+  unsigned long long t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = mma16(BF16{}, a, b, acc[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (timer && clocks != nullptr) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// Streaming copy, 16 bytes per lane per access, grid-stride, four accesses
+// in flight per lane.
+__global__ __launch_bounds__(256) void ceiling_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
+    dst[i] = x0;
+    dst[i + stride] = x1;
+    dst[i + 2 * stride] = x2;
+    dst[i + 3 * stride] = x3;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// Streaming read: every 16-byte chunk is loaded once and folded into an XOR
+// per lane, written to sink (one word per lane) so no load is dead.
+__global__ __launch_bounds__(256) void ceiling_read_kernel(const uint4* __restrict__ src, size_t n,
+                                                           uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
+    acc ^= (x0.x ^ x0.y ^ x0.z ^ x0.w) ^ (x1.x ^ x1.y ^ x1.z ^ x1.w) ^ (x2.x ^ x2.y ^ x2.z ^ x2.w) ^
+           (x3.x ^ x3.y ^ x3.z ^ x3.w);
+  }
+  for (; i < n; i += stride) acc ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+}  // namespace fa
+
+namespace {
+constexpr int kStreamGrid = 256 * 8;  // eight workgroups per CU
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  fa::record_hip_error((int)e);
+  return FA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+int fa_ceiling_mfma(float* sink, unsigned long long* clocks, int workgroups, int waves, int iters, void* stream) {
+  if (sink == nullptr) return FA_ERR_ARG;
+  if (workgroups < 1 || iters < 1 || (waves != 4 && waves != 8)) return FA_ERR_ARG;
+  if (!aligned16(sink) || (clocks != nullptr && !aligned16(clocks))) return FA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Eight accumulators per wave (128 registers) leave room for two waves
+  // per SIMD.
+  hipLaunchKernelGGL(fa::ceiling_mfma_kernel<8>, dim3((unsigned)workgroups), dim3((unsigned)(64 * waves)), 0, s,
+                     sink, clocks, iters);
+  return launch_status(hipGetLastError());
+}
+
+int fa_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes == 0 || bytes % 16 != 0) return FA_ERR_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return FA_ERR_ALIGN;
+  hipLaunchKernelGGL(fa::ceiling_copy_kernel, dim3(kStreamGrid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), bytes / 16);
+  return launch_status(hipGetLastError());
+}
+
+int fa_ceiling_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0) return FA_ERR_ARG;
+  if (!aligned16(src) || !aligned16(sink)) return FA_ERR_ALIGN;
+  hipLaunchKernelGGL(fa::ceiling_read_kernel, dim3(kStreamGrid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  return launch_status(hipGetLastError());
+}
+
+size_t fa_ceiling_read_sink_bytes(void) { return (size_t)kStreamGrid * 256 * 4; }
+
+}  // extern "C"

@@ -105,6 +105,9 @@ struct Fp8Args {
   hipStream_t stream;
 };
 
+// Keep a failed launch's hipError_t for fa_last_hip_error() (calling thread).
+void record_hip_error(int e);
+
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0 = all three launches in order; 1 = Delta, 2 = dK/dV, 3 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, int stage);

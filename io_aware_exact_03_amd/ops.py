@@ -31,10 +31,33 @@ def _check_qkv(*ts: torch.Tensor):
         raise ValueError(f"unsupported dtype {ref.dtype}")
 
 
+def _check_out(t, shape, dtype, device, name: str):
+    """A caller-supplied output, workspace or auxiliary input must be exactly
+    what the kernels address: the given shape and dtype, contiguous, on the
+    inputs' device.  Anything smaller or strided would be written (or read)
+    past its allocation or in the wrong order."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _check_bytes(t, nbytes: int, device, name: str):
+    """A byte workspace: contiguous, on the device, at least nbytes long."""
+    if t is None:
+        return
+    if t.device != device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: expected a contiguous buffer of at least {nbytes} bytes on {device}")
+
+
 def fwd(q, k, v, scale: float, causal: bool, out=None, lse=None):
     """Fused forward: returns (O [B,H,N,d] in q.dtype, LSE float32 [B,H,N])."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -45,10 +68,22 @@ def fwd(q, k, v, scale: float, causal: bool, out=None, lse=None):
     return out, lse
 
 
+def _check_bwd_bufs(q, lse, delta, dq, dk, dv, kv_shape):
+    B, H, N, d = q.shape
+    if lse is None:
+        raise ValueError("lse: the forward's LSE is required")
+    _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
+    _check_out(delta, (B, H, N), torch.float32, q.device, "delta")
+    _check_out(dq, (B, H, N, d), torch.float32, q.device, "dq")
+    _check_out(dk, kv_shape, torch.float32, q.device, "dk")
+    _check_out(dv, kv_shape, torch.float32, q.device, "dv")
+
+
 def bwd(q, k, v, o, dout, lse, scale: float, causal: bool, delta=None, dq=None, dk=None, dv=None):
     """Backward: returns (dQ, dK, dV float32 [B,H,N,d], Delta float32 [B,H,N])."""
     _check_qkv(q, k, v, o, dout)
     B, H, N, d = q.shape
+    _check_bwd_bufs(q, lse, delta, dq, dk, dv, (B, H, N, d))
     f32 = dict(dtype=torch.float32, device=q.device)
     delta = torch.empty((B, H, N), **f32) if delta is None else delta
     dq = torch.empty((B, H, N, d), **f32) if dq is None else dq
@@ -66,6 +101,10 @@ def bwd_stage(stage: int, q, k, v, o, dout, lse, scale: float, causal: bool, del
     buffers; stages 1, 2, 3 in order equal one bwd() call."""
     _check_qkv(q, k, v, o, dout)
     B, H, N, d = q.shape
+    for name, t in (("delta", delta), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            raise ValueError(f"{name}: bwd_stage writes into caller buffers")
+    _check_bwd_bufs(q, lse, delta, dq, dk, dv, (B, H, N, d))
     st = _lib.load().fa_bwd_stage(int(stage), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype],
@@ -89,6 +128,8 @@ def fwd_gqa(q, k, v, scale: float, causal: bool, out=None, lse=None):
     """Grouped-query forward: q [B,H,N,d], k and v [B,Hkv,N,d]; query head h
     reads K/V head h // (H // Hkv).  Returns (O [B,H,N,d], LSE [B,H,N])."""
     B, H, Hkv, N, d = _check_gqa(q, k, v)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -111,6 +152,8 @@ def fwd_chunk(q, k, v, scale: float, causal: bool, out=None, lse=None):
     Hkv, Nk = k.shape[1], k.shape[2]
     if k.shape[0] != B or k.shape[3] != d or H % Hkv != 0:
         raise ValueError(f"k, v shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H, Nq), torch.float32, q.device, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -125,6 +168,7 @@ def bwd_gqa(q, k, v, o, dout, lse, scale: float, causal: bool, delta=None, dq=No
     """Backward of fwd_gqa: returns (dQ [B,H,N,d], dK and dV [B,Hkv,N,d],
     all float32, each dK/dV summed over its group, Delta [B,H,N])."""
     B, H, Hkv, N, d = _check_gqa(q, k, v, o, dout)
+    _check_bwd_bufs(q, lse, delta, dq, dk, dv, (B, Hkv, N, d))
     f32 = dict(dtype=torch.float32, device=q.device)
     delta = torch.empty((B, H, N), **f32) if delta is None else delta
     dq = torch.empty((B, H, N, d), **f32) if dq is None else dq
@@ -178,11 +222,14 @@ def decode(q, k_cache, v_cache, scale: float, kv_lens=None, n_parts=None, out=No
         raise ValueError("kv_lens must be a contiguous int32 tensor of B values on q's device")
     if n_parts is None:
         n_parts = decode_plan(B, H, Hkv, Nkv, d)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H), torch.float32, q.device, "lse")
+    need = decode_workspace_bytes(B, H, Hkv, d, n_parts)
+    _check_bytes(ws, need, q.device, "ws")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    need = decode_workspace_bytes(B, H, Hkv, d, n_parts)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib.load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -219,6 +266,8 @@ def fwd_fp8(q8, k8, v8, descales, scale: float, causal: bool, out=None, lse=None
     Hkv = k8.shape[1]
     if k8.shape != v8.shape or k8.shape[0] != B or k8.shape[2:] != q8.shape[2:] or H % Hkv != 0:
         raise ValueError(f"k, v shape {tuple(k8.shape)} does not group q shape {tuple(q8.shape)}")
+    _check_out(out, (B, H, N, d), torch.bfloat16, q8.device, "out")
+    _check_out(lse, (B, H, N), torch.float32, q8.device, "lse")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
@@ -240,6 +289,9 @@ def fwd_fa1(q, k, v, scale: float, causal: bool, out=None, lse=None, ws=None):
     final running state afterwards."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
+    _check_bytes(ws, fa1_workspace_bytes(B, H, N, d), q.device, "ws")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -274,6 +326,10 @@ def naive_fwd(q, k, v, scale: float, causal: bool, out=None, lse=None, s_ws=None
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     ws_dtype = torch.float32 if q.dtype == torch.float32 else torch.float16
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
+    _check_out(s_ws, (B, H, N, N), ws_dtype, q.device, "s_ws")
+    _check_out(p_ws, (B, H, N, N), ws_dtype, q.device, "p_ws")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -302,3 +358,39 @@ def fwd_tile(d: int, dtype: torch.dtype):
     _lib.check(_lib.load().fa_fwd_tile(d, DTYPE_CODES[dtype], ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(w)),
                "fa_fwd_tile")
     return bm.value, bn.value, w.value
+
+
+# ---------------------------------------------------------------------------
+# Measured ceilings of the chip (no attention arithmetic).
+# ---------------------------------------------------------------------------
+def ceiling_mfma(workgroups: int, waves: int, iters: int, device="cuda", clocks: bool = False):
+    """Launch the matrix-core-only loop; returns (sink, clocks or None).  The
+    launch performs workgroups * waves * iters * 8 * 32768 flops."""
+    sink = torch.empty(workgroups * waves * 64, dtype=torch.float32, device=device)
+    clk = torch.empty(2 * workgroups, dtype=torch.int64, device=device) if clocks else None
+    st = _lib.load().fa_ceiling_mfma(sink.data_ptr(), clk.data_ptr() if clk is not None else None, workgroups,
+                                     waves, iters, _stream(sink))
+    _lib.check(st, "fa_ceiling_mfma")
+    return sink, clk
+
+
+def ceiling_mfma_flops(workgroups: int, waves: int, iters: int) -> float:
+    return float(workgroups) * waves * iters * 8 * 32768
+
+
+def ceiling_copy(src, dst):
+    """Copy src into dst (same byte size, a multiple of 16) with the
+    streaming-copy kernel; HBM traffic 2 x bytes."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous and of equal byte size")
+    _lib.check(_lib.load().fa_ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src)), "fa_ceiling_copy")
+
+
+def ceiling_read(src, sink=None):
+    """Read every byte of src once (streaming-read kernel); returns the sink."""
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(int(_lib.load().fa_ceiling_read_sink_bytes()), dtype=torch.uint8, device=src.device)
+    _lib.check(_lib.load().fa_ceiling_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src)), "fa_ceiling_read")
+    return sink

@@ -66,6 +66,20 @@ def test_head_size_limit(lib):
     assert lib.fa_bwd(*args, 1, 1, (1 << 31) // (64 * 2), 64, 1.0, 0, 1, None) == FA_ERR_UNSUPPORTED
 
 
+def test_bwd_fp32_gradient_head_limit(lib):
+    # dQ, dK, dV are fp32 [N, d] per head; the kernels' 32-bit offsets also
+    # reach the last block's padded rows (up to 255 past N), so the backward
+    # needs (N + 255) * d * 4 < 2^31 even where the 16-bit inputs are smaller.
+    # d = 128, N = 8,388,607 passes the 16-bit input limit but would wrap.
+    args = [A] * 10
+    assert lib.fa_bwd(*args, 1, 1, 8_388_607, 128, 1.0, 0, 2, None) == FA_ERR_UNSUPPORTED
+    n_first_bad = (1 << 31) // (128 * 4) - 255
+    for n in (n_first_bad, n_first_bad + 1):
+        assert lib.fa_bwd(*args, 1, 1, n, 128, 1.0, 1, 2, None) == FA_ERR_UNSUPPORTED
+        assert lib.fa_bwd_gqa(*args[:6], *args[6:], 1, 4, 2, n, 128, 1.0, 1, 1, None) == FA_ERR_UNSUPPORTED
+        assert lib.fa_bwd_stage(2, *args, 1, 1, n, 128, 1.0, 1, 2, None) == FA_ERR_UNSUPPORTED
+
+
 def test_bwd_rejects(lib):
     args = [A] * 10
     base = dict(B=1, H=1, N=8, d=64, scale=1.0, causal=0, dtype=2)
@@ -270,3 +284,29 @@ def test_package_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\bimport\s+oracle|from\s+oracle|oracle/", text), f
+
+
+def test_caller_buffers_are_checked():
+    """Caller-supplied outputs, workspaces and the backward's LSE must match
+    what the kernels address exactly; anything else is a ValueError raised
+    before any library call."""
+    import torch
+
+    from io_aware_exact_03_amd import ops
+    good = torch.empty((2, 3, 5), dtype=torch.float32)
+    ops._check_out(good, (2, 3, 5), torch.float32, good.device, "lse")
+    ops._check_out(None, (2, 3, 5), torch.float32, good.device, "lse")
+    bad = [
+        torch.empty((2, 3, 4), dtype=torch.float32),          # too small
+        torch.empty((2, 3, 5), dtype=torch.float16),          # wrong dtype
+        torch.empty((2, 5, 3), dtype=torch.float32).transpose(1, 2),  # strided
+        torch.empty((2, 3, 5, 1), dtype=torch.float32),       # wrong rank
+    ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            ops._check_out(t, (2, 3, 5), torch.float32, good.device, "lse")
+    ops._check_bytes(torch.empty(64, dtype=torch.uint8), 64, good.device, "ws")
+    with pytest.raises(ValueError):
+        ops._check_bytes(torch.empty(63, dtype=torch.uint8), 64, good.device, "ws")
+    with pytest.raises(ValueError):
+        ops._check_bytes(torch.empty(256, dtype=torch.uint8)[::2], 64, good.device, "ws")
