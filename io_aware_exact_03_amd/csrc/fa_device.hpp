@@ -75,6 +75,10 @@ __device__ __forceinline__ float add_pair(BF16, uint32_t, float a, float b, floa
 __device__ __forceinline__ float add_pair(F16, uint32_t w, float, float, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
 }
+// The first pair of a row sum: a + b, without a zero to add to first (the
+// compiler cannot drop 0 + x, which differs from x when x is -0).
+__device__ __forceinline__ float first_pair(BF16, uint32_t, float a, float b) { return a + b; }
+__device__ __forceinline__ float first_pair(F16, uint32_t w, float a, float b) { return add_pair(F16{}, w, a, b, 0.f); }
 __device__ __forceinline__ float lo16(BF16, uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(BF16, uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float lo16(F16, uint32_t w) {

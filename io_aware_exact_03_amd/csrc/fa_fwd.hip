@@ -246,7 +246,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         p1 = kb + 1 < key_lim ? p1 : 0.f;
       }
       pk[r / 2] = pack2(T{}, p0, p1);
-      part[(r / 2) % 2] = add_pair(T{}, pk[r / 2], p0, p1, part[(r / 2) % 2]);
+      part[(r / 2) % 2] = r < 4 ? first_pair(T{}, pk[r / 2], p0, p1)
+                                : add_pair(T{}, pk[r / 2], p0, p1, part[(r / 2) % 2]);
     }
     return part[0] + part[1];
   };
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
       a[i] = ka[i];
       b[i] = vb[i];
     }
-    float lsum = 0.f;  // one dot-product chain: its links are a slot apart
+    float lsum = 0.f;  // one chain: its links are a slot apart
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (k + PD < NS) {
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
         const float p0 = fast_exp2(__builtin_fmaf(cur[r], qk_scale, -m_run));
         const float p1 = fast_exp2(__builtin_fmaf(cur[r + 1], qk_scale, -m_run));
         pk[r / 2] = pack2(T{}, p0, p1);
-        lsum = add_pair(T{}, pk[r / 2], p0, p1, lsum);
+        lsum = r == 0 ? first_pair(T{}, pk[0], p0, p1) : add_pair(T{}, pk[r / 2], p0, p1, lsum);
       }
       if constexpr (PV) oacc[k % DB] = mma16(T{}, b[k % (PD + 1)], pp[k / DB], oacc[k % DB]);
       __builtin_amdgcn_sched_barrier(0);

@@ -27,7 +27,8 @@ __device__ __forceinline__ float from_h(uint16_t x) { return (float)__builtin_bi
 
 // ---------------------------------------------------------------------------
 // Kernel 1: S = scale * Q K^T.  Workgroup tile 128 queries x 64 keys, one
-// wave per 32 query rows; both operands are row-major 16-byte reads.
+// wave per 32 query rows; both operands are row-major 16-byte reads.  This
+// element-wise writer serves row lengths that are not a multiple of eight.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void naive_qk16(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
@@ -69,6 +70,74 @@ __global__ __launch_bounds__(256) void naive_qk16(const uint16_t* __restrict__ q
   }
 }
 
+// The same product for rows of 16-byte multiples (N % 8 == 0), written the
+// way a memory-bound kernel should write: each wave computes S^T (keys x its
+// 32 queries), so a lane holds one query's keys in runs of four; the tile of
+// 128 queries x 128 keys is staged in LDS as float16 rows and stored with
+// 16-byte accesses, sixteen lanes per 256-byte row segment.  K is staged in
+// LDS once per workgroup (rows padded by 16 bytes) and read by all four waves.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void naive_qk16_v(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
+                                                    uint16_t* __restrict__ sg, int N, int n_mt, int n_nt,
+                                                    float scale) {
+  constexpr int BQ = 128, BK = 128, KROW = D + 8, SROW = BK + 8, CPR = D / 8;
+  constexpr int LDS_ELEMS = (BK * KROW > BQ * SROW) ? BK * KROW : BQ * SROW;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
+  long long t = blockIdx.x;
+  const int nt = (int)(t % n_nt);
+  t /= n_nt;
+  const int mt = (int)(t % n_mt);
+  const int bh = (int)(t / n_mt);
+  const size_t head = (size_t)bh * N * D;
+  const int q0 = mt * BQ, k0 = nt * BK;
+  // K tile -> LDS (zeros past N)
+#pragma unroll
+  for (int c = 0; c < BK * CPR / 256; ++c) {
+    const int idx = c * 256 + tid, key = idx / CPR, ch = idx % CPR;
+    const uint4 x = k0 + key < N ? *reinterpret_cast<const uint4*>(kg + head + (size_t)(k0 + key) * D + 8 * ch)
+                                 : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&lds[key * KROW + 8 * ch]) = x;
+  }
+  // Q fragments (B operand of S^T = K Q^T): query q0 + 32 wave + n
+  const int q = q0 + 32 * wave + n;
+  uint4 qf[D / 16];
+#pragma unroll
+  for (int s2 = 0; s2 < D / 16; ++s2)
+    qf[s2] = q < N ? *reinterpret_cast<const uint4*>(qg + head + (size_t)q * D + 16 * s2 + 8 * g) : make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  f32x16 acc[BK / 32];
+#pragma unroll
+  for (int cb = 0; cb < BK / 32; ++cb) {
+    acc[cb] = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&lds[(32 * cb + n) * KROW + 16 * s2 + 8 * g]);
+      acc[cb] = mma16(T{}, a, qf[s2], acc[cb]);
+    }
+  }
+  __syncthreads();  // every wave is done with K: the buffer now stages S
+  // register r of block cb: key 32 cb + 8 (r / 4) + 4 g + r % 4, query n
+#pragma unroll
+  for (int cb = 0; cb < BK / 32; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 w = make_uint2((uint32_t)to_h(acc[cb][4 * j] * scale) | ((uint32_t)to_h(acc[cb][4 * j + 1] * scale) << 16),
+                                 (uint32_t)to_h(acc[cb][4 * j + 2] * scale) | ((uint32_t)to_h(acc[cb][4 * j + 3] * scale) << 16));
+      *reinterpret_cast<uint2*>(&lds[(32 * wave + n) * SROW + 32 * cb + 8 * j + 4 * g]) = w;
+    }
+  __syncthreads();
+  uint16_t* sh = sg + (size_t)bh * N * N;
+  constexpr int CH = BK / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int pass = 0; pass < BQ * CH / 256; ++pass) {
+    const int row = pass * (256 / CH) + tid / CH, ch = tid % CH;
+    const int qq = q0 + row, key = k0 + 8 * ch;
+    if (qq < N && key < N)  // N % 8 == 0: the chunk is whole
+      *reinterpret_cast<uint4*>(sh + (size_t)qq * N + key) = *reinterpret_cast<const uint4*>(&lds[row * SROW + 8 * ch]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void naive_qk32(const float* __restrict__ qg, const float* __restrict__ kg,
                                                   float* __restrict__ sg, int N, int n_mt, int n_nt, float scale) {
@@ -107,7 +176,8 @@ __global__ __launch_bounds__(256) void naive_qk32(const float* __restrict__ qg, 
 // Kernel 2: row softmax.  One workgroup of 256 threads per row; the row is
 // read once into registers (EPT elements per thread), reduced for max and
 // sum through LDS, and written back as P.  Causal: keys after the row get
-// P = 0.  Also writes LSE = m + ln l.
+// P = 0.  Also writes LSE = m + ln l.  This element-wise form serves rows
+// whose length is not a multiple of eight (and fp32 rows).
 // ---------------------------------------------------------------------------
 template <typename S, int EPT>
 __global__ __launch_bounds__(256) void naive_softmax(const S* __restrict__ sg, S* __restrict__ pg,
@@ -158,6 +228,80 @@ __global__ __launch_bounds__(256) void naive_softmax(const S* __restrict__ sg, S
     }
   }
   if (threadIdx.x == 0) lseg[row_id] = m + __logf(l);
+}
+
+// The same softmax for float16 rows of 16-byte multiples (N % 8 == 0): a row
+// belongs to TPR threads (one wave, or the whole workgroup for long rows),
+// each of which moves CPT 16-byte chunks, eight elements per load and per
+// store.  Causal rows read only their visible chunks and write zeros past
+// the diagonal.
+template <int TPR, int CPT>
+__global__ __launch_bounds__(256) void naive_softmax_v16(const uint16_t* __restrict__ sg, uint16_t* __restrict__ pg,
+                                                         float* __restrict__ lseg, int N, int causal,
+                                                         long long rows) {
+  static_assert(TPR == 64 || TPR == 256, "a wave or the workgroup per row");
+  constexpr int RPW = 256 / TPR;  // rows per workgroup
+  __shared__ float red[4];
+  const int t = threadIdx.x % TPR, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row_id = (long long)blockIdx.x * RPW + threadIdx.x / TPR;
+  const bool row_ok = row_id < rows;
+  const int i = row_ok ? (int)(row_id % N) : 0;
+  const int lim = causal ? i + 1 : N;  // keys < lim are allowed
+  const int nch = N / 8;
+  const uint4* srow = reinterpret_cast<const uint4*>(sg + (size_t)(row_ok ? row_id : 0) * N);
+  uint4* prow = reinterpret_cast<uint4*>(pg + (size_t)(row_ok ? row_id : 0) * N);
+  float x[CPT][8];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = c * TPR + t;
+    const bool any = row_ok && ch < nch && 8 * ch < lim;
+    const uint4 w = any ? srow[ch] : make_uint4(0, 0, 0, 0);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = from_h((uint16_t)((e & 1) ? (ws[e / 2] >> 16) : (ws[e / 2] & 0xffffu)));
+      x[c][e] = (any && 8 * ch + e < lim) ? v : kNegInf;
+    }
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, x[c][e]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if constexpr (TPR == 256) {
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+  }
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[c][e] = (x[c][e] == kNegInf) ? 0.f : __expf(x[c][e] - m);
+      l += x[c][e];
+    }
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  if constexpr (TPR == 256) {
+    if (lane == 0) red[wave] = l;
+    __syncthreads();
+    l = red[0] + red[1] + red[2] + red[3];
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = c * TPR + t;
+    if (row_ok && ch < nch) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)to_h(x[c][2 * e] * inv) | ((uint32_t)to_h(x[c][2 * e + 1] * inv) << 16);
+      prow[ch] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  if (row_ok && t == 0) lseg[row_id] = m + __logf(l);
 }
 
 // Rows longer than the register path: two passes over S (online max/sum,
@@ -229,6 +373,26 @@ __global__ __launch_bounds__(256) void naive_pv16(const uint16_t* __restrict__ p
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   for (int k0 = 0; k0 < N; k0 += BK) {
+    // this block's P (the A operand: 8 keys of the lane's query row per
+    // product), loaded first so it arrives while V is staged
+    uint4 pa[BK / 16];
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int key = k0 + 16 * s + 8 * g;  // first of this lane's 8 keys
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (q < N) {
+        if ((N & 7) == 0 && key + 8 <= N) {  // 16-byte aligned full slice
+          a = *reinterpret_cast<const uint4*>(ph + (size_t)q * N + key);
+        } else {
+          uint16_t tmp[8];
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) tmp[e2] = (key + e2 < N) ? ph[(size_t)q * N + key + e2] : (uint16_t)0;
+          a = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16), tmp[4] | (tmp[5] << 16),
+                         tmp[6] | (tmp[7] << 16));
+        }
+      }
+      pa[s] = a;
+    }
     // stage V[k0 .. k0+64) transposed, as float16
     uint4 x[KPT];
 #pragma unroll
@@ -257,23 +421,10 @@ __global__ __launch_bounds__(256) void naive_pv16(const uint16_t* __restrict__ p
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int key = k0 + 16 * s + 8 * g;  // first of this lane's 8 keys
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (q < N) {
-        if ((N & 7) == 0 && key + 8 <= N) {  // 16-byte aligned full slice
-          a = *reinterpret_cast<const uint4*>(ph + (size_t)q * N + key);
-        } else {
-          uint16_t tmp[8];
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) tmp[e2] = (key + e2 < N) ? ph[(size_t)q * N + key + e2] : (uint16_t)0;
-          a = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16), tmp[4] | (tmp[5] << 16),
-                         tmp[6] | (tmp[7] << 16));
-        }
-      }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const uint4 b = *reinterpret_cast<const uint4*>(&vt[(32 * db + n) * VROW + 16 * s + 8 * g]);
-        acc[db] = mma16(F16{}, a, b, acc[db]);
+        acc[db] = mma16(F16{}, pa[s], b, acc[db]);
       }
     }
   }
@@ -322,10 +473,39 @@ __global__ __launch_bounds__(256) void naive_pv32(const float* __restrict__ pg, 
     }
 }
 
+// float16 rows of 16-byte multiples: the vector softmax, a wave per row up
+// to 2048 keys, the workgroup per row up to 32768.  Returns false if the row
+// length has no vector variant.
+bool launch_softmax_v16(const NaiveArgs& a, hipError_t* err) {
+  const int N = a.N;
+  if ((N & 7) != 0 || N > 256 * 8 * 16) return false;
+  const long long rows = (long long)a.BH * N;
+  const uint16_t* s = static_cast<const uint16_t*>(a.s);
+  uint16_t* p = static_cast<uint16_t*>(a.p);
+  const int causal = a.causal ? 1 : 0;
+  auto go = [&](auto kern, int rpw) {
+    const long long grid = (rows + rpw - 1) / rpw;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, a.stream, s, p, a.lse, N, causal, rows);
+  };
+  if (N <= 64 * 8) go(naive_softmax_v16<64, 1>, 4);
+  else if (N <= 64 * 16) go(naive_softmax_v16<64, 2>, 4);
+  else if (N <= 64 * 32) go(naive_softmax_v16<64, 4>, 4);
+  else if (N <= 256 * 16) go(naive_softmax_v16<256, 2>, 1);
+  else if (N <= 256 * 32) go(naive_softmax_v16<256, 4>, 1);
+  else if (N <= 256 * 64) go(naive_softmax_v16<256, 8>, 1);
+  else go(naive_softmax_v16<256, 16>, 1);
+  *err = hipGetLastError();
+  return true;
+}
+
 template <typename S>
 hipError_t launch_softmax(const NaiveArgs& a) {
   const long long rows = (long long)a.BH * a.N;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if constexpr (sizeof(S) == 2) {
+    hipError_t e;
+    if (launch_softmax_v16(a, &e)) return e;
+  }
   const S* s = static_cast<const S*>(a.s);
   S* p = static_cast<S*>(a.p);
   const int causal = a.causal ? 1 : 0;
@@ -345,13 +525,19 @@ hipError_t launch_softmax(const NaiveArgs& a) {
 
 template <typename T, int D>
 hipError_t run16(const NaiveArgs& a) {
-  const int n_mt = (a.N + 127) / 128, n_nt = (a.N + 63) / 64;
+  const int n_mt = (a.N + 127) / 128, n_nt = (a.N + 63) / 64, n_nt128 = (a.N + 127) / 128;
   const long long g1 = (long long)a.BH * n_mt * n_nt;
   const long long g3 = (long long)a.BH * n_mt;
   if (g1 > 0x7fffffffLL || g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((naive_qk16<T, D>), dim3((unsigned)g1), dim3(256), 0, a.stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<uint16_t*>(a.s), a.N, n_mt, n_nt, a.scale);
+  if ((a.N & 7) == 0) {  // 16-byte rows: the staged, row-contiguous S writer
+    hipLaunchKernelGGL((naive_qk16_v<T, D>), dim3((unsigned)((long long)a.BH * n_mt * n_nt128)), dim3(256), 0,
+                       a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<uint16_t*>(a.s), a.N, n_mt, n_nt128, a.scale);
+  } else {
+    hipLaunchKernelGGL((naive_qk16<T, D>), dim3((unsigned)g1), dim3(256), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<uint16_t*>(a.s), a.N, n_mt, n_nt, a.scale);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_softmax<uint16_t>(a);

@@ -45,6 +45,36 @@ def test_small(N, causal, d, dtype):
         assert float(torch.triu(p.float(), 1).abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1000, 2056])
+def test_vector_paths(N, causal, d, dtype):
+    """Row lengths that are multiples of eight take the 16-byte kernels: the
+    staged S writer (tiles of 128 x 128, here with a partial last tile), the
+    vector softmax with a wave per row (N <= 2048) or the workgroup per row
+    (N > 2048).  O, LSE and S are compared element by element; P through
+    the oracle's probabilities where the V = I product stays small."""
+    fa = _fa()
+    q, k, v = fa_synth.make_inputs(1, 2, N, d, dtype, seed=8100 + N + d)
+    scale = 1 / math.sqrt(d)
+    o, lse, s, p = fa.naive_fwd(*P.to_dev(q, k, v), scale, causal)
+    torch.cuda.synchronize()
+    ctx = f"naive vector N={N} d={d} causal={causal} {dtype}"
+    P.check_fwd_full(q, k, v, o, lse, scale, causal, dtype, ctx, lse_tol=P.naive_lse_tol(q, k, scale, dtype))
+    qq, kk = P.f64(q), P.f64(k)
+    s_ref = scale * np.einsum("bhid,bhjd->bhij", qq, kk)
+    P.compare("S", P.f64(s), s_ref, max(1e-5, 2 * P.half_ulp(np.abs(s_ref).max(), "f16")), "f16", ctx)
+    if N <= 1000:
+        eye = np.broadcast_to(np.eye(N), (1, 2, N, N)).copy()
+        p_ref, _ = oracle.attn_fwd(qq, kk, eye, scale, causal)
+        P.compare("P", P.f64(p), p_ref, 2e-3, "f16", ctx)
+    if causal:
+        assert float(torch.triu(p.float(), 1).abs().max()) == 0.0
+    rows = torch.isfinite(p.float()).all()
+    assert bool(rows)
+
+
 @pytest.mark.parametrize("w", fa_synth.NONCAUSAL_SWEEP + (fa_synth.LONG_CAUSAL,), ids=lambda w: w.name)
 def test_full_size_sampled(w):
     fa = _fa()
