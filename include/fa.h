@@ -66,7 +66,8 @@ typedef enum {
   FA_ERR_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
   FA_ERR_ALIGN = 3,
-  FA_ERR_HIP = 4
+  FA_ERR_HIP = 4,
+  FA_ERR_SCRATCH = 5
 } fa_status;
 
 /*
@@ -220,6 +221,31 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 /* Workspace bytes fa_decode needs for n_parts (0 for n_parts = 1 and for
  * invalid arguments). */
 size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int d, int n_parts);
+
+/*
+ * fa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * computes exactly what fa_decode computes (same kernels, same partition)
+ * but keeps the pieces of cut units in a fixed scratch buffer the library
+ * holds on each device, instead of a caller workspace; the caller still
+ * passes q, the caches, kv_lens, o and lse.  No hipMalloc, hipFree or
+ * allocating library routine is called.
+ *
+ * Limit: fa_decode_workspace_bytes(B, H, Hkv, d, n_parts) must not exceed
+ * FA_DECODE_SCRATCH_BYTES (16 MiB), else FA_ERR_SCRATCH (checked on the host
+ * before any HIP call).  n_parts = 1 uses no scratch.  The buffer lives on
+ * every device the library runs on until the process ends; its address is
+ * looked up once per device, on the first call there (FA_ERR_HIP if that
+ * fails).  Nothing in it needs to start at zero: every piece the merge reads
+ * was written earlier in the same call.  All calls on one device share the
+ * buffer, so calls that overlap on one device (different streams, or
+ * threads) race and must be serialised by the caller.  Other arguments,
+ * checks and errors as fa_decode.
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                      void* o, float* lse, int B, int H, int Hkv, int Nkv, int d, float scale,
+                      int n_parts, int dtype, void* stream);
 
 /*
  * The part count the library suggests for a decode step on the current

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-STATUS = {0: "FA_OK", 1: "FA_ERR_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_ALIGN", 4: "FA_ERR_HIP"}
+STATUS = {0: "FA_OK", 1: "FA_ERR_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_ALIGN", 4: "FA_ERR_HIP", 5: "FA_ERR_SCRATCH"}
+DECODE_SCRATCH_BYTES = 16 << 20  # FA_DECODE_SCRATCH_BYTES
 
 # name -> (restype, argtypes), mirroring include/fa.h
 _vp, _i, _f, _fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
@@ -26,6 +27,7 @@ SIGNATURES = {
     "fa_kv_head": (_i, [_i, _i, _i]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "fa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_plan": (_i, [_i, _i, _i, _i, _i, _ip]),
     "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp]),
     "fa_fwd_fa1": (_i, [_vp, _vp, _vp, _vp, _fp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _i, _vp]),

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_kernels.hpp"
 #include "fa_plan.hpp"
@@ -46,6 +48,36 @@ namespace fa {
 void record_hip_error(int e) { g_last_hip_error = e; }
 }  // namespace fa
 
+// The allocation-free decode keeps the pieces of cut units here: one fixed
+// buffer per device, present for the life of the process.  In host code the
+// array's name is only a stand-in for the symbol; its device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* fa_strerror(int status) {
@@ -55,6 +87,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
     case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case FA_ERR_HIP: return "HIP launch error (see fa_last_hip_error)";
+    case FA_ERR_SCRATCH: return "request needs more than the library's fixed allocation-free scratch buffer holds";
     default: return "unknown fa_status";
   }
 }
@@ -209,6 +242,41 @@ int fa_decode_plan(int B, int H, int Hkv, int Nkv, int d, int* n_parts) {
   return FA_OK;
 }
 
+// Host checks shared by fa_decode and fa_decode_noalloc (no HIP call).
+static int decode_check(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens, void* o,
+                        float* lse, int B, int H, int Hkv, int Nkv, int d, float scale, int n_parts, int dtype) {
+  if (!q || !k_cache || !v_cache || !o || !lse) return FA_ERR_ARG;
+  if (Hkv < 1 || H < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_ARG;
+  if (n_parts < 1 || n_parts > fa::kDecodeMaxParts) return FA_ERR_ARG;
+  const int st = check_shape(B, H, Nkv, d, dtype, 0, scale);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (decode_units(B, H, Hkv) * fa::decode_tiles(Nkv) >= (1LL << 31) ||
+      (decode_units(B, H, Hkv) + n_parts) * 32 >= (1LL << 31))
+    return FA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k_cache, v_cache, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (kv_lens && ((uintptr_t)kv_lens & 3u)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Launch with a validated workspace (ignored for n_parts = 1).
+static int decode_launch(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens, void* o,
+                         float* lse, void* ws, int B, int H, int Hkv, int Nkv, int d, float scale, int n_parts,
+                         int dtype, void* stream) {
+  fa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_lens = kv_lens; a.o = o; a.lse = lse;
+  const size_t slots = (size_t)n_parts + (size_t)decode_units(B, H, Hkv);
+  a.opart = n_parts > 1 ? static_cast<float*>(ws) : nullptr;
+  a.lpart = n_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * 32 * d * 4)) : nullptr;
+  a.B = B; a.H = H; a.G = H / Hkv; a.Nkv = Nkv; a.d = d; a.dtype = dtype;
+  a.parts = n_parts;
+  a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(fa::launch_decode(a));
+}
+
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens, void* o, float* lse,
               void* ws, size_t ws_bytes, int B, int H, int Hkv, int Nkv, int d, float scale, int n_parts,
               int dtype, void* stream) {
@@ -229,16 +297,21 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if (kv_lens && ((uintptr_t)kv_lens & 3u)) return FA_ERR_ALIGN;
   if (n_parts > 1 && !aligned16(ws)) return FA_ERR_ALIGN;
-  fa::DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.kv_lens = kv_lens; a.o = o; a.lse = lse;
-  const size_t slots = (size_t)n_parts + (size_t)decode_units(B, H, Hkv);
-  a.opart = n_parts > 1 ? static_cast<float*>(ws) : nullptr;
-  a.lpart = n_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * 32 * d * 4)) : nullptr;
-  a.B = B; a.H = H; a.G = H / Hkv; a.Nkv = Nkv; a.d = d; a.dtype = dtype;
-  a.parts = n_parts;
-  a.scale = scale;
-  a.stream = static_cast<hipStream_t>(stream);
-  return hip_status(fa::launch_decode(a));
+  return decode_launch(q, k_cache, v_cache, kv_lens, o, lse, ws, B, H, Hkv, Nkv, d, scale, n_parts, dtype, stream);
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens, void* o,
+                      float* lse, int B, int H, int Hkv, int Nkv, int d, float scale, int n_parts, int dtype,
+                      void* stream) {
+  const int st = decode_check(q, k_cache, v_cache, kv_lens, o, lse, B, H, Hkv, Nkv, d, scale, n_parts, dtype);
+  if (st != FA_OK) return st;
+  if (fa_decode_workspace_bytes(B, H, Hkv, d, n_parts) > FA_DECODE_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (n_parts > 1) {
+    const int e = scratch_of_current_device(&ws);
+    if (e != FA_OK) return e;
+  }
+  return decode_launch(q, k_cache, v_cache, kv_lens, o, lse, ws, B, H, Hkv, Nkv, d, scale, n_parts, dtype, stream);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,

@@ -241,6 +241,42 @@ def decode(q, k_cache, v_cache, scale: float, kv_lens=None, n_parts=None, out=No
     return out, lse
 
 
+def decode_noalloc(q, k_cache, v_cache, scale: float, kv_lens=None, n_parts=None, out=None, lse=None):
+    """decode() through fa_decode_noalloc: the pieces of cut units go to the
+    library's fixed per-device scratch buffer instead of a workspace, so the
+    library allocates nothing (out / lse are allocated here only if None).
+    Calls that overlap on one device share that buffer and must not run
+    concurrently."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H,d] and caches [B,Hkv,Nkv,d]")
+    for t in (q, k_cache, v_cache):
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q and the caches must be contiguous, on one HIP device, of one dtype")
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, d = q.shape
+    Hkv, Nkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.device != q.device
+                                or kv_lens.numel() != B or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 tensor of B values on q's device")
+    if n_parts is None:
+        n_parts = decode_plan(B, H, Hkv, Nkv, d)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    _check_out(lse, (B, H), torch.float32, q.device, "lse")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       kv_lens.data_ptr() if kv_lens is not None else None, out.data_ptr(),
+                                       lse.data_ptr(), B, H, Hkv, Nkv, d, float(scale), int(n_parts),
+                                       DTYPE_CODES[q.dtype], _stream(q))
+    _lib.check(st, "fa_decode_noalloc")
+    return out, lse
+
+
 def decode_pieces(ws, B: int, H: int, Hkv: int, d: int, n_parts: int):
     """Views of a decode workspace after the call: (O [slots, 32, d], LSE
     [slots, 32]), both float32, slots = n_parts + units."""
