@@ -92,6 +92,15 @@ def test_many_heads():
     run_and_check(3, 5, 700, 64, "f16", True, 0.125, 9200, "B3 H5 N700")
 
 
+def test_noncausal_many_items():
+    """Non-causal forward and backward with more work items than CUs (B8 H64
+    N512 d128: 1024 forward and dQ items, 2048 dK/dV items over the
+    persistent grids), so workgroups walk several items and change K/V (or
+    query) block between them; sampled whole heads against the oracle."""
+    run_and_check(8, 64, 512, 128, "bf16", False, 1 / math.sqrt(128), 9250, "B8 H64 N512 non-causal",
+                  heads=P.heads_to_check(8, 64, 4, seed=9250))
+
+
 def test_deterministic():
     fa = _fa()
     q, k, v, do = P.to_dev(*fa_synth.make_inputs(2, 4, 1000, 128, "bf16", seed=9300, with_dout=True))

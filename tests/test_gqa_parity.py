@@ -153,6 +153,45 @@ def test_full_size_prefill():
         assert err <= 1e-4 * max(1.0, float(ref.abs().max())), f"{name} vs group sum: {err:.3e}"
 
 
+def _whole_kv_head(B, H, Hkv, N, d, causal, seed, b, g, context):
+    """fwd_gqa + bwd_gqa on the whole problem; one whole K/V head's dK, dV
+    and its G query heads' dQ against oracle.attn_bwd_gqa on that slice."""
+    fa = _fa()
+    q, k, v, do = _inputs(B, H, Hkv, N, d, "bf16", seed)
+    qd, kd, vd, dod = P.to_dev(q, k, v, do)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fwd_gqa(qd, kd, vd, scale, causal)
+    dq, dk, dv, _ = fa.bwd_gqa(qd, kd, vd, o, dod, lse, scale, causal)
+    torch.cuda.synchronize()
+    G = H // Hkv
+    hs = slice(g * G, (g + 1) * G)
+    sl_q = (slice(b, b + 1), hs)
+    sl_k = (slice(b, b + 1), slice(g, g + 1))
+    rdq, rdk, rdv, _ = oracle.attn_bwd_gqa(P.f64(q[sl_q]), P.f64(k[sl_k]), P.f64(v[sl_k]), P.f64(do[sl_q]), scale,
+                                           causal)
+    tol = grad_tol(scale, d)
+    P.compare("dK", P.f64(dk[sl_k]), rdk, tol * math.sqrt(G), "f32", context)
+    P.compare("dV", P.f64(dv[sl_k]), rdv, tol * math.sqrt(G), "f32", context)
+    P.compare("dQ", P.f64(dq[sl_q]), rdq, tol, "f32", context)
+    ro, rl = oracle.attn_fwd_gqa(P.f64(q[sl_q]), P.f64(k[sl_k]), P.f64(v[sl_k]), scale, causal)
+    P.compare("O", P.f64(o[sl_q]), ro, P.TOL_OUT["bf16"], "bf16", context)
+    P.compare("LSE", P.f64(lse[sl_q]), rl, P.TOL_LSE, "bf16", context)
+
+
+def test_whole_kv_head_many_segments():
+    """Eight query heads per K/V head at N = 2048 (causal): each dK/dV work
+    item walks eight segments back to back, with the next segment's Q/dO
+    loads issued across the segment boundary."""
+    _whole_kv_head(1, 16, 2, 2048, 128, True, 9700, 0, 1, "B1 H16 Hkv2 N2048 causal, K/V head 1")
+
+
+def test_whole_kv_head_many_items():
+    """More grouped dK/dV work items than CUs (128 K/V heads x 4 pair items
+    at N = 1024), so every workgroup walks two items; the last K/V head is
+    compared whole."""
+    _whole_kv_head(16, 32, 8, 1024, 128, True, 9710, 15, 7, "B16 H32 Hkv8 N1024 causal, K/V head (15, 7)")
+
+
 def test_deterministic():
     fa = _fa()
     q, k, v, do = P.to_dev(*_inputs(1, 8, 2, 1000, 128, "bf16", 9800))
