@@ -79,12 +79,20 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", " ", "".join(out)).strip()
 
 
-def source_digest() -> str:
+def digest_of(sources) -> str:
     h = hashlib.sha256()
-    for f in STEP_SOURCES:
+    for f in sources:
         h.update(f.encode())
         h.update(_code_only(open(os.path.join(CSRC, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
+
+
+def source_digest() -> str:
+    return digest_of(STEP_SOURCES)
+
+
+# The sources of the fused and naive forwards the traffic legs run.
+TRAFFIC_LEG_SOURCES = ("fa_device.hpp", "fa_fwd.hip", "fa_naive.hip", "fa_plan.hpp")
 
 
 # ---------------------------------------------------------------------------
@@ -183,7 +191,7 @@ def cpu_baseline(w, q, k, v, do, target_s: float):
     import fa_synth
     import oracle
 
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = len(os.sched_getaffinity(0))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
     def one(bh):
@@ -230,9 +238,24 @@ def main():
                     help="also run an elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_*.txt from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--traffic-legs", action="store_true",
+                    help="run only the fused and naive forwards of the non-causal sweep and the long causal "
+                         "workload (twice each, after the calibration copy), for counter passes")
+    ap.add_argument("--traffic-legs-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_naive_vs_fused.md from the counter passes of --traffic-legs")
+    ap.add_argument("--stats", metavar="KERNEL_TRACE_CSV",
+                    help="write profiles/kernel_stats_<workload>.md from a rocprofv3 kernel trace of the "
+                         "default training-step run (--legs 0 --cpu-baseline 0) and exit")
+    ap.add_argument("--ceilings", type=int, default=1, help="also measure the chip's ceilings (1) or not (0)")
     args = ap.parse_args()
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.calib_copy_mib)
+        return
+    if args.traffic_legs_write:
+        write_traffic_legs(args.traffic_legs_write[0], args.traffic_legs_write[1], args.calib_copy_mib)
+        return
+    if args.stats:
+        write_stats(args.stats, args.steps, args.warmup)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only (the attention kernels "
@@ -247,6 +270,9 @@ def main():
     fa._lib.load()
     dev = torch.device("cuda:0")
     digest = source_digest()
+    if args.traffic_legs:
+        run_traffic_legs(torch, fa, fa_synth, dev, args.calib_copy_mib)
+        return
 
     # ---------------- the timed step: causal training step ----------------
     w = fa_synth.TRAIN_STEP
@@ -314,6 +340,15 @@ def main():
     roof["kernel"] = dom
     roof["kernel_ms"] = kern_ms[dom]
     roof["traffic"] = read_traffic(dom, w.name, digest)
+    roof["timing"] = "HIP events on the launch stream around each launch of the timed steps"
+    prof = read_stats(w.name, digest)
+    if prof and dom in prof["kernel_us"]:
+        # the same kernel's average over the same steps, from the committed
+        # rocprofv3 kernel trace of this code
+        p_ms = prof["kernel_us"][dom] / 1e3
+        p_ach = roof["achieved"] * kern_ms[dom] / p_ms
+        roof["profile"] = {"kernel_ms": p_ms, "achieved": p_ach, "frac": p_ach / roof["peak"],
+                           "source": prof["path"]}
 
     kernels = {}
     for n_ in names:
@@ -331,9 +366,21 @@ def main():
     del o, lse, delta, dq, dk, dv
     torch.cuda.empty_cache()
 
+    ceil = None
+    if args.ceilings:
+        ceil = measure_ceilings(torch, fa, dev)
+        log(f"[bench] ceilings {ceil}")
+        if roof["unit"] == "TFLOP/s":
+            roof["measured_peak"] = ceil["mfma_bf16_tflops"]
+            roof["frac_of_measured_peak"] = roof["achieved"] / ceil["mfma_bf16_tflops"]
+
     legs = {}
     if args.legs:
         legs = run_legs(torch, fa, fa_synth, dev)
+        tl = read_traffic_legs(digest_of(TRAFFIC_LEG_SOURCES))
+        for name, entry in (tl or {}).items():
+            if name in legs:
+                legs[name].update(entry)
 
     cpu = None
     if args.cpu_baseline:
@@ -362,6 +409,7 @@ def main():
         "bwd_tflops": bwd_tf,
         "kernels": kernels,
         "roofline": roof,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "legs": legs,
         "source_digest": digest,
@@ -432,6 +480,233 @@ def write_traffic(fetch_csv: str, write_csv: str, calib_mib: int):
             f.write(f"hbm_bytes_per_launch = {byts:.0f}\n")
             f.write(f"source_digest = {digest}\n")
         print(f"wrote {path}: {byts / 1e6:.1f} MB per launch")
+
+
+def measure_ceilings(torch, fa, dev):
+    """What the chip sustains, measured with the library's own ceiling
+    kernels: matrix cores alone (8 independent v_mfma_f32_32x32x16_bf16
+    accumulators per wave, two waves per SIMD, one workgroup per CU), a
+    streaming copy and a streaming read of 2 GiB."""
+    out = {}
+    wgs, waves, iters = 256, 8, 4000
+    fa.ceiling_mfma(wgs, waves, iters)
+    ms, _ = time_reps(lambda: fa.ceiling_mfma(wgs, waves, iters), 5, torch)
+    out["mfma_bf16_tflops"] = fa.ceiling_mfma_flops(wgs, waves, iters) / (ms * 1e-3) / 1e12
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    fa.ceiling_copy(src, dst)
+    ms, _ = time_reps(lambda: fa.ceiling_copy(src, dst), 10, torch)
+    out["copy_gbs"] = 2 * nbytes / (ms * 1e-3) / 1e9  # read + write
+    sink = fa.ceiling_read(src)
+    ms, _ = time_reps(lambda: fa.ceiling_read(src, sink), 10, torch)
+    out["read_gbs"] = nbytes / (ms * 1e-3) / 1e9
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    out["how"] = ("fa_ceiling_mfma: 256 workgroups x 8 waves x 4000 x 8 products; fa_ceiling_copy / "
+                  "fa_ceiling_read over 2 GiB; medians of HIP-event timings")
+    return out
+
+
+STEP_KERNELS = {"fwd16_kernel": "fa_fwd", "bwd_delta_kernel": "bwd_delta", "bwd_dkdv_kernel": "bwd_dkdv",
+                "bwd_dq_kernel": "bwd_dq"}
+
+
+def write_stats(trace_csv: str, steps: int, warmup: int):
+    """profiles/kernel_stats_<training step>.md from a rocprofv3 kernel trace
+    of `bench.py --legs 0 --cpu-baseline 0 --ceilings 0` with the same
+    --steps / --warmup: per kernel, the average over the timed steps (the
+    last `steps` dispatches), the dispatches the bench's events time."""
+    import csv
+
+    import fa_synth
+    w = fa_synth.TRAIN_STEP
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = next((v for k_, v in STEP_KERNELS.items() if k_ in r["Kernel_Name"]), None)
+        if key is None:
+            continue
+        per.setdefault(key, []).append((int(r["Dispatch_Id"]),
+                                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    digest = source_digest()
+    path = os.path.join(PROFILES, f"kernel_stats_{w.name}.md")
+    total = {}
+    lines = []
+    for key in ("fa_fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"):
+        d = [t for _, t in sorted(per.get(key, []))]
+        if len(d) < steps + warmup:
+            sys.exit(f"{key}: {len(d)} dispatches in the trace, expected {steps + warmup}")
+        timed = d[-steps:]
+        total[key] = sum(timed) / len(timed)
+        lines.append(f"| `{key}` | {len(d)} | {total[key]:.1f} | {min(timed):.1f} | {max(timed):.1f} |")
+    step_us = sum(total.values())
+    with open(path, "w") as f:
+        f.write(f"# Kernel times: causal training step ({w.describe()})\n\n")
+        f.write("Command (repo root on the MI355X box, `TMPDIR=/tmp`):\n\n```\n")
+        f.write(f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kstats -o run -- \\\n"
+                f"    python3 bench.py --steps {steps} --warmup {warmup} --legs 0 --cpu-baseline 0 --ceilings 0\n"
+                f"python3 bench.py --stats gpurun_out/kstats/run_kernel_trace.csv --steps {steps} --warmup {warmup}\n"
+                "```\n\n")
+        f.write(f"Averages over the {steps} timed steps (the last {steps} dispatches of each kernel; the "
+                f"{warmup} warm-up steps before them are left out), the dispatches whose HIP-event times the "
+                "bench line's `roofline` uses; the bench reads the lines below back as `roofline.profile`.\n\n")
+        f.write("| kernel | dispatches | avg over timed steps (us) | min (us) | max (us) |\n|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n\n")
+        f.write(f"Sum of the four kernels: {step_us:.1f} us per step.\n\n")
+        f.write("```\n")
+        for key, v in total.items():
+            f.write(f"kernel_avg_us.{key} = {v:.2f}\n")
+        f.write(f"steps = {steps}\nsource_digest = {digest}\n```\n")
+    print(f"wrote {path}")
+
+
+def read_stats(workload: str, digest: str):
+    path = os.path.join(PROFILES, f"kernel_stats_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if " = " in line:
+            a, b = line.split(" = ", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_digest") != digest:
+        return None
+    us = {k_.split(".", 1)[1]: float(v) for k_, v in kv.items() if k_.startswith("kernel_avg_us.")}
+    return {"kernel_us": us, "path": os.path.relpath(path, ROOT)}
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the fused forward against the naive three-kernel path, from
+# counters ("Flash Attention -- five lessons converging into 80 lines",
+# Lessons 1-2: the naive path's N^2 round trips against the fused path's
+# N d; "Flash Attention: IO-awareness principle", the S+P traffic table).
+# ---------------------------------------------------------------------------
+def traffic_leg_workloads():
+    import fa_synth
+    return tuple(fa_synth.NONCAUSAL_SWEEP) + (fa_synth.LONG_CAUSAL,)
+
+
+def run_traffic_legs(torch, fa, fa_synth, dev, calib_mib: int):
+    """Calibration copy, then per workload: the fused forward twice, the
+    naive forward twice (three kernels each), in this fixed order."""
+    if calib_mib <= 0:
+        sys.exit("--traffic-legs needs --calib-copy-mib")
+    src = torch.ones(calib_mib * (1 << 18), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    for w in traffic_leg_workloads():
+        q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        s_ws = torch.empty((w.B, w.H, w.N, w.N), dtype=torch.float16, device=dev)
+        p_ws = torch.empty_like(s_ws)
+        for _ in range(2):
+            fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s_ws, p_ws=p_ws)
+        torch.cuda.synchronize()
+        log(f"[bench] traffic legs: {w.name} done")
+        del q, k, v, o, lse, s_ws, p_ws
+        torch.cuda.empty_cache()
+
+
+def _counter_dispatches(path: str, counter: str):
+    """[(dispatch id, kernel name, summed value)] of one counter, in order."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        name, val = acc.get(did, (r["Kernel_Name"], 0.0))
+        acc[did] = (name, val + float(r["Counter_Value"]))
+    return [(did, n, v) for did, (n, v) in sorted(acc.items())]
+
+
+def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
+    if calib_mib <= 0:
+        sys.exit("--traffic-legs-write needs the --calib-copy-mib the counter runs used")
+    rows = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = _counter_dispatches(path, counter)
+        calib = [v for _, n, v in ds if "elementwise" in n and "add" in n]
+        if not calib:
+            sys.exit(f"{path}: no calibration copy")
+        scale = calib_mib * 1024.0 / (sum(calib) / len(calib))
+        seq = [(n, v * scale * 1024.0) for _, n, v in ds if "fwd16_kernel" in n or "naive_" in n]
+        per_leg = 2 + 2 * 3
+        legs = traffic_leg_workloads()
+        if len(seq) != per_leg * len(legs):
+            sys.exit(f"{path}: {len(seq)} attention dispatches, expected {per_leg * len(legs)}")
+        for li, w in enumerate(legs):
+            part = seq[li * per_leg:(li + 1) * per_leg]
+            fused = [b for n, b in part[:2]]
+            assert all("fwd16_kernel" in n for n, _ in part[:2]), part[:2]
+            naive = part[2:]
+            kinds = ("qk", "softmax", "pv")
+            for j, (n, _) in enumerate(naive):
+                assert f"naive_{kinds[j % 3]}" in n, (n, kinds[j % 3])
+            nb = {kd: sum(b for (n, b) in naive[j::3]) / 2 for j, kd in enumerate(kinds)}
+            r = rows.setdefault(w.name, {"w": w, "scale": {}})
+            r[counter] = {"fused": sum(fused) / 2, **nb}
+            r["scale"][counter] = scale
+    digest = digest_of(TRAFFIC_LEG_SOURCES)
+    path = os.path.join(PROFILES, "traffic_naive_vs_fused.md")
+    with open(path, "w") as f:
+        f.write("# HBM-side bytes: fused forward against the naive three-kernel path\n\n")
+        f.write("Command (repo root on the MI355X box, `TMPDIR=/tmp`), two counter passes of their own:\n\n```\n")
+        for c, d in (("FETCH_SIZE", "tl_fetch"), ("WRITE_SIZE", "tl_write")):
+            f.write(f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/{d} -o run -- \\\n"
+                    f"    python3 bench.py --traffic-legs --calib-copy-mib {calib_mib}\n")
+        f.write(f"python3 bench.py --traffic-legs-write gpurun_out/tl_fetch/run_counter_collection.csv "
+                f"gpurun_out/tl_write/run_counter_collection.csv --calib-copy-mib {calib_mib}\n```\n\n")
+        f.write("Bytes past L2 (HBM or the memory-side cache) per call: FETCH_SIZE and WRITE_SIZE (KiB per "
+                "dispatch) scaled by what the same counters read for an elementwise copy of "
+                f"{calib_mib} MiB in and {calib_mib} MiB out (read scale "
+                f"{rows[traffic_leg_workloads()[0].name]['scale']['FETCH_SIZE']:.3f}, write scale "
+                f"{rows[traffic_leg_workloads()[0].name]['scale']['WRITE_SIZE']:.3f}), averaged over two calls. "
+                "Model bytes: fused = Q, K, V read and O written once (+ fp32 LSE); naive = that plus S and P "
+                "each written once and read once, 4 N^2 float16 elements per head.\n\n")
+        f.write("| workload | N | fused, counters (MB) | fused, model (MB) | naive QK^T (MB) | naive softmax (MB) "
+                "| naive PV (MB) | naive, counters (MB) | naive, model (MB) | ratio, counters | ratio, model |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+        machine = []
+        for name, r in rows.items():
+            w = r["w"]
+            fu = r["FETCH_SIZE"]["fused"] + r["WRITE_SIZE"]["fused"]
+            nk = {kd: r["FETCH_SIZE"][kd] + r["WRITE_SIZE"][kd] for kd in ("qk", "softmax", "pv")}
+            nt = sum(nk.values())
+            fm = fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)
+            nm = naive_fwd_bytes(w.B, w.H, w.N, w.d, 2, 2)
+            f.write(f"| `{name}` | {w.N} | {fu / 1e6:.2f} | {fm / 1e6:.2f} | {nk['qk'] / 1e6:.1f} | "
+                    f"{nk['softmax'] / 1e6:.1f} | {nk['pv'] / 1e6:.1f} | {nt / 1e6:.1f} | {nm / 1e6:.1f} | "
+                    f"{nt / fu:.1f} | {nm / fm:.1f} |\n")
+            machine.append(f"{name}.fused_counter_bytes = {fu:.0f}")
+            machine.append(f"{name}.naive_counter_bytes = {nt:.0f}")
+        f.write("\n```\n" + "\n".join(machine) + f"\nsource_digest = {digest}\n```\n")
+    print(f"wrote {path}")
+
+
+def read_traffic_legs(digest: str):
+    path = os.path.join(PROFILES, "traffic_naive_vs_fused.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if " = " in line:
+            a, b = line.split(" = ", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_digest") != digest:
+        return None
+    out = {}
+    for k_, v in kv.items():
+        if "." in k_ and k_.endswith("_counter_bytes"):
+            leg, field_ = k_.split(".", 1)
+            out.setdefault(leg, {})[field_] = float(v)
+    return out
 
 
 def run_legs(torch, fa, fa_synth, dev):
