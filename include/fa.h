@@ -78,7 +78,13 @@ typedef enum {
  * log2(e) folded into the scale, and a per-row LSE saved for fa_bwd
  * ("Triton 06: Flash Attention v2", Improvements 1-3).  Causal runs the
  * fully visible key blocks without a mask and masks only the diagonal
- * blocks; key blocks wholly in the future are never read.
+ * blocks; key blocks wholly in the future are never read.  Short 16-bit
+ * problems with fewer 256-query work items than compute units, whose keys
+ * fit in LDS (N <= 512 at d = 64, N <= 256 at d = 128), run 64-query
+ * blocks instead, each block's keys split over four waves and the partial
+ * results merged with the log-sum-exp form of the softmax decomposition
+ * ("Paper review: FlashAttention ...", "Tiling"); the result is the same
+ * softmax up to rounding.
  * q, k, v, o, lse: device pointers, 16-byte aligned, not aliased with each
  * other.
  */

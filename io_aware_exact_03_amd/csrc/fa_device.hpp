@@ -158,6 +158,28 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, void* dst, uint32_t byte_of
 __device__ __forceinline__ void load_lds4(rsrc_t r, void* dst, uint32_t byte_off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 4, byte_off, 0, 0, 0);
 }
+// The same 16-byte load straight into LDS, issued from inline assembly so
+// that the compiler does not track it.  The compiler's wait insertion cannot
+// tell one LDS range from another for these loads and would make the first
+// LDS read after them wait for all; with this form it adds no wait at all,
+// and the caller waits explicitly (vm_wait, then lds_fence) before it reads
+// the destination.  lds_dst is the wave-uniform LDS byte address (through
+// M0); the load has no result registers.  Counted in vmcnt like any load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t)(const_cast<void*>(p));
+}
+__device__ __forceinline__ void load_lds16_untracked(rsrc_t r, uint32_t lds_dst, uint32_t byte_off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_dst), "v"(byte_off), "s"(r)
+      : "memory", "m0");
+}
+// Keeps the compiler from moving memory accesses across this point (after an
+// explicit wait for loads it does not track).
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
+
 // Workgroup barrier for loops that keep loads into LDS in flight across
 // it.  __syncthreads() fences all LDS writes, including those loads, so it
 // would wait for every one of them; here the caller names how many of its

@@ -542,6 +542,272 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   }
 }
 // ===========================================================================
+// 16-bit forward for short sequences on few heads: the keys of a block are
+// split among the waves of its workgroup
+// ===========================================================================
+// When B H ceil(N / 256) work items leave CUs idle and every key a block can
+// see fits in LDS (at most KMAX keys), the query blocks shrink to 64 rows and
+// each workgroup's eight waves split the work as two 32-query groups x four
+// key ranges of at most SMAX 32-key sub-blocks.  A wave fetches what it
+// reads straight into LDS (swizzled row-major, as the persistent kernel's
+// tiles): its group's Q rows, then K, then V of its sub-blocks.  It waits
+// only for its own loads, so no barrier stands between the loads and the
+// products, and its score products start while V is still arriving; the two
+// query groups of a key range both fetch it and write identical bytes to
+// identical LDS addresses.  With at most SMAX sub-blocks per wave the
+// softmax needs no running correction: the wave forms S^T = K Q^T for all of
+// them, takes the exact row max once, then adds the weights and
+// O^T += V^T P^T sub-block by sub-block.  Only the sub-block that holds the
+// causal diagonal or the sequence end is masked.  The four partial results
+// of a query group are merged through LDS with the log-sum-exp form of the
+// softmax decomposition ("Paper review: FlashAttention ...",
+// osehyeon.github.io, "Tiling"): M = max_r m_r, L = sum_r l_r 2^(m_r - M),
+// O = sum_r O_r 2^(m_r - M) / L.  Square attention only (queries and keys
+// share positions).
+template <int D>
+struct FwdSplit {
+  static constexpr int NW = 8, NT = 64 * NW, QG = 2, KQ = 4, BM = 32 * QG;
+  static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  static constexpr int KMAX = D == 64 ? 512 : 256;  // keys of K and V in 128 KB
+  static constexpr int RPP = 64 / CPR;              // rows per 1 KB wave load
+  static constexpr int PPS = 32 / RPP;              // wave loads per 32-row sub-block of K (or V)
+  static constexpr int SMAX = KMAX / 32 / KQ;       // sub-blocks per key range, at most
+  static constexpr int PROW = D + 4;                // floats per row of a partial O (padded)
+  static constexpr int KV_BYTES = 2 * KMAX * D * 2 + BM * D * 2;  // K, V, then the block's Q rows
+  static constexpr int PART_BYTES = NW * 32 * PROW * 4;
+  static constexpr int LDS_BYTES = KV_BYTES > PART_BYTES ? KV_BYTES : PART_BYTES;
+  static_assert(PPS + 2 * PPS * SMAX < 64, "vmcnt range");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void fwd16_split_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    uint16_t* __restrict__ og, float* __restrict__ lseg, int N, int n_qblk, int G, float qk_scale,
+    uint32_t qsign) {
+  using C = FwdSplit<D>;
+  constexpr int DS = C::DS, DB = C::DB, CPR = C::CPR, PPS = C::PPS, SMAX = C::SMAX;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::LDS_BYTES];
+  __shared__ float mrg_m[C::QG][C::KQ][32], mrg_l[C::QG][C::KQ][32];
+  uint16_t* k_lds = reinterpret_cast<uint16_t*>(lds_raw);
+  uint16_t* v_lds = k_lds + C::KMAX * D;
+  uint16_t* q_lds = v_lds + C::KMAX * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const int qgrp = wave & 1, kq = wave >> 1;
+  // The blocks of one head go to one XCD (contiguous logical numbers per
+  // XCD), where they share the head's K/V in that XCD's L2.
+  const int lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lb / n_qblk, qblk = lb % n_qblk;
+  const int q0 = qblk * C::BM;
+  const int qw0 = q0 + 32 * qgrp;  // first query of this wave
+  const int query = qw0 + n;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;
+  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
+
+  // ---- this wave's sub-blocks ---------------------------------------------
+  // The block's visible keys form ns sub-blocks, dealt to the four key
+  // ranges; a causal wave stops at its diagonal sub-block (qw0 / 32), and a
+  // wave whose queries all lie past N has nothing to do.
+  const int kend = CAUSAL ? min(q0 + C::BM, N) : N;  // <= KMAX (host-checked)
+  const int ns = (kend + 31) / 32;
+  const int u0 = kq * ns / C::KQ;
+  int ul = (kq + 1) * ns / C::KQ - 1;
+  if (CAUSAL) ul = min(ul, qw0 / 32);
+  if (qw0 >= N) ul = u0 - 1;
+  const int nsb = max(ul - u0 + 1, 0);  // 0 .. SMAX
+  // The one sub-block that needs the mask: the diagonal, or the one that
+  // holds the sequence end when N is not a multiple of 32.  Keys before it
+  // are visible to every query of the wave.
+  const int mu = CAUSAL ? qw0 / 32 : (N % 32 != 0 ? ns - 1 : -1);
+  const int key_lim = CAUSAL ? min(query + 1, N) : N;
+
+  const rsrc_t qrs = make_rsrc(qg + (size_t)bh * N * D, head_bytes);
+  uint4 qf[DS];
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_raw = kNegInf;               // row max of the raw scores
+  float m_run = kNegInf, l_run = 0.f;  // row max (scaled, log2 units) and this lane's sum
+
+  // Slot i of the wave holds sub-block u0 + i; slots past the wave's last
+  // sub-block hold the block's last one again (loaded, not used).
+  uint16_t* const qs = q_lds + qgrp * 32 * D;
+  auto slot_u = [&](int i) { return min(u0 + i, ns - 1); };
+  auto kslot = [&](int i) { return k_lds + 32 * slot_u(i) * D; };
+  auto vslot = [&](int i) { return v_lds + 32 * slot_u(i) * D; };
+  {
+    // Wave load p of 32 rows fills RPP of them: lane l writes bytes 16 l,
+    // i.e. row RPP p + l / CPR, stored chunk l % CPR holding the row's
+    // logical chunk (l % CPR) ^ swz_chunk(row) (the swizzle repeats every 16
+    // rows, so slot rows and block rows agree).  Rows past N read as zeros.
+    // Every wave issues the same loads in the same order, so the count still
+    // in flight behind any of them is a compile-time constant.
+    auto issue32 = [&](const rsrc_t& rs, uint16_t* dst, int row0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < PPS; ++p) {
+        const int row = p * C::RPP + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_chunk<D>(row);
+        load_lds16_untracked(rs, lds_addr(dst + p * C::RPP * D), ((uint32_t)(row0 + row) * D + 8 * chunk) * 2);
+      }
+    };
+    issue32(qrs, qs, qw0);
+#pragma unroll
+    for (int i = 0; i < SMAX; ++i) issue32(krs, kslot(i), 32 * slot_u(i));
+#pragma unroll
+    for (int i = 0; i < SMAX; ++i) issue32(vrs, vslot(i), 32 * slot_u(i));
+
+    // ---- scores of every slot, then the exact row max over them -----------
+    f32x16 sc[SMAX];
+    auto scores = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (i >= nsb) return;
+      // Q and this slot's K are in LDS once only later K slots and the V
+      // slots may remain in flight
+      vm_wait<(SMAX - 1 - i) * PPS + SMAX * PPS>();
+      lds_fence();
+      if (i == 0) {
+        // Q fragments (B operand of S^T = K Q^T): lane supplies
+        // Q[query][16 s + 8 g + 0..7]; a negative scale flips their sign bits
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          qf[s] = read_row<D>(qs, n, 16 * s + 8 * g);
+          qf[s].x ^= qsign; qf[s].y ^= qsign; qf[s].z ^= qsign; qf[s].w ^= qsign;
+        }
+      }
+      const uint16_t* kt = kslot(i);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int st = 0; st < DS; ++st) s = mma16(T{}, read_row<D>(kt, n, 16 * st + 8 * g), qf[st], s);
+      sc[i] = s;
+      const int u = u0 + i;
+      // raw max; only the diagonal / sequence-end sub-block has invisible keys
+      if (u == mu) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kb = 32 * u + 4 * g + 8 * (r / 4) + (r % 4);
+          m_raw = fmaxf(m_raw, kb < key_lim ? s[r] : kNegInf);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m_raw = fmaxf(m_raw, s[r]);
+      }
+    };
+    // ---- weights and O^T += V^T P^T, slot by slot --------------------------
+    auto accumulate = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (i >= nsb) return;
+      const int u = u0 + i;
+      const f32x16& s = sc[i];
+      uint32_t pk[8];
+      // weights packed to 16 bits (the B operand of the PV product); returns
+      // this lane's sum of them
+      auto weights = [&](auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = fast_exp2(__builtin_fmaf(s[r], qk_scale, -m_run));
+          float p1 = fast_exp2(__builtin_fmaf(s[r + 1], qk_scale, -m_run));
+          if constexpr (MASKED) {
+            const int kb = 32 * u + 4 * g + 8 * (r / 4) + (r % 4);
+            p0 = kb < key_lim ? p0 : 0.f;
+            p1 = kb + 1 < key_lim ? p1 : 0.f;
+          }
+          pk[r / 2] = pack2(T{}, p0, p1);
+          part[(r / 2) % 2] = r < 4 ? first_pair(T{}, pk[r / 2], p0, p1)
+                                    : add_pair(T{}, pk[r / 2], p0, p1, part[(r / 2) % 2]);
+        }
+        return part[0] + part[1];
+      };
+      l_run += (u == mu) ? weights(std::true_type{}) : weights(std::false_type{});
+      const uint4 pp[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+      // this slot's V is in LDS once only the later V slots remain in flight
+      vm_wait<(SMAX - 1 - i) * PPS>();
+      lds_fence();
+      const uint16_t* vt = vslot(i);
+#pragma unroll
+      for (int k2 = 0; k2 < DS; ++k2) {
+        const uint4 b = read_tr<D>(vt, 16 * (k2 / DB), 32 * (k2 % DB), lane);
+        oacc[k2 % DB] = mma16(T{}, b, pp[k2 / DB], oacc[k2 % DB]);
+      }
+    };
+    scores(std::integral_constant<int, 0>{});
+    scores(std::integral_constant<int, 1>{});
+    if constexpr (SMAX == 4) {
+      scores(std::integral_constant<int, 2>{});
+      scores(std::integral_constant<int, 3>{});
+    }
+    // the two lane halves hold different keys of the same queries; the
+    // scale is >= 0, so scaling the raw max gives the max of the scaled scores
+    m_run = halves_max(m_raw) * qk_scale;
+    accumulate(std::integral_constant<int, 0>{});
+    accumulate(std::integral_constant<int, 1>{});
+    if constexpr (SMAX == 4) {
+      accumulate(std::integral_constant<int, 2>{});
+      accumulate(std::integral_constant<int, 3>{});
+    }
+  }
+  const float m = nsb > 0 ? m_run : kNegInf;
+
+  // ---- merge the four key ranges of each query group ----------------------
+  const float l_tot = halves_sum(l_run);
+  if (g == 0) {
+    mrg_m[qgrp][kq][n] = m;
+    mrg_l[qgrp][kq][n] = l_tot;
+  }
+  // Every load into LDS has landed (a wave with idle slots, or none live,
+  // still has loads in flight here, which the compiler does not know of)
+  // before the partial results below overwrite K and V.
+  vm_wait<0>();
+  lds_fence();
+  __syncthreads();  // every wave is done with K and V, and m, l are shared
+  float M = kNegInf;
+#pragma unroll
+  for (int r = 0; r < C::KQ; ++r) M = fmaxf(M, mrg_m[qgrp][r][n]);
+  float L = 0.f;
+#pragma unroll
+  for (int r = 0; r < C::KQ; ++r) {
+    const float mr = mrg_m[qgrp][r][n];
+    L += (mr == kNegInf) ? 0.f : mrg_l[qgrp][r][n] * fast_exp2(mr - M);
+  }
+  const float wself = (m == kNegInf) ? 0.f : fast_exp2(m - M) / L;
+  // this wave's weighted partial O, row-major [32][PROW] fp32: register r of
+  // d block db is column 32 db + 8 (r / 4) + 4 g + r % 4 of row n
+  float* part = reinterpret_cast<float*>(lds_raw) + wave * 32 * C::PROW;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(part + n * C::PROW + 32 * db + 8 * j + 4 * g) =
+          make_float4(oacc[db][4 * j] * wself, oacc[db][4 * j + 1] * wself, oacc[db][4 * j + 2] * wself,
+                      oacc[db][4 * j + 3] * wself);
+  if (kq == 0 && g == 0 && query < N) lseg[(size_t)bh * N + query] = (M + __log2f(L)) * kLn2;
+  __syncthreads();
+  // O = the sum of the four partials, 8 elements (16 bytes) per store
+  const rsrc_t ors = make_rsrc(og + (size_t)bh * N * D, head_bytes);
+  for (int c = threadIdx.x; c < C::BM * CPR; c += C::NT) {
+    const int row = c / CPR, ch = c % CPR, grp = row / 32, rn = row % 32;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < C::KQ; ++r) {
+      const float* src = reinterpret_cast<const float*>(lds_raw) + (2 * r + grp) * 32 * C::PROW + rn * C::PROW + 8 * ch;
+      const float4 x = *reinterpret_cast<const float4*>(src);
+      const float4 y = *reinterpret_cast<const float4*>(src + 4);
+      acc8[0] += x.x; acc8[1] += x.y; acc8[2] += x.z; acc8[3] += x.w;
+      acc8[4] += y.x; acc8[5] += y.y; acc8[6] += y.z; acc8[7] += y.w;
+    }
+    const uint4 o = make_uint4(pack2(T{}, acc8[0], acc8[1]), pack2(T{}, acc8[2], acc8[3]),
+                               pack2(T{}, acc8[4], acc8[5]), pack2(T{}, acc8[6], acc8[7]));
+    // rows past N fall outside the head's range and are dropped
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, o), ors,
+                                           ((uint32_t)(q0 + row) * D + 8 * ch) * 2, 0, 0);
+  }
+}
+// ===========================================================================
 // fp32 forward: same structure on v_mfma_f32_32x32x2_f32, P kept in fp32.
 // ===========================================================================
 template <int D, int BN, int NW, bool CAUSAL>
@@ -718,6 +984,13 @@ struct Tile16 {
   static constexpr int BN = D == 128 ? 64 : 128;
 };
 
+// The key-split kernel serves square problems whose work items leave CUs
+// idle and whose keys fit its LDS.
+template <int D>
+bool split_keys(const FwdArgs& a, int items, int cus) {
+  return a.Nk == a.N && items < cus && a.N <= FwdSplit<D>::KMAX;
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const FwdArgs& a) {
   constexpr int BN = Tile16<D>::BN;
@@ -735,6 +1008,16 @@ hipError_t launch16(const FwdArgs& a) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
+  if (split_keys<D>(a, (int)items, cus)) {
+    // fewer items than CUs: 64-query blocks, keys split inside the workgroup
+    using S = FwdSplit<D>;
+    const int nb = (a.N + S::BM - 1) / S::BM;
+    hipLaunchKernelGGL((fwd16_split_kernel<T, D, CAUSAL>), dim3((unsigned)(nb * a.BH)), dim3(S::NT), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, nb, a.G,
+                       a.qk_scale, a.neg ? 0x80008000u : 0u);
+    return hipGetLastError();
+  }
   const int grid = (int)(items < cus ? items : cus);
   hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),

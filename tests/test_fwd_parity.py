@@ -37,6 +37,27 @@ def test_small_shapes(N, causal, d, dtype):
     P.check_fwd_full(q, k, v, o, lse, scale, causal, dtype, f"N={N} d={d} causal={causal} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 65, 129, 300, 513])
+def test_small_shapes_persistent_kernel(N, causal, d, dtype):
+    """Short sequences with enough heads (B2 H128) that the persistent
+    256-query kernel has at least one work item per CU and serves them
+    (with fewer heads the key-split kernel does): ragged tails, the masked
+    sub-block, several heads per workgroup; sampled whole heads."""
+    fa = _fa()
+    q, k, v = fa_synth.make_inputs(2, 128, N, d, dtype, seed=7050 + N + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(*P.to_dev(q, k, v), scale, causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for (b, h) in P.heads_to_check(2, 128, 3, seed=7050 + N):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        P.check_fwd_full(q[sl], k[sl], v[sl], o[sl], lse[sl], scale, causal, dtype,
+                         f"B2 H128 head ({b},{h}) N={N} d={d} causal={causal} {dtype}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_heads_grid_order(dtype, causal):
@@ -51,15 +72,18 @@ def test_many_heads_grid_order(dtype, causal):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
-def test_scale_values(dtype, scale):
+@pytest.mark.parametrize("d,N", [(128, 333), (64, 333), (128, 200)])
+def test_scale_values(dtype, scale, d, N):
     """Negative scale (folded into the sign of Q), zero scale (uniform
-    weights) and a large scale (sharp softmax)."""
+    weights) and a large scale (sharp softmax); with two heads, d = 128 at
+    N = 333 runs the persistent kernel and the other two shapes the
+    key-split one (16-bit types)."""
     fa = _fa()
     for causal in (False, True):
-        q, k, v = fa_synth.make_inputs(1, 2, 333, 128, dtype, seed=7200)
+        q, k, v = fa_synth.make_inputs(1, 2, N, d, dtype, seed=7200)
         o, lse = fa.fwd(*P.to_dev(q, k, v), scale, causal)
         torch.cuda.synchronize()
-        P.check_fwd_full(q, k, v, o, lse, scale, causal, dtype, f"scale={scale} causal={causal} {dtype}")
+        P.check_fwd_full(q, k, v, o, lse, scale, causal, dtype, f"scale={scale} d={d} N={N} causal={causal} {dtype}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
