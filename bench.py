@@ -11,8 +11,11 @@ The same run also times, as separate legs reported under "legs": the causal
 prefill forward (B2 H32 N8192 d128 bf16), the long causal forward and the
 naive three-kernel baseline (B1 H16 N16384 d64 bf16), the non-causal fp16
 sweep N=512..4096 (fused vs naive, with the byte models), and the fp32
-single-head forward.  `cpu_baseline` times the fp64 oracle on a sample of the
-step's heads on the host cores.
+single-head forward.  The sweep and the single-head legs are short calls:
+their times come from back-to-back calls replayed from a HIP graph (host
+launch cost excluded), with the single eager call's time beside them.
+`cpu_baseline` times the fp64 oracle on a sample of the step's heads on the
+host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -178,6 +181,30 @@ def time_reps(fn, reps: int, torch):
         ts.append(a.elapsed_time(b))
     ts.sort()
     return ts[len(ts) // 2], ts[0]
+
+
+def time_graph(fn, torch, eager_ms: float, reps: int = 10, target_ms: float = 1.0):
+    """Per-call milliseconds of fn() with the host launch cost taken out:
+    `calls` back-to-back calls (enough for about target_ms of GPU work) are
+    captured into one HIP graph, which is replayed reps times between HIP
+    events; returns (median per-call ms, calls)."""
+    calls = max(1, min(50, int(math.ceil(target_ms / max(eager_ms, 1e-3)))))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ms, _ = time_reps(g.replay, reps, torch)
+    del g
+    return ms / calls, calls
 
 
 def cpu_baseline(w, q, k, v, do, target_s: float):
@@ -804,13 +831,20 @@ def run_legs(torch, fa, fa_synth, dev):
         del q, k, v, lens, ws, o, lse
         torch.cuda.empty_cache()
 
-    # non-causal fp16 sweep, fused vs naive, with the byte models
+    # non-causal fp16 sweep, fused vs naive, with the byte models.  These
+    # calls are short (tens of microseconds at N = 512), so one call between
+    # two events mostly measures the host launch; fwd_ms is the per-call time
+    # of back-to-back calls replayed from a HIP graph, and fwd_ms_eager_call
+    # the single-call figure beside it.
     for w in fa_synth.NONCAUSAL_SWEEP:
         q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
         o, lse = fa.fwd(q, k, v, w.scale, w.causal)
-        ms, _ = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 20, torch)
+        fn = lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        ms_eager, _ = time_reps(fn, 20, torch)
+        ms, calls = time_graph(fn, torch, ms_eager)
         tf = fwd_flops(w.B, w.H, w.N, w.d, False) / (ms * 1e-3) / 1e12
-        entry = {"fwd_ms": ms, "fwd_tflops": tf, "alg_bytes": fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)}
+        entry = {"fwd_ms": ms, "fwd_tflops": tf, "fwd_ms_eager_call": ms_eager, "graph_calls": calls,
+                 "alg_bytes": fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)}
         entry.update(naive_leg(torch, fa, w, q, k, v, dev, ms))
         legs[w.name] = entry
         log(f"[bench] {w.name}: {entry}")
@@ -844,12 +878,15 @@ def run_legs(torch, fa, fa_synth, dev):
         del q, k, v, ws, o, lse
         torch.cuda.empty_cache()
 
-    # fp32 single head
+    # fp32 single head (graph-replayed like the sweep: one call is short)
     w = fa_synth.SINGLE_HEAD_F32
     q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
     o, lse = fa.fwd(q, k, v, w.scale, w.causal)
-    ms, _ = time_reps(lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), 50, torch)
-    entry = {"fwd_ms": ms, "fwd_gflops": fwd_flops(1, 1, w.N, w.d, False) / (ms * 1e-3) / 1e9}
+    fn = lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+    ms_eager, _ = time_reps(fn, 50, torch)
+    ms, calls = time_graph(fn, torch, ms_eager)
+    entry = {"fwd_ms": ms, "fwd_gflops": fwd_flops(1, 1, w.N, w.d, False) / (ms * 1e-3) / 1e9,
+             "fwd_ms_eager_call": ms_eager, "graph_calls": calls}
     entry.update(naive_leg(torch, fa, w, q, k, v, dev, ms))
     legs[w.name] = entry
     log(f"[bench] {w.name}: {entry}")
@@ -867,13 +904,16 @@ def naive_leg(torch, fa, w, q, k, v, dev, fused_ms):
     p = torch.empty_like(s)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s, p_ws=p)
-    ms, _ = time_reps(lambda: fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s, p_ws=p), 5, torch)
+    fn = lambda: fa.naive_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, s_ws=s, p_ws=p)
+    fn()
+    ms_eager, _ = time_reps(fn, 5, torch)
+    ms, calls = time_graph(fn, torch, ms_eager, reps=5)
     naive_bytes = naive_fwd_bytes(w.B, w.H, w.N, w.d, e_in, e_ws)
     fused_bytes = fused_fwd_bytes(w.B, w.H, w.N, w.d, e_in)
     del s, p, o, lse
     torch.cuda.empty_cache()
-    return {"naive_ms": ms, "speedup_fused_over_naive": ms / fused_ms, "naive_model_bytes": naive_bytes,
+    return {"naive_ms": ms, "naive_ms_eager_call": ms_eager, "naive_graph_calls": calls,
+            "speedup_fused_over_naive": ms / fused_ms, "naive_model_bytes": naive_bytes,
             "fused_model_bytes": fused_bytes, "model_byte_ratio": naive_bytes / fused_bytes,
             "naive_model_gbs": naive_bytes / (ms * 1e-3) / 1e9}
 
