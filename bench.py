@@ -274,6 +274,13 @@ def main():
                     help="write profiles/kernel_stats_<workload>.md from a rocprofv3 kernel trace of the "
                          "default training-step run (--legs 0 --cpu-baseline 0) and exit")
     ap.add_argument("--ceilings", type=int, default=1, help="also measure the chip's ceilings (1) or not (0)")
+    ap.add_argument("--lib", metavar="PATH",
+                    help="load this build of libfa.so (a tile variant from io_aware_exact_03_amd.build --variant)")
+    ap.add_argument("--tile-probe", action="store_true",
+                    help="run only the kernels the tile sweep profiles: the training step and the d = 64 "
+                         "forwards (non-causal fp16 B4 H8 N4096, causal bf16 B1 H16 N16384), --steps times each")
+    ap.add_argument("--tile-sweep-write", metavar="DIR",
+                    help="write profiles/tile_sweep_*.md from DIR/<variant>/{sq,kt} rocprofv3 runs of --tile-probe")
     args = ap.parse_args()
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.calib_copy_mib)
@@ -284,6 +291,11 @@ def main():
     if args.stats:
         write_stats(args.stats, args.steps, args.warmup)
         return
+    if args.tile_sweep_write:
+        write_tile_sweep(args.tile_sweep_write)
+        return
+    if args.lib:
+        os.environ["IO_AWARE_FA_LIB"] = os.path.abspath(args.lib)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only (the attention kernels "
               f"run per (batch, head) on a single MI355X; no multi-GPU path exists)", file=sys.stderr)
@@ -299,6 +311,9 @@ def main():
     digest = source_digest()
     if args.traffic_legs:
         run_traffic_legs(torch, fa, fa_synth, dev, args.calib_copy_mib)
+        return
+    if args.tile_probe:
+        run_tile_probe(torch, fa, fa_synth, dev, args.steps, args.warmup)
         return
 
     # ---------------- the timed step: causal training step ----------------
@@ -442,6 +457,176 @@ def main():
         "source_digest": digest,
     }
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Tile sweep: the same kernels built with other tile constants (the FA_*
+# defines of csrc/fa_plan.hpp), each profiled with one SQ-counter pass and a
+# kernel trace of --tile-probe.
+# ---------------------------------------------------------------------------
+TILE_VARIANTS = [
+    # name, defines, forward (waves, BN at d = 64), dQ waves
+    ("shipped", (), (8, 128), 8),
+    ("fwd_w4", ("FA_FWD16_WAVES=4",), (4, 128), 8),
+    ("fwd_bn64", ("FA_FWD16_BN_D64=64",), (8, 64), 8),
+    ("fwd_w4_bn64", ("FA_FWD16_WAVES=4", "FA_FWD16_BN_D64=64"), (4, 64), 8),
+    ("dq_w4", ("FA_DQ_WAVES=4",), (8, 128), 4),
+]
+TILE_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+                 "SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE")
+
+
+def run_tile_probe(torch, fa, fa_synth, dev, reps: int, warmup: int):
+    """The kernels the tile sweep compares, reps times each after warmup:
+    the causal training step (fwd16 and dQ at d = 128, dK/dV) and the d = 64
+    forwards of the non-causal sweep (N = 4096) and the long causal
+    workload.  Prints one JSON line of mean event milliseconds."""
+    res = {"lib": os.environ.get("IO_AWARE_FA_LIB", "shipped")}
+    w = fa_synth.TRAIN_STEP
+    q, k, v, do = (t.to(dev) for t in fa_synth.workload_inputs(w))
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), **f32)
+    bufs = dict(delta=torch.empty((w.B, w.H, w.N), **f32), dq=torch.empty((w.B, w.H, w.N, w.d), **f32),
+                dk=torch.empty((w.B, w.H, w.N, w.d), **f32), dv=torch.empty((w.B, w.H, w.N, w.d), **f32))
+    def step():
+        fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, **bufs)
+    for _ in range(warmup):
+        step()
+    ms, _ = time_reps(step, reps, torch)
+    res[w.name] = ms
+    del q, k, v, do, o, lse, bufs
+    for w in (fa_synth.NONCAUSAL_SWEEP[-1], fa_synth.LONG_CAUSAL):
+        q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        fn = lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        for _ in range(warmup):
+            fn()
+        res[w.name], _ = time_reps(fn, reps, torch)
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
+def _tile_rows(sq_csv: str, kt_csv: str):
+    """Per kernel name: mean duration (us) and the summed counters, averaged
+    over its dispatches (counters summed over the counter instances first)."""
+    import collections
+    import csv
+
+    dur = collections.defaultdict(list)
+    with open(kt_csv) as f:
+        for r in csv.DictReader(f):
+            dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    with open(sq_csv) as f:
+        for r in csv.DictReader(f):
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    by_name = collections.defaultdict(list)
+    for did, c in per.items():
+        by_name[names[did]].append(c)
+    out = {}
+    for name, lst in by_name.items():
+        keys = set().union(*lst)
+        ds = sorted(dur.get(name, []))
+        out[name] = {"n": len(lst), "dur_us": ds[len(ds) // 2] if ds else float("nan"), "n_trace": len(ds),
+                     **{k2: sum(c.get(k2, 0.0) for c in lst) / len(lst) for k2 in keys}}
+    return out
+
+
+def _kernel_label(name: str) -> str:
+    """fwd16<BF16, d128, BN64, causal> style label from a kernel's
+    demangled name (its template arguments)."""
+    import re
+
+    m = re.search(r"(fwd16_kernel|bwd_dq_kernel|bwd_dkdv_kernel)<fa::(\w+), (\d+), (\w+)(?:, (\w+))?(?:, (\w+))?>", name)
+    if not m:
+        return name.split("(")[0]
+    kind, dt, d = m.group(1), m.group(2), m.group(3)
+    if kind == "fwd16_kernel":  # <T, D, BN, CAUSAL>
+        return f"fwd16<{dt}, d{d}, BN{m.group(4)}, {'causal' if m.group(5) == 'true' else 'non-causal'}>"
+    return f"{kind[:-7]}<{dt}, d{d}, {'causal' if m.group(4) == 'true' else 'non-causal'}>"
+
+
+def write_tile_sweep(root: str):
+    """profiles/tile_sweep_{fwd16,dq,dkdv}.md from the --tile-probe runs under
+    root/<variant>/sq (counter pass) and root/<variant>/kt (kernel trace)."""
+    rows = {}
+    for name, _, _, _ in TILE_VARIANTS:
+        d = os.path.join(root, name)
+        rows[name] = _tile_rows(os.path.join(d, "sq", "run_counter_collection.csv"),
+                                os.path.join(d, "kt", "run_kernel_trace.csv"))
+
+    def line(variant, shape, kname, c):
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8  # summed over the 8 XCDs
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * gui) if gui else float("nan")
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        lds_act = c.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        conflicts = 100 * c.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds_act if lds_act else 0.0
+        lds_wait = 100 * c.get("SQ_WAIT_INST_LDS", 0.0) / wc if wc else 0.0
+        return (f"| {variant} | `{_kernel_label(kname)}` | {shape} | {c['dur_us']:.1f} | {mf / 1e6:.2f} | "
+                f"{c.get('SQ_INSTS_VALU', 0.0) / mf:.2f} | {c.get('SQ_INSTS_LDS', 0.0) / mf:.2f} | "
+                f"{conflicts:.2f}% | {lds_wait:.1f}% | {100 * busy:.1f}% |")
+
+    head = ("| variant | kernel | tile (BM x BN, waves) | median time (us) | MFMA (M) | VALU / MFMA | LDS / MFMA | "
+            "LDS bank conflicts / LDS active | LDS wait / wave cycles | MFMA busy |\n"
+            "|---|---|---|---|---|---|---|---|---|---|\n")
+    cmd = ("For each variant V (defines in the table below), on the MI355X box with TMPDIR=/tmp:\n\n```\n"
+           "python3 -m io_aware_exact_03_amd.build --variant V -D MACRO=VALUE ...   # not for 'shipped'\n"
+           f"rocprofv3 --pmc {TILE_COUNTERS} --output-format csv \\\n"
+           "    -d gpurun_out/tile/V/sq -o run -- python3 bench.py --tile-probe --steps 3 --warmup 1 --lib LIB\n"
+           "rocprofv3 --kernel-trace --output-format csv -d gpurun_out/tile/V/kt -o run -- \\\n"
+           "    python3 bench.py --tile-probe --steps 15 --warmup 2 --lib LIB\n"
+           "python3 bench.py --tile-sweep-write gpurun_out/tile\n```\n\n"
+           "LIB is io_aware_exact_03_amd/_build/variants/V/libfa.so (for 'shipped', io_aware_exact_03_amd/libfa.so).  "
+           "Each variant passed the forward and chunked-prefill parity tests (forward variants) or the backward "
+           "parity tests (dQ variant) against the oracle before it was profiled.  Per kernel: the median duration "
+           "over the kernel-trace run's dispatches, and the counters averaged over the counter run's.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8), "
+           "the fraction of SIMD cycles the matrix cores were busy at the clock the chip held.  Counts are wave "
+           "instructions; one MFMA is one 32x32x16 product.\n\n"
+           "| variant | defines |\n|---|---|\n"
+           + "".join(f"| {n} | {' '.join(dd) or '(none)'} |\n" for n, dd, _, _ in TILE_VARIANTS) + "\n")
+
+    def table(match, shape_of):
+        out = head
+        for name, _, fw, qw in TILE_VARIANTS:
+            for kname, c in sorted(rows[name].items()):
+                if match(kname):
+                    out += line(name, shape_of(kname, fw, qw), kname, c) + "\n"
+        return out
+
+    def fwd_shape(kname, fw, qw):
+        import re
+
+        m = re.search(r"fwd16_kernel<fa::\w+, \d+, (\d+),", kname)
+        return f"{32 * fw[0]} x {m.group(1) if m else '?'}, {fw[0]}"
+
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "tile_sweep_fwd16.md"), "w") as f:
+        f.write("# Tile sweep: 16-bit forward (fwd16_kernel)\n\n"
+                "Workloads: the causal train step B4 H16 N4096 d128 bf16 (its forward), the non-causal "
+                "B4 H8 N4096 d64 fp16 forward and the long causal B1 H16 N16384 d64 bf16 forward.  At d = 128 "
+                "the K/V tile stays at 64 keys: five ring buffers of 16 KB each for K and for V fill the 160 KB "
+                "LDS, so BN = 128 would need a shallower ring.\n\n"
+                + cmd + table(lambda k: "fwd16_kernel" in k, fwd_shape))
+    with open(os.path.join(PROFILES, "tile_sweep_dq.md"), "w") as f:
+        f.write("# Tile sweep: dQ kernel (bwd_dq_kernel)\n\n"
+                "Workload: the causal train step B4 H16 N4096 d128 bf16.  The K/V tile is 64 keys at d = 128 "
+                "(four ring buffers fill the LDS).\n\n"
+                + cmd + table(lambda k: "bwd_dq_kernel" in k, lambda kname, fw, qw: f"{32 * qw} x 64, {qw}"))
+    with open(os.path.join(PROFILES, "tile_sweep_dkdv.md"), "w") as f:
+        f.write("# Tile sweep: dK/dV kernel (bwd_dkdv_kernel)\n\n"
+                "Workload: the causal train step B4 H16 N4096 d128 bf16.  The dK/dV kernel has one shape: 128 "
+                "keys per workgroup as four pairs of waves (32 keys each), 64-query blocks taken as two 32-query "
+                "halves in alternating phases.  Its causal plan relies on that shape (the masked query blocks of "
+                "a 128-key block are its first two), so every variant builds it unchanged and its rows show the "
+                "run-to-run spread of one kernel.\n\n"
+                + cmd + table(lambda k: "bwd_dkdv_kernel" in k, lambda kname, fw, qw: "64 x 128, 8"))
+    print("wrote profiles/tile_sweep_fwd16.md, tile_sweep_dq.md, tile_sweep_dkdv.md")
 
 
 TRAFFIC_KERNELS = {"fwd16_kernel": "fa_fwd", "bwd_delta_kernel": "bwd_delta", "bwd_dkdv_kernel": "bwd_dkdv",

@@ -57,11 +57,13 @@ class FaError(RuntimeError):
 
 
 def load(path: str | None = None):
-    """Load libfa.so once (raises OSError if it is not built)."""
+    """Load libfa.so once (raises OSError if it is not built).  The
+    IO_AWARE_FA_LIB environment variable names another build of the same
+    library (a tile variant) to load instead."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("IO_AWARE_FA_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise OSError(f"{p} is not built; run io_aware_exact_03_amd.build or __graft_entry__.build()")
     lib = ctypes.CDLL(p)

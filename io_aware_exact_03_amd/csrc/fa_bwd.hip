@@ -623,7 +623,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct QG {
-  static constexpr int NW = 8, NT = 64 * NW, BM = NW * 32;
+  static constexpr int NW = FA_DQ_WAVES, NT = 64 * NW, BM = NW * 32;
   static constexpr int BN = D == 128 ? 64 : 128;  // 16 KB of K and of V per tile
   static constexpr int DS = D / 16, DB = D / 32, SUB = BN / 32, CPR = D / 8;
   static constexpr int RPP = 64 / CPR;            // tile rows per 1 KB wave load

@@ -49,7 +49,8 @@ namespace fa {
 // ===========================================================================
 // 16-bit (bf16 / fp16) forward
 // ===========================================================================
-// Workgroup: 8 waves x 32 queries (BM = 256, two waves per SIMD).  K/V tiles
+// Workgroup: 8 waves x 32 queries (BM = 256, two waves per SIMD; a build may
+// define FA_FWD16_WAVES = 4 to time the one-wave-per-SIMD shape).  K/V tiles
 // of BN keys go from global memory straight into LDS (no registers), row-major
 // with the XOR chunk swizzle, into five buffers: the previous tile (whose V
 // the first step still reads), the tile being consumed, the next one (whose
@@ -58,7 +59,7 @@ namespace fa {
 // feeds O^T += V^T P^T through transposing reads (ds_read_b64_tr_b16).
 template <typename T, int D, int BN, bool CAUSAL>
 struct Fwd16 {
-  static constexpr int NW = 8, NT = NW * 64, BM = NW * 32;
+  static constexpr int NW = FA_FWD16_WAVES, NT = NW * 64, BM = NW * 32;
   static constexpr int DS = D / 16;          // k-steps of the S product
   static constexpr int DB = D / 32;          // 32-wide d blocks of O
   static constexpr int SUB = BN / 32;        // 32-key sub-blocks per tile
@@ -978,10 +979,11 @@ namespace {
 
 // Tile per head dim: 8 waves x 32 queries (two waves per SIMD), 64 keys per
 // tile for d = 128 and 128 for d = 64 (16 KB of K and of V per tile either
-// way).  Must agree with fwd_tile() in fa_plan.hpp.
+// way; five such buffers fill the LDS, so d = 128 has no larger tile).
+// Must agree with fwd_tile() in fa_plan.hpp.
 template <int D>
 struct Tile16 {
-  static constexpr int BN = D == 128 ? 64 : 128;
+  static constexpr int BN = D == 128 ? 64 : FA_FWD16_BN_D64;
 };
 
 // The key-split kernel serves square problems whose work items leave CUs

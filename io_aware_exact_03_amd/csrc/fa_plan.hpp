@@ -95,6 +95,23 @@ constexpr int kDecodeMaxParts = 1024;
 FA_HD int decode_tiles(int len) { return (len + kDecodeTileKeys - 1) / kDecodeTileKeys; }
 FA_HD int decode_query_blocks(int G) { return (G + 31) / 32; }
 
+// Tile constants of the 16-bit forward and of the dQ kernel.  The defaults
+// are the shapes the library ships; a build may define others (each wave
+// owns 32 queries; BN is the K/V tile of the d = 64 forward) to time the
+// alternatives.
+#ifndef FA_FWD16_WAVES
+#define FA_FWD16_WAVES 8
+#endif
+#ifndef FA_FWD16_BN_D64
+#define FA_FWD16_BN_D64 128
+#endif
+#ifndef FA_DQ_WAVES
+#define FA_DQ_WAVES 8
+#endif
+static_assert(FA_FWD16_WAVES == 4 || FA_FWD16_WAVES == 8, "forward waves per workgroup");
+static_assert(FA_FWD16_BN_D64 == 64 || FA_FWD16_BN_D64 == 128, "forward K/V tile at d = 64");
+static_assert(FA_DQ_WAVES == 4 || FA_DQ_WAVES == 8, "dQ waves per workgroup");
+
 // Forward tile shapes (query rows per workgroup, keys per K/V block, waves).
 struct FwdTile {
   int bm, bn, waves;
@@ -102,7 +119,7 @@ struct FwdTile {
 
 FA_HD FwdTile fwd_tile(int d, bool is_f32) {
   if (is_f32) return FwdTile{128, 64, 4};
-  return d == 128 ? FwdTile{256, 64, 8} : FwdTile{256, 128, 8};
+  return FwdTile{32 * FA_FWD16_WAVES, d == 128 ? 64 : FA_FWD16_BN_D64, FA_FWD16_WAVES};
 }
 
 }  // namespace fa
