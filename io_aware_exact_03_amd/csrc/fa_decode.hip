@@ -428,27 +428,35 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
   }
 }
 
-// Merge of the segments of one (unit, query column) that was cut between
-// parts: threads stride over the segments (32 column chunks x 8 segment
-// groups), then reduce through LDS.
+// Merge of the pieces of one (unit, live query column) that was cut between
+// parts: the 256 threads are 8 piece groups x 32 element chunks; each group
+// folds every 8th piece, and the groups are combined through LDS once for
+// the max and once for the sums.  With uniform lengths (kv_lens null) the
+// unit's first tile has a closed form; otherwise block sums over the batch
+// lengths locate it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ lpart,
                                                            const int* __restrict__ kv_lens,
                                                            uint16_t* __restrict__ og, float* __restrict__ lseg,
                                                            int B, int H, int G, int Nkv, int n_parts) {
-  constexpr int CH = D / 32;  // floats per column chunk
+  constexpr int CH = D / 32;  // floats per element chunk
   __shared__ float red[8][D];
-  __shared__ float rs[256];
+  __shared__ float rs[2][8];
   __shared__ int sums[512];
-  const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB;
-  const int u = blockIdx.x / 32, col = blockIdx.x % 32;
+  const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB, CPU = min(32, G);
+  const int u = blockIdx.x / CPU, col = blockIdx.x % CPU;
   const int b = u / UB, ui = u % UB, qb = ui % QB;
-  if (col >= min(32, G - 32 * qb)) return;
+  if (col >= min(32, G - 32 * qb)) return;  // (block-uniform returns throughout)
   const int nb = decode_tiles(decode_len(kv_lens, b, Nkv));
   if (nb == 0) return;
   int Ttot, P_b;
-  decode_block_sums<256>(kv_lens, B, Nkv, UB, b, sums, &Ttot, &P_b);
+  if (kv_lens == nullptr) {
+    Ttot = B * UB * nb;
+    P_b = b * UB * nb;
+  } else {
+    decode_block_sums<256>(kv_lens, B, Nkv, UB, b, sums, &Ttot, &P_b);
+  }
   const int per = (Ttot + n_parts - 1) / n_parts;
   const int P_u = P_b + ui * nb;
   const int w_first = P_u / per, w_last = (P_u + nb - 1) / per;
@@ -457,18 +465,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   const size_t slot0 = (size_t)w_first + u;
 
   const int tid = threadIdx.x, c = tid % 32, grp = tid / 32;
-  // M = max over the segments' LSEs.
+  // M = max over the pieces' LSEs
   float m = kNegInf;
-  for (int i = tid; i < np; i += 256) m = fmaxf(m, lpart[(slot0 + i) * 32 + col]);
-  rs[tid] = m;
+  for (int i = grp; i < np; i += 8) m = fmaxf(m, lpart[(slot0 + i) * 32 + col]);
+  if (c == 0) rs[0][grp] = m;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) rs[tid] = fmaxf(rs[tid], rs[tid + s]);
-    __syncthreads();
-  }
-  const float M = rs[0];
-  __syncthreads();
-  // Weighted sums: w_i = exp(LSE_i - M).
+  float M = kNegInf;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) M = fmaxf(M, rs[0][q]);
+  // weighted sums, w_i = exp(LSE_i - M)
   float acc[CH] = {};
   float wsum = 0.f;
   for (int i = grp; i < np; i += 8) {
@@ -480,12 +485,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   }
 #pragma unroll
   for (int e = 0; e < CH; ++e) red[grp][CH * c + e] = acc[e];
-  if (c == 0) rs[grp] = wsum;
+  if (c == 0) rs[1][grp] = wsum;
   __syncthreads();
   if (grp == 0) {
     float W = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) W += rs[q];
+    for (int q = 0; q < 8; ++q) W += rs[1][q];
     const float inv = 1.f / W;
     float o[CH];
 #pragma unroll
@@ -514,9 +519,11 @@ hipError_t run(const DecodeArgs& a) {
                      a.lpart, a.B, a.H, a.G, a.Nkv, qk_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.parts == 1) return e;
+  // one workgroup per (unit, query column that a unit can have live)
   const long long units = (long long)a.B * (a.H / a.G) * decode_query_blocks(a.G);
-  if (units * 32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(units * 32)), dim3(256), 0, a.stream, a.opart,
+  const long long grid = units * (a.G < 32 ? a.G : 32);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, a.stream, a.opart,
                      a.lpart, a.kv_lens, static_cast<uint16_t*>(a.o), a.lse, a.B, a.H, a.G, a.Nkv, a.parts);
   return hipGetLastError();
 }
