@@ -977,6 +977,147 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 // ===========================================================================
 namespace {
 
+// ===========================================================================
+// fp32 forward for short sequences on few heads: one 32-query block per
+// workgroup, its keys split over the eight waves
+// ===========================================================================
+// When the 128-query blocks of the fp32 kernel leave CUs idle, each
+// workgroup takes one block of 32 queries and its eight waves split the
+// block's visible keys into eight ranges of 32-key sub-blocks.  Each wave
+// runs the online softmax of the fp32 kernel over its range, and the eight
+// partial results are merged through LDS with the log-sum-exp form of the
+// softmax decomposition ("Paper review: FlashAttention ...",
+// osehyeon.github.io, "Tiling").  The operands come straight from global
+// memory (through L1/L2; no K/V tile is shared within the workgroup): in
+// S^T = K Q^T the contraction may run over the head dimension in any order,
+// so lane half g supplies elements g D/2 .. g D/2 + D/2 - 1 of its K and Q
+// rows, contiguous floats; O^T += V^T P^T takes, as in the fp32 kernel, the
+// key of accumulator register r on both operands.
+template <int D>
+struct Fwd32Split {
+  static constexpr int NW = 8, NT = 64 * NW, BM = 32;
+  static constexpr int DB = D / 32, HD = D / 2;  // d blocks of O; dimensions per lane half
+  static constexpr int PROW = D + 4;             // floats per row of a partial O (padded)
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void fwd32_split_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
+                                                          const float* __restrict__ vg, float* __restrict__ og,
+                                                          float* __restrict__ lseg, int N, int n_qblk, int G,
+                                                          float qk_scale, float qsign) {
+  using C = Fwd32Split<D>;
+  constexpr int DB = C::DB, HD = C::HD;
+  __shared__ __attribute__((aligned(16))) float part[C::NW][32 * C::PROW];
+  __shared__ float mrg_m[C::NW][32], mrg_l[C::NW][32];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  // the blocks of one head go to one XCD, where they share its K/V in L2
+  const int lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lb / n_qblk, qblk = lb % n_qblk;
+  const int q0 = qblk * C::BM, query = q0 + n;
+  const uint32_t head_bytes = (uint32_t)N * D * 4;
+  const rsrc_t qrs = make_rsrc(qg + (size_t)bh * N * D, head_bytes);
+  const size_t kvhead = (size_t)kv_head_of(bh, G) * (size_t)N * D;
+  const rsrc_t krs = make_rsrc(kg + kvhead, head_bytes);
+  const rsrc_t vrs = make_rsrc(vg + kvhead, head_bytes);
+
+  // The block's visible keys form ns sub-blocks, dealt to the eight waves.
+  // Only the last one can hold invisible keys (the causal diagonal, or the
+  // sequence end); keys before it are visible to every query of the block.
+  const int kend = CAUSAL ? min(q0 + C::BM, N) : N;
+  const int ns = (kend + 31) / 32;
+  const int u0 = wave * ns / C::NW, u1 = (wave + 1) * ns / C::NW;
+  const int key_lim = CAUSAL ? min(query + 1, N) : N;
+
+  // Q (B operand of S^T = K Q^T): lane half g holds elements g HD .. of its
+  // query's row, zeros past N; a negative scale flips its sign.
+  float qf[HD];
+#pragma unroll
+  for (int t = 0; t < HD / 4; ++t) {
+    const float4 x = load16f(qrs, ((uint32_t)query * D + g * HD + 4 * t) * 4);
+    qf[4 * t] = x.x * qsign; qf[4 * t + 1] = x.y * qsign; qf[4 * t + 2] = x.z * qsign; qf[4 * t + 3] = x.w * qsign;
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  for (int u = u0; u < u1; ++u) {
+    const int key0 = 32 * u;
+    f32x16 s1[1] = {f32x16{}};
+#pragma unroll
+    for (int t = 0; t < HD / 4; ++t) {
+      const float4 kx = load16f(krs, ((uint32_t)(key0 + n) * D + g * HD + 4 * t) * 4);
+      s1[0] = mma32(kx.x, qf[4 * t], s1[0]);
+      s1[0] = mma32(kx.y, qf[4 * t + 1], s1[0]);
+      s1[0] = mma32(kx.z, qf[4 * t + 2], s1[0]);
+      s1[0] = mma32(kx.w, qf[4 * t + 3], s1[0]);
+    }
+    const bool masked = u == ns - 1;
+    const float mt = masked ? tile_max<1, true>(s1, qk_scale, key0 + 4 * g, key_lim)
+                            : tile_max<1, false>(s1, qk_scale, 0, 0);
+    float alpha;
+    if (raise_max(mt, m_run, l_run, &alpha)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    l_run += masked ? tile_exp<1, true>(s1, qk_scale, m_use, key0 + 4 * g, key_lim)
+                    : tile_exp<1, false>(s1, qk_scale, m_use, 0, 0);
+    // O^T += V^T P^T: k-step r takes key key0 + 8 (r / 4) + 4 g + r % 4 on
+    // both operands (rows past N read as zeros and carry weight 0)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mma32(load4f(vrs, ((uint32_t)key * D + 32 * db + n) * 4), s1[0][r], oacc[db]);
+    }
+  }
+
+  // ---- merge the eight key ranges ------------------------------------------
+  // this wave's (m, l) and its un-normalised O, row-major [32][PROW]:
+  // register r of d block db is column 32 db + 8 (r / 4) + 4 g + r % 4 of row n
+  const float l_tot = halves_sum(l_run);
+  if (g == 0) {
+    mrg_m[wave][n] = m_run;
+    mrg_l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&part[wave][n * C::PROW + 32 * db + 8 * j + 4 * g]) =
+          make_float4(oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]);
+  __syncthreads();
+  // M = max_w m_w, L = sum_w l_w 2^(m_w - M), O = sum_w O_w 2^(m_w - M) / L;
+  // thread c forms row c / (D / 4), columns 4 (c % (D / 4)) .. + 3
+  const size_t head = (size_t)bh * N * D;
+  for (int c = threadIdx.x; c < 32 * D / 4; c += C::NT) {
+    const int row = c / (D / 4), col = 4 * (c % (D / 4));
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) M = fmaxf(M, mrg_m[w][row]);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) {
+      const float mw = mrg_m[w][row];
+      const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      L += wt * mrg_l[w][row];
+      const float4 x = *reinterpret_cast<const float4*>(&part[w][row * C::PROW + col]);
+      o.x += wt * x.x; o.y += wt * x.y; o.z += wt * x.z; o.w += wt * x.w;
+    }
+    if (q0 + row < N) {
+      const float inv = 1.f / L;
+      *reinterpret_cast<float4*>(og + head + (size_t)(q0 + row) * D + col) =
+          make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      if (col == 0) lseg[(size_t)bh * N + q0 + row] = (M + __log2f(L)) * kLn2;
+    }
+  }
+}
+
 // Tile per head dim: 8 waves x 32 queries (two waves per SIMD), 64 keys per
 // tile for d = 128 and 128 for d = 64 (16 KB of K and of V per tile either
 // way; five such buffers fill the LDS, so d = 128 has no larger tile).
@@ -1035,6 +1176,21 @@ hipError_t launch32(const FwdArgs& a) {
   const int n_qblk = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)n_qblk * a.BH;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (a.Nk == a.N && grid < cus) {
+    // fewer 128-query blocks than CUs: 32-query blocks, keys split inside
+    using S = Fwd32Split<D>;
+    const long long nb = (a.N + S::BM - 1) / S::BM;
+    if (nb * a.BH > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd32_split_kernel<D, CAUSAL>), dim3((unsigned)(nb * a.BH)), dim3(S::NT), 0, a.stream,
+                       static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                       static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.N, (int)nb, a.G,
+                       a.qk_scale, a.neg ? -1.f : 1.f);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fwd32_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
                      static_cast<float*>(a.o), a.lse, a.N, n_qblk, a.G, a.qk_scale, a.neg ? -1.f : 1.f);

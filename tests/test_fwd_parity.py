@@ -37,15 +37,16 @@ def test_small_shapes(N, causal, d, dtype):
     P.check_fwd_full(q, k, v, o, lse, scale, causal, dtype, f"N={N} d={d} causal={causal} {dtype}")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 17, 65, 129, 300, 513])
 def test_small_shapes_persistent_kernel(N, causal, d, dtype):
-    """Short sequences with enough heads (B2 H128) that the persistent
-    256-query kernel has at least one work item per CU and serves them
-    (with fewer heads the key-split kernel does): ragged tails, the masked
-    sub-block, several heads per workgroup; sampled whole heads."""
+    """Short sequences with enough heads (B2 H128) that the 256-query
+    persistent kernel (16-bit) or the 128-query fp32 kernel has at least one
+    work item per CU and serves them (with fewer heads the key-split kernels
+    do): ragged tails, the masked sub-block, several heads per workgroup;
+    sampled whole heads."""
     fa = _fa()
     q, k, v = fa_synth.make_inputs(2, 128, N, d, dtype, seed=7050 + N + d)
     scale = 1.0 / math.sqrt(d)
