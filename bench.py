@@ -279,6 +279,10 @@ def main():
     ap.add_argument("--tile-probe", action="store_true",
                     help="run only the kernels the tile sweep profiles: the training step and the d = 64 "
                          "forwards (non-causal fp16 B4 H8 N4096, causal bf16 B1 H16 N16384), --steps times each")
+    ap.add_argument("--sq-write", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="write profiles/sq_counters_<step>.md from the two SQ counter passes over the step")
+    ap.add_argument("--legs-stats", metavar="KERNEL_TRACE_CSV",
+                    help="write profiles/kernel_stats_bench_legs.md from a kernel trace of a full bench run")
     ap.add_argument("--tile-sweep-write", metavar="DIR",
                     help="write profiles/tile_sweep_*.md from DIR/<variant>/{sq,kt} rocprofv3 runs of --tile-probe")
     args = ap.parse_args()
@@ -293,6 +297,12 @@ def main():
         return
     if args.tile_sweep_write:
         write_tile_sweep(args.tile_sweep_write)
+        return
+    if args.sq_write:
+        write_sq(args.sq_write[0], args.sq_write[1])
+        return
+    if args.legs_stats:
+        write_legs_stats(args.legs_stats)
         return
     if args.lib:
         os.environ["IO_AWARE_FA_LIB"] = os.path.abspath(args.lib)
@@ -788,6 +798,128 @@ def read_stats(workload: str, digest: str):
     return {"kernel_us": us, "path": os.path.relpath(path, ROOT)}
 
 
+SQ_PASS1 = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+            "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE")
+SQ_PASS2 = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+            "SQ_ACTIVE_INST_ANY SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE")
+
+
+def _counters_by_kernel(counter_csv: str, skip_first: int = 1):
+    """{step kernel: {counter: mean per dispatch}} from a counter pass over
+    the training step (counters summed over their instances per dispatch;
+    the first `skip_first` dispatches of each kernel, the warm-up, left out)."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(counter_csv)):
+        per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for did in sorted(per):
+        key = next((v for k_, v in STEP_KERNELS.items() if k_ in names[did]), None)
+        if key is not None:
+            out[key].append(per[did])
+    res = {}
+    for key, lst in out.items():
+        lst = lst[skip_first:] or lst
+        res[key] = {c: sum(d.get(c, 0.0) for d in lst) / len(lst) for c in set().union(*lst)}
+    return res
+
+
+def write_sq(dir1: str, dir2: str):
+    """profiles/sq_counters_<training step>.md from the two SQ counter passes
+    (dir1 also holds a kernel trace of its run, for the clock)."""
+    import csv
+    import collections
+
+    import fa_synth
+    w = fa_synth.TRAIN_STEP
+    p1 = _counters_by_kernel(os.path.join(dir1, "run_counter_collection.csv"))
+    p2 = _counters_by_kernel(os.path.join(dir2, "run_counter_collection.csv"))
+    dur = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(dir1, "run_kernel_trace.csv"))):
+        key = next((v for k_, v in STEP_KERNELS.items() if k_ in r["Kernel_Name"]), None)
+        if key is not None:
+            dur[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    rows = []
+    for key in ("fa_fwd", "bwd_dkdv", "bwd_dq", "bwd_delta"):
+        a, b = p1.get(key), p2.get(key)
+        if not a or not b:
+            continue
+        ds = dur[key][1:] or dur[key]
+        t = sum(ds) / len(ds)
+        gui = a["GRBM_GUI_ACTIVE"] / 8  # summed over the 8 XCDs
+        clock = gui / t / 1e9
+        mf = b.get("SQ_INSTS_MFMA", 0.0)
+        wc = a["SQ_WAVE_CYCLES"]
+        per_mf = (lambda x: f"{x / mf:.2f}") if mf else (lambda x: "-")
+        busy = f"{100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * gui):.1f}%" if mf else "-"
+        conf = 100 * a["SQ_LDS_BANK_CONFLICT"] / a["SQ_LDS_IDX_ACTIVE"] if a["SQ_LDS_IDX_ACTIVE"] else 0.0
+        rows.append(f"| `{key}` | {t * 1e6:.1f} | {clock:.2f} | {mf / 1e6:.2f} | {per_mf(b['SQ_INSTS_VALU'])} | "
+                    f"{per_mf(b['SQ_INSTS_LDS'])} | {per_mf(b['SQ_INSTS_SALU'])} | {per_mf(b['SQ_INSTS_VMEM_RD'])} | "
+                    f"{100 * a['SQ_WAIT_ANY'] / wc:.1f}% | {100 * a['SQ_WAIT_INST_LDS'] / wc:.1f}% | {conf:.2f}% | "
+                    f"{busy} |")
+    path = os.path.join(PROFILES, f"sq_counters_{w.name}.md")
+    with open(path, "w") as f:
+        f.write(f"# SQ counters and shader clock of the training-step kernels ({w.describe()})\n\n")
+        f.write("Commands (repo root on the MI355X box, `TMPDIR=/tmp`), two passes of their own:\n\n```\n"
+                f"rocprofv3 --pmc {SQ_PASS1} --kernel-trace --output-format csv -d gpurun_out/sq1 -o run -- \\\n"
+                "    python3 bench.py --steps 2 --warmup 1 --legs 0 --cpu-baseline 0 --ceilings 0\n"
+                f"rocprofv3 --pmc {SQ_PASS2} --output-format csv -d gpurun_out/sq2 -o run -- \\\n"
+                "    python3 bench.py --steps 2 --warmup 1 --legs 0 --cpu-baseline 0 --ceilings 0\n"
+                "python3 bench.py --sq-write gpurun_out/sq1 gpurun_out/sq2\n```\n\n")
+        f.write("Per dispatch, averaged over each kernel's dispatches after its first (the warm-up).  Time: the "
+                "kernel trace of the first pass (counters slow it little).  Clock: GRBM_GUI_ACTIVE (GPU-busy "
+                "cycles, summed over the 8 XCDs) / 8 / time -- the shader clock the chip held under the kernel "
+                "(for a kernel of a few tens of microseconds, such as bwd_delta, the counter window runs past "
+                "the traced duration and the figure reads high).  "
+                "Instruction counts are wave instructions (one MFMA is one 32x32x16 product, 32768 flops); the "
+                "'per MFMA' columns divide by the MFMA count.  Waits are fractions of SQ_WAVE_CYCLES.  MFMA busy "
+                "= SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8): the fraction of SIMD cycles "
+                "the matrix cores were busy, at the clock held.\n\n")
+        f.write("| kernel | time (us) | clock (GHz) | MFMA (M) | VALU / MFMA | LDS / MFMA | SALU / MFMA | "
+                "VMEM rd / MFMA | wait, any | wait, LDS | LDS bank conflicts / LDS active | MFMA busy |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        f.write("\n".join(rows) + "\n\n")
+        f.write(f"```\nsource_digest = {source_digest()}\n```\n")
+    print(f"wrote {path}")
+
+
+def write_legs_stats(trace_csv: str):
+    """profiles/kernel_stats_bench_legs.md: every kernel of a full bench run
+    (step and legs), grouped by kernel and launch shape."""
+    import collections
+    import csv
+    import re
+
+    grp = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if "fa::" not in name:
+            continue
+        short = re.sub(r"\(.*$", "", name).replace("void ", "").replace("fa::(anonymous namespace)::", "")
+        short = short.replace("fa::", "")
+        key = (short, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])), int(r["Workgroup_Size_X"]))
+        grp[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    path = os.path.join(PROFILES, "kernel_stats_bench_legs.md")
+    with open(path, "w") as f:
+        f.write("# Kernel times of every bench leg (one MI355X)\n\nCommand (repo root on the MI355X box, "
+                "`TMPDIR=/tmp`):\n\n```\nrocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/klegs "
+                "-o run -- \\\n    python3 bench.py --steps 5 --warmup 2 --cpu-baseline 0\n"
+                "python3 bench.py --legs-stats gpurun_out/klegs/run_kernel_trace.csv\n```\n\n"
+                "Durations from the kernel trace (end - start per dispatch), grouped by kernel and launch shape "
+                "(workgroups x threads); warm-up calls included, so the median is the figure to read.  The "
+                "workloads behind each launch shape are the bench legs'.\n\n"
+                "| kernel | workgroups x threads | dispatches | median (us) | min (us) |\n|---|---|---|---|---|\n")
+        for (short, wgs, nt), d in sorted(grp.items()):
+            d.sort()
+            f.write(f"| `{short}` | {wgs} x {nt} | {len(d)} | {d[len(d) // 2]:.1f} | {d[0]:.1f} |\n")
+        f.write(f"\n```\nsource_digest = {source_digest()}\n```\n")
+    print(f"wrote {path}")
+
+
 # ---------------------------------------------------------------------------
 # HBM traffic of the fused forward against the naive three-kernel path, from
 # counters ("Flash Attention -- five lessons converging into 80 lines",
@@ -848,7 +980,8 @@ def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
         if not calib:
             sys.exit(f"{path}: no calibration copy")
         scale = calib_mib * 1024.0 / (sum(calib) / len(calib))
-        seq = [(n, v * scale * 1024.0) for _, n, v in ds if "fwd16_kernel" in n or "naive_" in n]
+        fused_k = ("fwd16_kernel", "fwd16_split_kernel")  # the persistent or the key-split forward
+        seq = [(n, v * scale * 1024.0) for _, n, v in ds if any(x in n for x in fused_k) or "naive_" in n]
         per_leg = 2 + 2 * 3
         legs = traffic_leg_workloads()
         if len(seq) != per_leg * len(legs):
@@ -856,13 +989,14 @@ def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
         for li, w in enumerate(legs):
             part = seq[li * per_leg:(li + 1) * per_leg]
             fused = [b for n, b in part[:2]]
-            assert all("fwd16_kernel" in n for n, _ in part[:2]), part[:2]
+            assert all(any(x in n for x in fused_k) for n, _ in part[:2]), part[:2]
             naive = part[2:]
             kinds = ("qk", "softmax", "pv")
             for j, (n, _) in enumerate(naive):
                 assert f"naive_{kinds[j % 3]}" in n, (n, kinds[j % 3])
             nb = {kd: sum(b for (n, b) in naive[j::3]) / 2 for j, kd in enumerate(kinds)}
             r = rows.setdefault(w.name, {"w": w, "scale": {}})
+            r["kernel"] = "key-split" if "fwd16_split_kernel" in part[0][0] else "persistent"
             r[counter] = {"fused": sum(fused) / 2, **nb}
             r["scale"][counter] = scale
     digest = digest_of(TRAFFIC_LEG_SOURCES)
@@ -882,9 +1016,10 @@ def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
                 f"{rows[traffic_leg_workloads()[0].name]['scale']['WRITE_SIZE']:.3f}), averaged over two calls. "
                 "Model bytes: fused = Q, K, V read and O written once (+ fp32 LSE); naive = that plus S and P "
                 "each written once and read once, 4 N^2 float16 elements per head.\n\n")
-        f.write("| workload | N | fused, counters (MB) | fused, model (MB) | naive QK^T (MB) | naive softmax (MB) "
-                "| naive PV (MB) | naive, counters (MB) | naive, model (MB) | ratio, counters | ratio, model |\n")
-        f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+        f.write("| workload | N | fused kernel | fused, counters (MB) | fused, model (MB) | naive QK^T (MB) | "
+                "naive softmax (MB) | naive PV (MB) | naive, counters (MB) | naive, model (MB) | ratio, counters | "
+                "ratio, model |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         machine = []
         for name, r in rows.items():
             w = r["w"]
@@ -893,7 +1028,7 @@ def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
             nt = sum(nk.values())
             fm = fused_fwd_bytes(w.B, w.H, w.N, w.d, 2)
             nm = naive_fwd_bytes(w.B, w.H, w.N, w.d, 2, 2)
-            f.write(f"| `{name}` | {w.N} | {fu / 1e6:.2f} | {fm / 1e6:.2f} | {nk['qk'] / 1e6:.1f} | "
+            f.write(f"| `{name}` | {w.N} | {r['kernel']} | {fu / 1e6:.2f} | {fm / 1e6:.2f} | {nk['qk'] / 1e6:.1f} | "
                     f"{nk['softmax'] / 1e6:.1f} | {nk['pv'] / 1e6:.1f} | {nt / 1e6:.1f} | {nm / 1e6:.1f} | "
                     f"{nt / fu:.1f} | {nm / fm:.1f} |\n")
             machine.append(f"{name}.fused_counter_bytes = {fu:.0f}")
