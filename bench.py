@@ -725,9 +725,17 @@ def measure_ceilings(torch, fa, dev):
     out["read_gbs"] = nbytes / (ms * 1e-3) / 1e9
     del src, dst, sink
     torch.cuda.empty_cache()
+    # vector issue cost of the softmax's instructions, one wave (shader-clock
+    # cycles per wave instruction; loop overhead included)
+    c = {m: min(fa.ceiling_valu(m, 20000) for _ in range(2)) for m in (0, 1, 2)}
+    fma = c[1] / 96
+    out["valu_issue_cycles"] = {"fma": fma, "exp": (c[0] - 32 * fma) / 32,
+                                "exp_fma_mix_per_iter": c[2], "serial_per_iter": c[0] + c[1],
+                                "full_overlap_per_iter": 128 * fma}
     out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     out["how"] = ("fa_ceiling_mfma: 256 workgroups x 8 waves x 4000 x 8 products; fa_ceiling_copy / "
-                  "fa_ceiling_read over 2 GiB; medians of HIP-event timings")
+                  "fa_ceiling_read over 2 GiB; medians of HIP-event timings; fa_ceiling_valu: one wave, "
+                  "20000 iterations of 32 exp + 32 mul / 96 fma / both")
     return out
 
 

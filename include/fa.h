@@ -366,6 +366,18 @@ int fa_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
 int fa_ceiling_read(const void* src, size_t bytes, void* sink, void* stream);
 size_t fa_ceiling_read_sink_bytes(void);
 
+/*
+ * fa_ceiling_valu: the issue cost of the softmax's two kinds of vector
+ * instruction, one wavefront on one SIMD, timed with the shader clock.  Per
+ * loop iteration mode 0 issues 32 v_exp_f32 (each after a v_mul_f32) on 8
+ * independent chains, mode 1 issues 96 v_fma_f32 on 24 independent chains,
+ * mode 2 issues both sets.  cycles: caller-owned uint64 [1] (8-byte
+ * aligned), the shader-clock cycles (s_memtime) of iters iterations.  sink:
+ * caller-owned float [64] (16-byte aligned).  FA_ERR_ARG for a bad mode,
+ * iters < 1 or a null pointer.
+ */
+int fa_ceiling_valu(int mode, float* sink, unsigned long long* cycles, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,7 @@ SIGNATURES = {
     "fa_ceiling_copy": (_i, [_vp, _vp, ctypes.c_size_t, _vp]),
     "fa_ceiling_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
     "fa_ceiling_read_sink_bytes": (ctypes.c_size_t, []),
+    "fa_ceiling_valu": (_i, [_i, _vp, _vp, _i, _vp]),
 }
 
 _lib = None

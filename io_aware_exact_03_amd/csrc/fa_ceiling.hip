@@ -88,6 +88,46 @@ __global__ __launch_bounds__(256) void ceiling_read_kernel(const uint4* __restri
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Vector issue cost, one wave on one SIMD, timed with the shader clock: per
+// loop iteration, MODE 0 issues 32 exponentials (v_exp_f32), each after a
+// v_mul_f32, on 8 independent chains; MODE 1 issues 96 v_fma_f32 on 24
+// independent chains; MODE 2 issues both sets, interleaved by the compiler.
+// The softmax of the attention kernels is made of these two kinds of
+// instruction; MODE 2 against MODE 0 + MODE 1 shows how far the
+// transcendental unit's work overlaps the FMAs of the same wave.
+template <int MODE>
+__global__ __launch_bounds__(64) void ceiling_valu_kernel(float* __restrict__ sink,
+                                                          unsigned long long* __restrict__ cycles, int iters,
+                                                          float a, float b) {
+  float e[8], f[24];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = 0.001f * (float)(threadIdx.x + i);
+#pragma unroll
+  for (int i = 0; i < 24; ++i) f[i] = 0.002f * (float)(threadIdx.x + i);
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (MODE != 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(e[i] * 0.5f);
+      }
+      if constexpr (MODE != 0) {
+#pragma unroll
+        for (int i = 0; i < 24; ++i) f[i] = __builtin_fmaf(f[i], a, b);
+      }
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += e[i];
+#pragma unroll
+  for (int i = 0; i < 24; ++i) s += f[i];
+  sink[threadIdx.x] = s;
+  if (threadIdx.x == 0) cycles[0] = t1 - t0;
+}
+
 }  // namespace fa
 
 namespace {
@@ -131,5 +171,15 @@ int fa_ceiling_read(const void* src, size_t bytes, void* sink, void* stream) {
 }
 
 size_t fa_ceiling_read_sink_bytes(void) { return (size_t)kStreamGrid * 256 * 4; }
+
+int fa_ceiling_valu(int mode, float* sink, unsigned long long* cycles, int iters, void* stream) {
+  if (!sink || !cycles || iters < 1 || mode < 0 || mode > 2) return FA_ERR_ARG;
+  if (!aligned16(sink) || ((uintptr_t)cycles & 7u)) return FA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == 0) hipLaunchKernelGGL(fa::ceiling_valu_kernel<0>, dim3(1), dim3(64), 0, st, sink, cycles, iters, 0.999f, 0.001f);
+  if (mode == 1) hipLaunchKernelGGL(fa::ceiling_valu_kernel<1>, dim3(1), dim3(64), 0, st, sink, cycles, iters, 0.999f, 0.001f);
+  if (mode == 2) hipLaunchKernelGGL(fa::ceiling_valu_kernel<2>, dim3(1), dim3(64), 0, st, sink, cycles, iters, 0.999f, 0.001f);
+  return launch_status(hipGetLastError());
+}
 
 }  // extern "C"

@@ -423,6 +423,16 @@ def ceiling_copy(src, dst):
     _lib.check(_lib.load().fa_ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src)), "fa_ceiling_copy")
 
 
+def ceiling_valu(mode: int, iters: int, device="cuda") -> float:
+    """Shader-clock cycles per loop iteration of the vector-issue loop (mode
+    0: 32 exp + 32 mul, 1: 96 fma, 2: both; one wavefront).  Synchronises."""
+    sink = torch.empty(64, dtype=torch.float32, device=device)
+    cyc = torch.zeros(1, dtype=torch.int64, device=device)
+    _lib.check(_lib.load().fa_ceiling_valu(int(mode), sink.data_ptr(), cyc.data_ptr(), int(iters), _stream(sink)),
+               "fa_ceiling_valu")
+    return cyc.item() / iters
+
+
 def ceiling_read(src, sink=None):
     """Read every byte of src once (streaming-read kernel); returns the sink."""
     nbytes = src.numel() * src.element_size()

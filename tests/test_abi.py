@@ -203,6 +203,22 @@ def test_naive_rejects(lib):
     assert call(args, d=80) == FA_ERR_UNSUPPORTED
 
 
+def test_ceilings_reject(lib):
+    """The chip-ceiling entry points check their arguments on the host
+    before any launch (no GPU call is made by a rejected call)."""
+    assert lib.fa_ceiling_mfma(None, None, 1, 8, 1, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_mfma(A, None, 1, 6, 1, None) == FA_ERR_ARG  # waves must be 4 or 8
+    assert lib.fa_ceiling_mfma(A + 4, None, 1, 8, 1, None) == FA_ERR_ALIGN
+    assert lib.fa_ceiling_copy(A, A, 100, None) == FA_ERR_ARG  # not a multiple of 16
+    assert lib.fa_ceiling_copy(A + 8, A, 64, None) == FA_ERR_ALIGN
+    assert lib.fa_ceiling_read(None, 64, A, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_valu(3, A, A, 10, None) == FA_ERR_ARG  # modes 0-2
+    assert lib.fa_ceiling_valu(0, A, A, 0, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_valu(0, None, A, 10, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_valu(1, A + 4, A, 10, None) == FA_ERR_ALIGN
+    assert lib.fa_ceiling_valu(2, A, A + 4, 10, None) == FA_ERR_ALIGN
+
+
 def test_workspace_bytes(lib):
     assert lib.fa_naive_workspace_bytes(4, 8, 4096, 1) == 4 * 8 * 4096 * 4096 * 2
     assert lib.fa_naive_workspace_bytes(1, 16, 16384, 2) == 16 * 16384 * 16384 * 2  # fp16 S for bf16 inputs
