@@ -60,7 +60,7 @@ struct Fp8 {
   static constexpr int RPP = 1024 / D;     // rows per 1 KB wave load
   static constexpr int PPT = BN / RPP;     // 1 KB pieces per K (or V) tile
   static constexpr int LPW = 2 * PPT / NW; // loads per wave per tile
-  static_assert(LPW >= 1 && LPW * NW == 2 * PPT && (NBUF - 2) * LPW < 64, "tile loads");
+  static_assert(LPW >= 1 && LPW * NW == 2 * PPT && PPT % LPW == 0 && 3 * LPW < 64, "tile loads");
 };
 
 // Stored 16-byte chunk of logical chunk c in row r.  D = 128: the two low
@@ -128,19 +128,22 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
     const int j_end = CAUSAL ? min(n_tiles, last_row / BN + 1) : n_tiles;
     const int key_lim = CAUSAL ? min(query + 1, N) : N;
 
-    // Tile j into ring slot sl: LDS row r, stored chunk c holds global chunk
-    // c ^ fp8_swz(r) of key j BN + r.  Rows past N read as zeros.
-    auto issue = [&](int j, uint8_t* __restrict__ kd, uint8_t* __restrict__ vd) __attribute__((always_inline)) {
+    // Waves 0 .. NW/2 - 1 load K tiles, the others V tiles: K tile jk into
+    // slot kd, V tile jv into slot vd, each only if that tile exists.  LDS row
+    // r, stored chunk c holds global chunk c ^ fp8_swz(r) of key j BN + r;
+    // rows past N read as zeros.
+    auto issue = [&](int jk, uint8_t* __restrict__ kd, int jv, uint8_t* __restrict__ vd) __attribute__((always_inline)) {
       const int lrow = lane / C::CPR;
+      const bool k_wave = wave * C::LPW < C::PPT;
+      if (!(k_wave ? jk < j_end : jv >= 0 && jv < j_end)) return;
 #pragma unroll
       for (int e = 0; e < C::LPW; ++e) {
         const int t = wave * C::LPW + e;
         const int p = t % C::PPT;
         const int row = p * C::RPP + lrow;
         const int ch = (lane % C::CPR) ^ fp8_swz<D>(row);
-        const uint32_t off = (uint32_t)(j * BN + row) * D + 16 * ch;
-        if (t < C::PPT) load_lds16(krs, kd + p * C::RPP * D, off);
-        else load_lds16(vrs, vd + p * C::RPP * D, off);
+        if (k_wave) load_lds16(krs, kd + p * C::RPP * D, (uint32_t)(jk * BN + row) * D + 16 * ch);
+        else load_lds16(vrs, vd + p * C::RPP * D, (uint32_t)(jv * BN + row) * D + 16 * ch);
       }
     };
 
@@ -186,137 +189,213 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(const uint8_t* __restrict_
       }
     };
 
-    // Softmax step of tile j with a lazy reference.  The weights are
+    // Softmax of tile j with a lazy reference.  The weights are
     // P 2^8 = exp2(x qk_scale - (m - 8)) against a reference m that is only
     // raised when some weight would leave E4M3's range (> 448): the common
-    // path computes no row max and never rescales.  An overflow shows as a
-    // NaN code (E4M3 has no infinity; the conversion does not saturate) and
-    // is tested on the packed bytes.  Then (rare; always on a row's first
-    // tile, where m is -inf) m is raised to the tile's row max plus
-    // kFp8Lift, O and l are rescaled and the weights redone.  The lift keeps
-    // later, slightly larger scores in range.  qk_scale >= 0, so the max of
-    // the raw scores gives the max.  MASK: keys past a lane's limit get
-    // weight zero (set directly; an infinite score times a zero qk_scale
-    // would be NaN).
-    auto softmax = [&](f32x16 (&sc)[2], int j, auto mask_tag) __attribute__((always_inline)) {
+    // path computes no row max and never rescales.  The fp32 sum of a word's
+    // four weights is at least each of them (rounded sums of non-negative
+    // terms never fall below a term), so while every such sum is at most 448
+    // no weight overflows and nothing more is tested.  Otherwise the packed
+    // bytes are tested: an overflow shows as a NaN code (E4M3 has no
+    // infinity; the conversion does not saturate).  Then (rare; always on a
+    // row's first tile, where m is -inf and the sums are infinite) m is
+    // raised to the tile's row max plus kFp8Lift, O and l are rescaled and
+    // the weights redone.  The lift keeps later, slightly larger scores in
+    // range.  qk_scale >= 0, so the max of the raw scores gives the max.
+    // MASK: keys past a lane's limit get weight zero (set directly; an
+    // infinite score times a zero qk_scale would be NaN).
+    // Word w of the packed weights: keys 32 (w / 4) + 8 (w % 4) + 4 g + i.
+    auto weight_word = [&](const f32x16 (&sc)[2], int j, auto mask_tag, v8i& pk, float& psum, float& qmax, float base,
+                           int w)
+        __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      auto visible = [&](int b, int r) { return !MASK || j * BN + 32 * b + 8 * (r / 4) + 4 * g + (r % 4) < key_lim; };
-      v8i pk;
-      float psum = 0.f;
-      uint32_t ovf = 0;
-      auto weights = [&]() __attribute__((always_inline)) {
-        const float base = m_run - 8.f;  // -inf before the first raise: every weight overflows
-        psum = 0.f;
-        ovf = 0;
+      const int b = w / 4, r = 4 * (w % 4);
+      float p[4];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int b = w / 4, r = 4 * (w % 4);
-          float p[4];
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(__builtin_fmaf(sc[b][r + i], qk_scale, -base));
+        if (MASK && j * BN + 32 * b + 8 * (r / 4) + 4 * g + i >= key_lim) p[i] = 0.f;
+      }
+      const float s4 = (p[0] + p[1]) + (p[2] + p[3]);
+      psum = w == 0 ? s4 : psum + s4;
+      qmax = w == 0 ? s4 : fmaxf(qmax, s4);
+      // the two conversions fill the low and the high half of the word,
+      // overwriting the codes it held before in place
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pk[w], false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+      pk[w] = word;
+    };
+    auto weights = [&](const f32x16 (&sc)[2], int j, auto mask_tag, v8i& pk, float& psum, float& qmax)
+        __attribute__((always_inline)) {
+      const float base = m_run - 8.f;  // -inf before the first raise: every weight overflows
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(__builtin_fmaf(sc[b][r + i], qk_scale, -base));
-            if (MASK && !visible(b, r + i)) p[i] = 0.f;
-          }
-          psum += (p[0] + p[1]) + (p[2] + p[3]);
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-          pk[w] = word;
-          // a byte whose low seven bits are all set is a NaN code
-          ovf |= (((uint32_t)word & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+      for (int w = 0; w < 8; ++w) weight_word(sc, j, mask_tag, pk, psum, qmax, base, w);
+    };
+    // The overflow test and the rare raise; then the tile's sum joins l.
+    auto settle = [&](const f32x16 (&sc)[2], int j, auto mask_tag, v8i& pk, float& psum, float& qmax)
+        __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // !(<=) also takes an infinite or NaN group sum to the byte test
+      if (__builtin_amdgcn_ballot_w64(!(qmax <= 448.f)) != 0) {
+        uint32_t ovf = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w)  // a byte whose low seven bits are all set is a NaN code
+          ovf |= (((uint32_t)pk[w] & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+        if (__builtin_amdgcn_ballot_w64(ovf != 0) != 0) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool vis = !MASK || j * BN + 32 * b + 8 * (r / 4) + 4 * g + (r % 4) < key_lim;
+              mx = fmaxf(mx, vis ? sc[b][r] : kNegInf);
+            }
+          mx = halves_max(mx);
+          mx = mx == kNegInf ? kNegInf : mx * qk_scale;
+          const float m_new = fmaxf(m_run, mx == kNegInf ? kNegInf : mx + kFp8Lift);
+          const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          m_run = m_new;
+          weights(sc, j, mask_tag, pk, psum, qmax);
         }
-      };
-      weights();
-      if (__builtin_amdgcn_ballot_w64(ovf != 0) != 0) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, visible(b, r) ? sc[b][r] : kNegInf);
-        mx = halves_max(mx);
-        mx = mx == kNegInf ? kNegInf : mx * qk_scale;
-        const float m_new = fmaxf(m_run, mx == kNegInf ? kNegInf : mx + kFp8Lift);
-        const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-        weights();
       }
       l_run += psum;
-      return pk;
     };
 
     // Ring and pipeline.  Iteration j computes the scores of tile j + 1, the
-    // softmax of tile j (already scored) and tile j's PV product, so the
-    // score products overlap the vector work.  Its barrier makes tile j + 1
-    // visible (tile j + 2 may still load) and frees the slot of tile j - 1,
-    // which receives tile j + 3.
-    static_assert(C::NBUF == 4, "ring of four tiles, loads three ahead of the scores");
-#pragma unroll
-    for (int j = 0; j < C::NBUF - 1; ++j)
-      if (j < j_end) issue(j, k_lds[j], v_lds[j]);
-    // prologue: tile 0 in LDS, its scores
+    // weights of tile j (already scored) and the PV product of tile j - 1
+    // (weighted in iteration j - 1).  Neither product depends on the vector
+    // work beside it, so the eight matrix instructions are spread through the
+    // weights and one wave keeps both units busy.  Loads run ahead: K tile
+    // j + 3 and V tile j + 2 go out in iteration j, into the slots that K
+    // tile j - 1 (scored in iteration j - 2) and V tile j - 2 (read in
+    // iteration j - 1) have left.  The barrier at the top of iteration j
+    // makes K tile j + 1 and V tile j - 1 visible; the loads still allowed in
+    // flight are each wave's latest.
+    static_assert(C::NBUF == 4, "ring of four K and four V slots");
+    issue(0, k_lds[0], -1, v_lds[3]);
+    issue(1, k_lds[1], 0, v_lds[0]);
+    issue(2, k_lds[2], 1, v_lds[1]);
+    // prologue: K tile 0 in LDS (K waves issued up to three tiles), its scores
     if (j_end > 2) lds_barrier<2 * C::LPW>();
     else if (j_end > 1) lds_barrier<C::LPW>();
     else lds_barrier<0>();
     f32x16 sA[2], sB[2];
     s_gemm(k_lds[0], sA);
-    // One iteration; the loop runs two per trip so the score registers
-    // alternate without copies.
-    // The ring slots arrive as distinct __restrict__ pointers: with that, the
-    // compiler does not make the reads of one slot wait for the loads just
-    // issued into another.
-    auto step_in = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint8_t* __restrict__ kn,
-                       const uint8_t* __restrict__ vt, uint8_t* __restrict__ kl, uint8_t* __restrict__ vl,
-                       auto mask_tag) __attribute__((always_inline)) {
-      // tile j + 1 must be in LDS: the loads still allowed in flight are
-      // those of tile j + 2
+    v8i pkA = v8i{}, pkB = v8i{};  // E4M3 weights of alternate tiles
+    // One iteration; the loop runs two per trip so the score and weight
+    // registers alternate without copies.  The ring slots arrive as distinct
+    // __restrict__ pointers: with that, the compiler does not make the reads
+    // of one slot wait for the loads just issued into another.
+    auto step_in = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const v8i& prv, v8i& pk,
+                       const uint8_t* __restrict__ kn, const uint8_t* __restrict__ vt,
+                       uint8_t* __restrict__ kl, uint8_t* __restrict__ vl, auto mask_tag, auto pv_tag)
+        __attribute__((always_inline)) {
+      constexpr bool PV = decltype(pv_tag)::value;
       if (j + 1 < j_end) {
         if (j + 2 < j_end) lds_barrier<C::LPW>();
         else lds_barrier<0>();
       }
-      if (j + 3 < j_end) issue(j + 3, kl, vl);
-      // Every wave runs every tile of the block: a tile wholly past a
-      // wave's causal limit is fully masked (P = 0), which costs less than
-      // branching around the accumulators.
-      if (j + 1 < j_end) s_gemm(kn, nxt);
-      // V^T fragments: the first PF are read before the vector work, which
-      // hides their latency (all of them would not fit in registers at
-      // d = 128), the rest behind the first PV products.
-      constexpr int PF = DB > 2 ? 2 : DB;
-      v8i vf[DB];
+      issue(j + 3, kl, j + 2, vl);
+      // The step's matrix instructions: the PV products of tile j - 1 (d
+      // blocks 0 .. DB - 1), then the score products of tile j + 1, ordered so
+      // the two k-steps of a key block are not adjacent.  Past the last tile
+      // the scores are of stale slot contents and unused.  Each takes its A
+      // operand from LDS, read LA instructions ahead.
+      constexpr int NPV = PV ? DB : 0, NMM = NPV + 2 * DS, LA = 2;
+      auto read_a = [&](int i) __attribute__((always_inline)) {
+        if (i < NPV) return vfrag(vt, i);
+        const int b = (i - NPV) % 2, st = (i - NPV) / 2;
+        const int row = 32 * b + n;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kn + fp8_off<D>(row, 4 * st + 2 * g));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(kn + fp8_off<D>(row, 4 * st + 2 * g + 1));
+        return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      auto mma = [&](int i, const v8i& a) __attribute__((always_inline)) {
+        if (i < NPV) {
+          oacc[i] = mma_fp8(a, prv, oacc[i]);
+        } else {
+          const int b = (i - NPV) % 2, st = (i - NPV) / 2;
+          nxt[b] = mma_fp8(a, qf[st], st == 0 ? f32x16{} : nxt[b]);
+        }
+      };
+      // Weight word w runs before matrix instructions i with i * 8 / NMM == w;
+      // scheduling barriers keep that order, so one wave issues vector work
+      // while its own matrix instructions execute.
+      v8i ops[NMM];
 #pragma unroll
-      for (int db = 0; db < PF; ++db) vf[db] = vfrag(vt, db);
-      const v8i pk = softmax(cur, j, mask_tag);
+      for (int i = 0; i < LA && i < NMM; ++i) ops[i] = read_a(i);
+      float psum, qmax;
+      const float base = m_run - 8.f;  // -inf before the first raise: every weight overflows
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = PF; db < DB; ++db) vf[db] = vfrag(vt, db);
+      for (int w = 0; w < 8; ++w) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mma_fp8(vf[db], pk, oacc[db]);
+        for (int i = 0; i < NMM; ++i)
+          if (i * 8 / NMM == w && i + LA < NMM) ops[i + LA] = read_a(i + LA);
+        weight_word(cur, j, mask_tag, pk, psum, qmax, base, w);
+        int mm = 0;
+#pragma unroll
+        for (int i = 0; i < NMM; ++i)
+          if (i * 8 / NMM == w) {
+            mma(i, ops[i]);
+            ++mm;
+          }
+        // within the chunk: its LDS reads, then the vector work, then the
+        // matrix instruction
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 32, 0);
+        if (mm) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // at most one per chunk (NMM <= 8)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      settle(cur, j, mask_tag, pk, psum, qmax);
     };
-    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto mask_tag) __attribute__((always_inline)) {
-      step_in(j, cur, nxt, k_lds[(j + 1) % C::NBUF], v_lds[j % C::NBUF], k_lds[(j + 3) % C::NBUF],
-              v_lds[(j + 3) % C::NBUF], mask_tag);
+    // The first iteration has no PV product before it.
+    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const v8i& prv, v8i& pk, auto mask_tag, auto pv_tag)
+        __attribute__((always_inline)) {
+      step_in(j, cur, nxt, prv, pk, k_lds[(j + 1) % C::NBUF], v_lds[(j + 3) % C::NBUF], k_lds[(j + 3) % C::NBUF],
+              v_lds[(j + 2) % C::NBUF], mask_tag, pv_tag);
     };
     // Tiles every key of which every query of the block sees run without
     // the mask; the rest (the diagonal tiles, the sequence tail) with it.
     // Each range has one code path, so the accumulators need no merging.
+    // Between iterations the scores of the next tile are in sA and the
+    // weights of the previous one in pkB.
     auto run = [&](int j0, int j1, auto mask_tag) __attribute__((always_inline)) {
       int j = j0;
-      for (; j + 1 < j1; j += 2) {
-        step(j, sA, sB, mask_tag);
-        step(j + 1, sB, sA, mask_tag);
-      }
-      if (j < j1) {
-        step(j, sA, sB, mask_tag);
+      if (j == 0 && j < j1) {
+        step(0, sA, sB, pkB, pkA, mask_tag, std::false_type{});
         sA[0] = sB[0];
         sA[1] = sB[1];
+        pkB = pkA;
+        j = 1;
+      }
+      for (; j + 1 < j1; j += 2) {
+        step(j, sA, sB, pkB, pkA, mask_tag, std::true_type{});
+        step(j + 1, sB, sA, pkA, pkB, mask_tag, std::true_type{});
+      }
+      if (j < j1) {
+        step(j, sA, sB, pkB, pkA, mask_tag, std::true_type{});
+        sA[0] = sB[0];
+        sA[1] = sB[1];
+        pkB = pkA;
       }
     };
     const int j_full = min(j_end, CAUSAL ? q0 / BN : N / BN);
     run(0, j_full, std::false_type{});
     run(j_full, j_end, std::true_type{});
+    // The last tile's PV product.  Its V tile is in LDS and visible: the
+    // barrier of the second-to-last iteration waited for every load (the
+    // prologue's, with a single tile).
+    {
+      const uint8_t* vt = v_lds[(j_end - 1) % C::NBUF];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mma_fp8(vfrag(vt, db), pkB, oacc[db]);
+    }
     // No tile load is in flight (none is issued for the last three tiles, and
     // the last barrier waited for all); saying so spares the O staging below
     // a wait for loads the compiler would otherwise take as pending.
