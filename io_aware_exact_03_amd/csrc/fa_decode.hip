@@ -429,11 +429,12 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
 }
 
 // Merge of the pieces of one (unit, live query column) that was cut between
-// parts: the 256 threads are 8 piece groups x 32 element chunks; each group
-// folds every 8th piece, and the groups are combined through LDS once for
-// the max and once for the sums.  With uniform lengths (kv_lens null) the
-// unit's first tile has a closed form; otherwise block sums over the batch
-// lengths locate it.
+// parts: the 256 threads are 8 piece groups x 32 element chunks.  Each group
+// folds every 8th piece with the same decomposition (a running max and
+// rescaled sums), loading four pieces' LSEs and output chunks at once so
+// that one memory latency covers them; the 8 groups are then combined
+// through LDS.  With uniform lengths (kv_lens null) the unit's first tile
+// has a closed form; otherwise block sums over the batch lengths locate it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ lpart,
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
                                                            uint16_t* __restrict__ og, float* __restrict__ lseg,
                                                            int B, int H, int G, int Nkv, int n_parts) {
   constexpr int CH = D / 32;  // floats per element chunk
+  constexpr int U = 4;        // pieces per group in flight
   __shared__ float red[8][D];
   __shared__ float rs[2][8];
   __shared__ int sums[512];
@@ -465,27 +467,59 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   const size_t slot0 = (size_t)w_first + u;
 
   const int tid = threadIdx.x, c = tid % 32, grp = tid / 32;
-  // M = max over the pieces' LSEs
-  float m = kNegInf;
-  for (int i = grp; i < np; i += 8) m = fmaxf(m, lpart[(slot0 + i) * 32 + col]);
+  // this group's running max (natural log units), weight sum and sums
+  float m = kNegInf, wsum = 0.f;
+  float acc[CH] = {};
+  for (int i0 = grp; i0 < np; i0 += 8 * U) {
+    float li[U];
+    float oi[U][CH];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int i = i0 + 8 * q;
+      li[q] = kNegInf;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) oi[q][e] = 0.f;
+      if (i < np) {
+        li[q] = lpart[(slot0 + i) * 32 + col];
+        // CH consecutive floats, 4 CH bytes aligned (the workspace is)
+        const float* src = opart + ((slot0 + i) * 32 + col) * D + CH * c;
+        if constexpr (CH == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src);
+          oi[q][0] = x.x; oi[q][1] = x.y; oi[q][2] = x.z; oi[q][3] = x.w;
+        } else {
+          static_assert(CH == 2, "d = 64 or 128");
+          const float2 x = *reinterpret_cast<const float2*>(src);
+          oi[q][0] = x.x; oi[q][1] = x.y;
+        }
+      }
+    }
+    float mb = m;
+#pragma unroll
+    for (int q = 0; q < U; ++q) mb = fmaxf(mb, li[q]);
+    if (mb == kNegInf) continue;  // nothing live yet (every LSE of a cut piece is finite)
+    const float r = fast_exp2((m - mb) * kLog2e);  // m = -inf gives 0
+    wsum *= r;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] *= r;
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const float wi = fast_exp2((li[q] - mb) * kLog2e);  // absent pieces: exp(-inf) = 0
+      wsum += wi;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[e] += wi * oi[q][e];
+    }
+    m = mb;
+  }
+  // combine the groups: M = max m_g, each group's sums scaled by exp(m_g - M)
   if (c == 0) rs[0][grp] = m;
   __syncthreads();
   float M = kNegInf;
 #pragma unroll
   for (int q = 0; q < 8; ++q) M = fmaxf(M, rs[0][q]);
-  // weighted sums, w_i = exp(LSE_i - M)
-  float acc[CH] = {};
-  float wsum = 0.f;
-  for (int i = grp; i < np; i += 8) {
-    const float wi = fast_exp2((lpart[(slot0 + i) * 32 + col] - M) * kLog2e);
-    wsum += wi;
-    const float* src = opart + ((slot0 + i) * 32 + col) * D + CH * c;
+  const float sg = m == kNegInf ? 0.f : fast_exp2((m - M) * kLog2e);
 #pragma unroll
-    for (int e = 0; e < CH; ++e) acc[e] += wi * src[e];
-  }
-#pragma unroll
-  for (int e = 0; e < CH; ++e) red[grp][CH * c + e] = acc[e];
-  if (c == 0) rs[1][grp] = wsum;
+  for (int e = 0; e < CH; ++e) red[grp][CH * c + e] = acc[e] * sg;
+  if (c == 0) rs[1][grp] = wsum * sg;
   __syncthreads();
   if (grp == 0) {
     float W = 0.f;
