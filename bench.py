@@ -732,10 +732,21 @@ def measure_ceilings(torch, fa, dev):
     out["valu_issue_cycles"] = {"fma": fma, "exp": (c[0] - 32 * fma) / 32,
                                 "exp_fma_mix_per_iter": c[2], "serial_per_iter": c[0] + c[1],
                                 "full_overlap_per_iter": 128 * fma}
+    # the 16-bit forward's step mix without HBM traffic: operands in
+    # registers, read from LDS, and LDS plus the per-tile barrier
+    mix = {}
+    for mode, name in ((0, "registers"), (1, "lds_operands"), (2, "lds_operands_barrier")):
+        fa.ceiling_mix(mode, wgs, 1000)
+        ms, _ = time_reps(lambda: fa.ceiling_mix(mode, wgs, 1000), 5, torch)
+        tf = fa.ceiling_mix_flops(wgs, 1000) / (ms * 1e-3) / 1e12
+        mix[name] = {"tflops": tf, "frac_of_mfma_ceiling": tf / out["mfma_bf16_tflops"],
+                     "frac_of_spec": tf / PEAK_BF16_TFLOPS}
+    out["fwd_step_mix"] = mix
     out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     out["how"] = ("fa_ceiling_mfma: 256 workgroups x 8 waves x 4000 x 8 products; fa_ceiling_copy / "
                   "fa_ceiling_read over 2 GiB; medians of HIP-event timings; fa_ceiling_valu: one wave, "
-                  "20000 iterations of 32 exp + 32 mul / 96 fma / both")
+                  "20000 iterations of 32 exp + 32 mul / 96 fma / both; fa_ceiling_mix: 256 workgroups x 8 "
+                  "waves x 2000 forward steps of 16 products and 16 weights")
     return out
 
 
@@ -907,8 +918,9 @@ def write_legs_stats(trace_csv: str):
         name = r["Kernel_Name"]
         if "fa::" not in name:
             continue
-        short = re.sub(r"\(.*$", "", name).replace("void ", "").replace("fa::(anonymous namespace)::", "")
-        short = short.replace("fa::", "")
+        # the anonymous namespace goes before the argument list is cut at its "("
+        short = name.replace("(anonymous namespace)::", "")
+        short = re.sub(r"\(.*$", "", short).replace("void ", "").replace("fa::", "")
         key = (short, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])), int(r["Workgroup_Size_X"]))
         grp[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     path = os.path.join(PROFILES, "kernel_stats_bench_legs.md")

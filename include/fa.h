@@ -378,6 +378,23 @@ size_t fa_ceiling_read_sink_bytes(void);
  */
 int fa_ceiling_valu(int mode, float* sink, unsigned long long* cycles, int iters, void* stream);
 
+/*
+ * fa_ceiling_mix: the 16-bit forward's inner step without HBM traffic, to
+ * show what its mix of instructions sustains on the matrix cores.
+ * workgroups x 512 threads (eight waves, two per SIMD, as the forward); per
+ * wave iters x 2 steps of 8 slots, a slot being one 32x32x16 bf16 score
+ * product (a dependent chain), the weights of two keys (fma, exp2, bf16
+ * pack, add) and one 32x32x16 PV product (four accumulators).  Mode 0:
+ * operands from registers; mode 1: each slot's A operands read from LDS as
+ * the forward reads them (a 16-byte row read, two transposing 8-byte
+ * reads), three slots ahead; mode 2: mode 1 plus a workgroup barrier every
+ * two steps.  One launch performs workgroups * 8 * iters * 32 * 32768
+ * matrix flops.  sink: caller-owned float [workgroups * 512] (16-byte
+ * aligned), written so no product is dead.  FA_ERR_ARG for a bad mode,
+ * workgroups or iters < 1, or a null sink.
+ */
+int fa_ceiling_mix(int mode, float* sink, int workgroups, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,6 +128,92 @@ __global__ __launch_bounds__(64) void ceiling_valu_kernel(float* __restrict__ si
   if (threadIdx.x == 0) cycles[0] = t1 - t0;
 }
 
+// The 16-bit forward's inner step without HBM traffic: what its mix of
+// instructions sustains on the matrix cores.  Eight waves per workgroup (two
+// per SIMD), each running 32-key steps of 8 slots; a slot issues one product
+// of the score chain S^T = K Q^T (32x32x16, accumulating), the weights of
+// two keys (fma, exp2, bf16 pack, row-sum add) and one PV product into one
+// of four accumulators, as the forward's slots do.  MODE 0: operands from
+// registers.  MODE 1: each slot's A operands come from LDS as in the forward
+// (one 16-byte row read for the score product, two 8-byte transposing reads
+// for the PV product), read three slots ahead.  MODE 2: MODE 1 plus a
+// workgroup barrier every two steps (the forward's one per 64-key tile).
+// Operands are built from the lane index, every result feeds the sink.
+template <int MODE>
+__global__ __launch_bounds__(512) void ceiling_mix_kernel(float* __restrict__ sink, int iters, float a, float b) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[16384];  // 16 KB row-read area, 16 KB transposing-read area
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) lds[i] = (uint16_t)(0x3C00 + (i & 255));
+  __syncthreads();
+  const uint32_t w0 = 0x3F803F80u ^ ((uint32_t)lane << 3);
+  const uint4 ka = make_uint4(w0, w0 ^ 0x10001u, w0 ^ 0x20002u, w0 ^ 0x30003u);
+  uint4 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = make_uint4(w0 ^ (s << 1), w0, w0 ^ 0x50005u, w0 ^ (0x60006u + s));
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  f32x16 sA, sB;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sA[i] = 0.001f * (float)(lane + i);
+    sB[i] = 0.f;
+  }
+  float lsum = 0.f;
+  auto row_read = [&](int slot) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(lds + ((slot & 7) * 1024 + lane * 16) / 2);
+  };
+  auto tr_read = [&](int slot) __attribute__((always_inline)) {
+    const uint16_t* p = lds + (16384 + (slot & 7) * 1024 + lane * 8) / 2;
+    const uint2 lo = read_tr_b64(p), hi = read_tr_b64(p + 256);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  uint4 ra[4], rb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = MODE >= 1 && i < 3 ? row_read(i) : ka;
+    rb[i] = MODE >= 1 && i < 3 ? tr_read(i) : ka;
+  }
+  // PV products take the previous step's packed weights, as in the forward
+  uint32_t pkA[8] = {}, pkB[8] = {};
+  auto step = [&](const f32x16& cur, f32x16& nxt, uint32_t (&pk)[8], const uint32_t (&pkp)[8])
+      __attribute__((always_inline)) {
+    const uint4 pp[2] = {make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]), make_uint4(pkp[4], pkp[5], pkp[6], pkp[7])};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (MODE >= 1) {
+        ra[(k + 3) % 4] = row_read(k + 3);
+        rb[(k + 3) % 4] = tr_read(k + 3);
+      }
+      nxt = mma16(BF16{}, ra[k % 4], qf[k], k == 0 ? f32x16{} : nxt);
+      const float p0 = fast_exp2(__builtin_fmaf(cur[2 * k], a, -b));
+      const float p1 = fast_exp2(__builtin_fmaf(cur[2 * k + 1], a, -b));
+      pk[k] = pack2(BF16{}, p0, p1);
+      lsum += p0 + p1;
+      oacc[k % 4] = mma16(BF16{}, rb[k % 4], pp[k / 4], oacc[k % 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int it = 0; it < iters; ++it) {
+    step(sA, sB, pkA, pkB);
+    step(sB, sA, pkB, pkA);
+    if constexpr (MODE == 2) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  float r = lsum;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r += __uint_as_float(pkA[i] & 0x3FFF3FFFu);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) r += oacc[i][k];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) r += sA[k] + sB[k];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
 }  // namespace fa
 
 namespace {
@@ -171,6 +257,21 @@ int fa_ceiling_read(const void* src, size_t bytes, void* sink, void* stream) {
 }
 
 size_t fa_ceiling_read_sink_bytes(void) { return (size_t)kStreamGrid * 256 * 4; }
+
+// Scores of the mix loop are sums of products near 1; this scale and shift
+// keep its weights exp2(score * scale - shift) well inside range.
+constexpr float kMixScale = 1.f / 1024, kMixShift = 4.f;
+
+int fa_ceiling_mix(int mode, float* sink, int workgroups, int iters, void* stream) {
+  if (!sink || workgroups < 1 || iters < 1 || mode < 0 || mode > 2) return FA_ERR_ARG;
+  if (!aligned16(sink)) return FA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)workgroups), blk(512);
+  if (mode == 0) hipLaunchKernelGGL(fa::ceiling_mix_kernel<0>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
+  if (mode == 1) hipLaunchKernelGGL(fa::ceiling_mix_kernel<1>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
+  if (mode == 2) hipLaunchKernelGGL(fa::ceiling_mix_kernel<2>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
+  return launch_status(hipGetLastError());
+}
 
 int fa_ceiling_valu(int mode, float* sink, unsigned long long* cycles, int iters, void* stream) {
   if (!sink || !cycles || iters < 1 || mode < 0 || mode > 2) return FA_ERR_ARG;

@@ -433,6 +433,21 @@ def ceiling_valu(mode: int, iters: int, device="cuda") -> float:
     return cyc.item() / iters
 
 
+def ceiling_mix(mode: int, workgroups: int, iters: int, device="cuda"):
+    """Launch the forward-step instruction-mix loop (mode 0: operands in
+    registers, 1: operands read from LDS, 2: plus a barrier every two steps);
+    returns the sink.  The launch performs ceiling_mix_flops(...) matrix
+    flops."""
+    sink = torch.empty(workgroups * 512, dtype=torch.float32, device=device)
+    _lib.check(_lib.load().fa_ceiling_mix(int(mode), sink.data_ptr(), int(workgroups), int(iters), _stream(sink)),
+               "fa_ceiling_mix")
+    return sink
+
+
+def ceiling_mix_flops(workgroups: int, iters: int) -> float:
+    return float(workgroups) * 8 * iters * 32 * 32768
+
+
 def ceiling_read(src, sink=None):
     """Read every byte of src once (streaming-read kernel); returns the sink."""
     nbytes = src.numel() * src.element_size()

@@ -58,3 +58,15 @@ def test_valu_loop_counts():
     # the mix issues both sets, so it takes at least as long as either
     assert exp_c > 64 and fma_c > 96
     assert mix_c >= 0.95 * max(exp_c, fma_c)
+
+
+def test_mix_loop_runs_and_is_finite():
+    """The forward-step mix loop in its three modes: finite sink values, and
+    the same values from two launches (no atomics, fixed order)."""
+    fa = _fa()
+    for mode in (0, 1, 2):
+        a = fa.ceiling_mix(mode, 4, 20).clone()
+        b = fa.ceiling_mix(mode, 4, 20)
+        torch.cuda.synchronize()
+        assert torch.isfinite(a).all(), mode
+        assert torch.equal(a, b), mode
