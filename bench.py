@@ -704,6 +704,13 @@ def write_traffic(fetch_csv: str, write_csv: str, calib_mib: int):
         print(f"wrote {path}: {byts / 1e6:.1f} MB per launch")
 
 
+def _clock_ghz(clk) -> float:
+    """Median over workgroups of shader-clock ticks / constant-clock (100 MHz)
+    ticks, in GHz."""
+    c = clk.view(-1, 2).cpu().double()
+    return float((c[:, 0] / c[:, 1] * 0.1).median())
+
+
 def measure_ceilings(torch, fa, dev):
     """What the chip sustains, measured with the library's own ceiling
     kernels: matrix cores alone (8 independent v_mfma_f32_32x32x16_bf16
@@ -714,6 +721,8 @@ def measure_ceilings(torch, fa, dev):
     fa.ceiling_mfma(wgs, waves, iters)
     ms, _ = time_reps(lambda: fa.ceiling_mfma(wgs, waves, iters), 5, torch)
     out["mfma_bf16_tflops"] = fa.ceiling_mfma_flops(wgs, waves, iters) / (ms * 1e-3) / 1e12
+    _, clk = fa.ceiling_mfma(wgs, waves, iters, clocks=True)
+    out["mfma_clock_ghz"] = _clock_ghz(clk)
     nbytes = 2 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -739,8 +748,9 @@ def measure_ceilings(torch, fa, dev):
         fa.ceiling_mix(mode, wgs, 1000)
         ms, _ = time_reps(lambda: fa.ceiling_mix(mode, wgs, 1000), 5, torch)
         tf = fa.ceiling_mix_flops(wgs, 1000) / (ms * 1e-3) / 1e12
+        _, clk = fa.ceiling_mix(mode, wgs, 1000, clocks=True)
         mix[name] = {"tflops": tf, "frac_of_mfma_ceiling": tf / out["mfma_bf16_tflops"],
-                     "frac_of_spec": tf / PEAK_BF16_TFLOPS}
+                     "frac_of_spec": tf / PEAK_BF16_TFLOPS, "clock_ghz": _clock_ghz(clk)}
     out["fwd_step_mix"] = mix
     out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     out["how"] = ("fa_ceiling_mfma: 256 workgroups x 8 waves x 4000 x 8 products; fa_ceiling_copy / "

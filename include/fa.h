@@ -390,10 +390,14 @@ int fa_ceiling_valu(int mode, float* sink, unsigned long long* cycles, int iters
  * reads), three slots ahead; mode 2: mode 1 plus a workgroup barrier every
  * two steps.  One launch performs workgroups * 8 * iters * 32 * 32768
  * matrix flops.  sink: caller-owned float [workgroups * 512] (16-byte
- * aligned), written so no product is dead.  FA_ERR_ARG for a bad mode,
- * workgroups or iters < 1, or a null sink.
+ * aligned), written so no product is dead.  clocks: null, or caller-owned
+ * uint64 [2 * workgroups] (16-byte aligned) that receives per workgroup the
+ * shader-clock (s_memtime) and 100 MHz constant-clock (s_memrealtime)
+ * ticks of its loop, whose ratio gives the clock the chip held.
+ * FA_ERR_ARG for a bad mode, workgroups or iters < 1, or a null sink.
  */
-int fa_ceiling_mix(int mode, float* sink, int workgroups, int iters, void* stream);
+int fa_ceiling_mix(int mode, float* sink, unsigned long long* clocks, int workgroups, int iters,
+                   void* stream);
 
 #ifdef __cplusplus
 }

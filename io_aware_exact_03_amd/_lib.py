@@ -43,7 +43,7 @@ SIGNATURES = {
     "fa_ceiling_read": (_i, [_vp, ctypes.c_size_t, _vp, _vp]),
     "fa_ceiling_read_sink_bytes": (ctypes.c_size_t, []),
     "fa_ceiling_valu": (_i, [_i, _vp, _vp, _i, _vp]),
-    "fa_ceiling_mix": (_i, [_i, _vp, _i, _i, _vp]),
+    "fa_ceiling_mix": (_i, [_i, _vp, _vp, _i, _i, _vp]),
 }
 
 _lib = None

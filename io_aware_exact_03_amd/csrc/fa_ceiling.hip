@@ -140,7 +140,9 @@ __global__ __launch_bounds__(64) void ceiling_valu_kernel(float* __restrict__ si
 // workgroup barrier every two steps (the forward's one per 64-key tile).
 // Operands are built from the lane index, every result feeds the sink.
 template <int MODE>
-__global__ __launch_bounds__(512) void ceiling_mix_kernel(float* __restrict__ sink, int iters, float a, float b) {
+__global__ __launch_bounds__(512) void ceiling_mix_kernel(float* __restrict__ sink,
+                                                         unsigned long long* __restrict__ clocks, int iters,
+                                                         float a, float b) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[16384];  // 16 KB row-read area, 16 KB transposing-read area
   const int lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < 16384; i += blockDim.x) lds[i] = (uint16_t)(0x3C00 + (i & 255));
@@ -194,6 +196,12 @@ __global__ __launch_bounds__(512) void ceiling_mix_kernel(float* __restrict__ si
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  const bool timer = threadIdx.x == 0;
+  unsigned long long t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   for (int it = 0; it < iters; ++it) {
     step(sA, sB, pkA, pkB);
     step(sB, sA, pkB, pkA);
@@ -212,6 +220,10 @@ __global__ __launch_bounds__(512) void ceiling_mix_kernel(float* __restrict__ si
 #pragma unroll
   for (int k = 0; k < 16; ++k) r += sA[k] + sB[k];
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+  if (timer && clocks != nullptr) {
+    clocks[2 * blockIdx.x] = __builtin_amdgcn_s_memtime() - t0;
+    clocks[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
 }
 
 }  // namespace fa
@@ -262,14 +274,14 @@ size_t fa_ceiling_read_sink_bytes(void) { return (size_t)kStreamGrid * 256 * 4; 
 // keep its weights exp2(score * scale - shift) well inside range.
 constexpr float kMixScale = 1.f / 1024, kMixShift = 4.f;
 
-int fa_ceiling_mix(int mode, float* sink, int workgroups, int iters, void* stream) {
+int fa_ceiling_mix(int mode, float* sink, unsigned long long* clocks, int workgroups, int iters, void* stream) {
   if (!sink || workgroups < 1 || iters < 1 || mode < 0 || mode > 2) return FA_ERR_ARG;
-  if (!aligned16(sink)) return FA_ERR_ALIGN;
+  if (!aligned16(sink) || (clocks != nullptr && !aligned16(clocks))) return FA_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 g((unsigned)workgroups), blk(512);
-  if (mode == 0) hipLaunchKernelGGL(fa::ceiling_mix_kernel<0>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
-  if (mode == 1) hipLaunchKernelGGL(fa::ceiling_mix_kernel<1>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
-  if (mode == 2) hipLaunchKernelGGL(fa::ceiling_mix_kernel<2>, g, blk, 0, st, sink, iters, kMixScale, kMixShift);
+  if (mode == 0) hipLaunchKernelGGL(fa::ceiling_mix_kernel<0>, g, blk, 0, st, sink, clocks, iters, kMixScale, kMixShift);
+  if (mode == 1) hipLaunchKernelGGL(fa::ceiling_mix_kernel<1>, g, blk, 0, st, sink, clocks, iters, kMixScale, kMixShift);
+  if (mode == 2) hipLaunchKernelGGL(fa::ceiling_mix_kernel<2>, g, blk, 0, st, sink, clocks, iters, kMixScale, kMixShift);
   return launch_status(hipGetLastError());
 }
 

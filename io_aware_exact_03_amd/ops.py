@@ -433,15 +433,16 @@ def ceiling_valu(mode: int, iters: int, device="cuda") -> float:
     return cyc.item() / iters
 
 
-def ceiling_mix(mode: int, workgroups: int, iters: int, device="cuda"):
+def ceiling_mix(mode: int, workgroups: int, iters: int, device="cuda", clocks: bool = False):
     """Launch the forward-step instruction-mix loop (mode 0: operands in
     registers, 1: operands read from LDS, 2: plus a barrier every two steps);
-    returns the sink.  The launch performs ceiling_mix_flops(...) matrix
-    flops."""
+    returns (sink, clocks or None).  The launch performs
+    ceiling_mix_flops(...) matrix flops."""
     sink = torch.empty(workgroups * 512, dtype=torch.float32, device=device)
-    _lib.check(_lib.load().fa_ceiling_mix(int(mode), sink.data_ptr(), int(workgroups), int(iters), _stream(sink)),
-               "fa_ceiling_mix")
-    return sink
+    clk = torch.empty(2 * workgroups, dtype=torch.int64, device=device) if clocks else None
+    _lib.check(_lib.load().fa_ceiling_mix(int(mode), sink.data_ptr(), clk.data_ptr() if clk is not None else None,
+                                          int(workgroups), int(iters), _stream(sink)), "fa_ceiling_mix")
+    return sink, clk
 
 
 def ceiling_mix_flops(workgroups: int, iters: int) -> float:

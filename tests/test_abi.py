@@ -217,11 +217,12 @@ def test_ceilings_reject(lib):
     assert lib.fa_ceiling_valu(0, None, A, 10, None) == FA_ERR_ARG
     assert lib.fa_ceiling_valu(1, A + 4, A, 10, None) == FA_ERR_ALIGN
     assert lib.fa_ceiling_valu(2, A, A + 4, 10, None) == FA_ERR_ALIGN
-    assert lib.fa_ceiling_mix(3, A, 1, 1, None) == FA_ERR_ARG  # modes 0-2
-    assert lib.fa_ceiling_mix(0, None, 1, 1, None) == FA_ERR_ARG
-    assert lib.fa_ceiling_mix(0, A, 0, 1, None) == FA_ERR_ARG
-    assert lib.fa_ceiling_mix(1, A, 1, 0, None) == FA_ERR_ARG
-    assert lib.fa_ceiling_mix(2, A + 4, 1, 1, None) == FA_ERR_ALIGN
+    assert lib.fa_ceiling_mix(3, A, None, 1, 1, None) == FA_ERR_ARG  # modes 0-2
+    assert lib.fa_ceiling_mix(0, None, None, 1, 1, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_mix(0, A, None, 0, 1, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_mix(1, A, None, 1, 0, None) == FA_ERR_ARG
+    assert lib.fa_ceiling_mix(2, A + 4, None, 1, 1, None) == FA_ERR_ALIGN
+    assert lib.fa_ceiling_mix(2, A, A + 8, 1, 1, None) == FA_ERR_ALIGN
 
 
 def test_workspace_bytes(lib):

@@ -65,8 +65,10 @@ def test_mix_loop_runs_and_is_finite():
     the same values from two launches (no atomics, fixed order)."""
     fa = _fa()
     for mode in (0, 1, 2):
-        a = fa.ceiling_mix(mode, 4, 20).clone()
-        b = fa.ceiling_mix(mode, 4, 20)
+        a = fa.ceiling_mix(mode, 4, 20)[0].clone()
+        b, clk = fa.ceiling_mix(mode, 4, 20, clocks=True)
         torch.cuda.synchronize()
         assert torch.isfinite(a).all(), mode
         assert torch.equal(a, b), mode
+        c = clk.view(4, 2).cpu()
+        assert (c > 0).all(), mode
