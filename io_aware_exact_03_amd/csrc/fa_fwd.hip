@@ -357,9 +357,11 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   auto tile = [&](int j, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                   const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vp, uint16_t* __restrict__ kl,
                   uint16_t* __restrict__ vl, bool load) __attribute__((always_inline)) {
-    if (load) issue(j + 3, kl, vl);
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
+      // tile j + 3's loads go out halfway through the tile rather than
+      // right after the barrier, where every wave's first reads are
+      if (i == SUB / 2 && load) issue(j + 3, kl, vl);
       const int u = j * SUB + i;
       f32x16& cur = (i % 2 == 0) ? sA : sB;
       f32x16& nxt = (i % 2 == 0) ? sB : sA;
