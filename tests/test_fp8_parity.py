@@ -121,3 +121,40 @@ def test_deterministic():
     b = fa.fwd_fp8(q8, k8, v8, ds, 0.09, True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _codes(x):
+    """E4M3 codes (uint8) of a float tensor, round to nearest even."""
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+@pytest.mark.parametrize("pattern", ["rising", "plateau"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_raises(pattern, causal):
+    """Score patterns that drive the lazy reference: 'rising' scores grow
+    along the keys, so the reference is raised again and again (O and l
+    rescaled, weights redone); 'plateau' keeps every key after the first
+    tile 1 nat above the first tile's maximum, so each tile's four-weight
+    sums exceed 448 (the byte test runs) while no weight overflows (no
+    raise).  Q is all ones, every K row constant, so score j is
+    scale * d * t_j exactly."""
+    fa = _fa()
+    B, H, N, d = 1, 2, 300, 64
+    scale = 1.0 / 8
+    g = torch.Generator(device="cpu").manual_seed(9940)
+    q = torch.ones(B, H, N, d)
+    if pattern == "rising":
+        t = torch.linspace(0.0, 2.0, N)
+    else:
+        t = torch.full((N,), 0.125)
+        t[:64] = 0.0
+    k = t.view(1, 1, N, 1).expand(B, H, N, d).contiguous()
+    v = torch.randn(B, H, N, d, generator=g)
+    q8, k8, v8 = _codes(q), _codes(k), _codes(v)
+    ds = (1.0, 1.0, 1.0)
+    o, lse = fa.fwd_fp8(*P.to_dev(q8, k8, v8), ds, scale, causal)
+    torch.cuda.synchronize()
+    a = (_np(q8), _np(k8), _np(v8), ds, scale, causal)
+    ro, rl = oracle.attn_fwd_fp8(*a)
+    check(o, lse, ro, rl, oracle.p_rounding_bound(*a), f"{pattern} causal={causal}",
+          lse_tol(_np(q8), _np(k8), ds, scale))
