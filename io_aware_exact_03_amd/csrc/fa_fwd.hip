@@ -77,6 +77,13 @@ struct Fwd16 {
 // of its 16 weights stays at or below 2^8 (so every weight does); otherwise
 // the reference max is raised to the true row max and the weights are redone.
 constexpr float kSumLimit = 256.f;
+// A raised reference sits this far (log2 units) above the row max it was
+// raised to, so later, larger scores stay under the limit longer.  bf16
+// weights keep their relative precision at any scale, so for bf16 the lift
+// costs nothing; fp16 weights far below the maximum would fall into fp16's
+// subnormal range sooner, so for fp16 the reference is the row max itself.
+constexpr float ref_lift(BF16) { return 8.f; }
+constexpr float ref_lift(F16) { return 0.f; }
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd16_kernel(
@@ -253,13 +260,14 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
     return part[0] + part[1];
   };
   // Rare path: some lane's weights exceeded the limit.  Raise the reference
-  // to the true row max of this sub-block where it is higher, rescale O and
-  // l, and redo the weights.  Exact: O, l and the LSE share the reference.
+  // to the true row max of this sub-block (plus the lift) where it is
+  // higher, rescale O and l, and redo the weights.  Exact: O, l and the LSE
+  // share the reference.
   auto raise_redo = [&](const f32x16& cur, int key0, uint32_t (&pk)[8], auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     f32x16 c1[1] = {cur};
     const float mt = tile_max<1, MASKED>(c1, qk_scale, key0 + 4 * g, key_lim);
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = fmaxf(m_run, mt + ref_lift(T{}));
     const float alpha = fast_exp2(m_run - m_new);
     l_run *= alpha;
     m_run = m_new;
@@ -389,7 +397,8 @@ __global__ __launch_bounds__(512) void fwd16_kernel(
   if (wave_live) {
     s_gemm(k_lds[0], 0, sA);
     f32x16 s1[1] = {sA};
-    m_run = tile_max<1, true>(s1, qk_scale, 4 * g, key_lim);  // key 0 is visible to every query
+    // key 0 is visible to every query
+    m_run = tile_max<1, true>(s1, qk_scale, 4 * g, key_lim) + ref_lift(T{});
     if (u_last >= 1) {
       // step 0: scores of sub-block 1, weights of 0, no PV product yet
       const uint16_t* k2 = k_lds[2 / SUB];
