@@ -50,16 +50,17 @@ namespace fa {
 // 16-bit (bf16 / fp16) forward
 // ===========================================================================
 // Workgroup: 8 waves x 32 queries (BM = 256, two waves per SIMD; a build may
-// define FA_FWD16_WAVES = 4 to time the one-wave-per-SIMD shape).  K/V tiles
+// define FA_FWD16_WAVES = 4 to time the one-wave-per-SIMD shape), or 4 waves
+// (BM = 128) for problems whose 256-query items would leave CUs idle.  K/V tiles
 // of BN keys go from global memory straight into LDS (no registers), row-major
 // with the XOR chunk swizzle, into five buffers: the previous tile (whose V
 // the first step still reads), the tile being consumed, the next one (whose
 // first score product starts in the current tile's last step) and two in
 // flight.  K feeds S^T = K Q^T with 16-byte row reads; V
 // feeds O^T += V^T P^T through transposing reads (ds_read_b64_tr_b16).
-template <typename T, int D, int BN, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL, int NW_ = FA_FWD16_WAVES>
 struct Fwd16 {
-  static constexpr int NW = FA_FWD16_WAVES, NT = NW * 64, BM = NW * 32;
+  static constexpr int NW = NW_, NT = NW * 64, BM = NW * 32;
   static constexpr int DS = D / 16;          // k-steps of the S product
   static constexpr int DB = D / 32;          // 32-wide d blocks of O
   static constexpr int SUB = BN / 32;        // 32-key sub-blocks per tile
@@ -85,12 +86,12 @@ constexpr float kSumLimit = 256.f;
 constexpr float ref_lift(BF16) { return 8.f; }
 constexpr float ref_lift(F16) { return 0.f; }
 
-template <typename T, int D, int BN, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL, int NW>
 __global__ __launch_bounds__(512) void fwd16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     uint16_t* __restrict__ og, float* __restrict__ lseg, int Nq, int Nk, int qshift, int koff, int n_qblk,
     int BH, int G, float qk_scale, uint32_t qsign) {
-  using C = Fwd16<T, D, BN, CAUSAL>;
+  using C = Fwd16<T, D, BN, CAUSAL, NW>;
   constexpr int DS = C::DS, DB = C::DB, SUB = C::SUB;
   // Swizzled row-major tiles, V below K: the transposing V reads of ring
   // slots 0-3 then reach their address with a per-lane base register and
@@ -1145,6 +1146,23 @@ bool split_keys(const FwdArgs& a, int items, int cus) {
   return a.Nk == a.N && items < cus && a.N <= FwdSplit<D>::KMAX;
 }
 
+// The persistent kernel with NW waves per workgroup: one workgroup per CU
+// (the LDS ring takes the whole 160 KB), never more workgroups than items.
+template <typename T, int D, bool CAUSAL, int NW>
+hipError_t launch16_nw(const FwdArgs& a, int cus, int qshift, int koff) {
+  constexpr int BN = Tile16<D>::BN;
+  using C = Fwd16<T, D, BN, CAUSAL, NW>;
+  const int n_qblk = (a.N + qshift + C::BM - 1) / C::BM;
+  const long long items = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int grid = (int)(items < cus ? items : cus);
+  hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL, NW>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, a.Nk, qshift, koff,
+                     n_qblk, a.BH, a.G, a.qk_scale, a.neg ? 0x80008000u : 0u);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const FwdArgs& a) {
   constexpr int BN = Tile16<D>::BN;
@@ -1156,8 +1174,6 @@ hipError_t launch16(const FwdArgs& a) {
   const int n_qblk = (a.N + qshift + C::BM - 1) / C::BM;
   const long long items = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // One workgroup per CU (the LDS ring takes the whole 160 KB), never more
-  // workgroups than items.
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1172,12 +1188,11 @@ hipError_t launch16(const FwdArgs& a) {
                        a.qk_scale, a.neg ? 0x80008000u : 0u);
     return hipGetLastError();
   }
-  const int grid = (int)(items < cus ? items : cus);
-  hipLaunchKernelGGL((fwd16_kernel<T, D, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, a.stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.N, a.Nk, qshift, koff,
-                     n_qblk, a.BH, a.G, a.qk_scale, a.neg ? 0x80008000u : 0u);
-  return hipGetLastError();
+  // Fewer 256-query items than CUs: 128-query items on four waves fill
+  // twice the CUs; a CU then runs one wave per SIMD, slower per query than
+  // two, but every CU works.
+  if (C::NW == 8 && 2 * items <= cus) return launch16_nw<T, D, CAUSAL, 4>(a, cus, qshift, koff);
+  return launch16_nw<T, D, CAUSAL, C::NW>(a, cus, qshift, koff);
 }
 
 template <int D, bool CAUSAL>
