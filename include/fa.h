@@ -333,8 +333,12 @@ int fa_causal_stages(int row0, int row_end, int bn, int n, int* s1_end, int* s2_
 
 /*
  * The forward's tile for (d, dtype): *bm query rows per workgroup,
- * *bn keys per K/V block, *waves wavefronts of 64 lanes per workgroup.
- * Pure host function; FA_ERR_UNSUPPORTED for unsupported d/dtype.
+ * *bn keys per K/V block, *waves wavefronts of 64 lanes per workgroup, as
+ * the persistent kernel runs it when its work items fill the CUs.  (16-bit
+ * problems whose items would fill at most half the CUs run half as many
+ * waves and query rows per workgroup; short square ones the key-split
+ * kernel, 64 query rows per workgroup.)  Pure host function;
+ * FA_ERR_UNSUPPORTED for unsupported d/dtype.
  */
 int fa_fwd_tile(int d, int dtype, int* bm, int* bn, int* waves);
 
