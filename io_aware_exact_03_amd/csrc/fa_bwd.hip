@@ -621,9 +621,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 // u's vector work (P and dS), then the dQ product of u.  Only a wave's last
 // sub-block (the diagonal, or the sequence tail) is masked.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW_ = FA_DQ_WAVES>
 struct QG {
-  static constexpr int NW = FA_DQ_WAVES, NT = 64 * NW, BM = NW * 32;
+  static constexpr int NW = NW_, NT = 64 * NW, BM = NW * 32;
   static constexpr int BN = D == 128 ? 64 : 128;  // 16 KB of K and of V per tile
   static constexpr int DS = D / 16, DB = D / 32, SUB = BN / 32, CPR = D / 8;
   static constexpr int RPP = 64 / CPR;            // tile rows per 1 KB wave load
@@ -633,13 +633,13 @@ struct QG {
   static_assert(SUB % 2 == 0 && LPW >= 1 && LPW * NW == 2 * PPT && 2 * DB == DS, "tile shape");
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ deltag,
     float* __restrict__ dqg, int N, int n_qblk, int BH, int G, float qk_scale, float dq_scale,
     uint32_t qsign) {
-  using C = QG<D>;
+  using C = QG<D, NW>;
   constexpr int BN = C::BN, DS = C::DS, DB = C::DB, SUB = C::SUB, NS = C::DS;
   // Swizzled row-major tiles, one LDS variable (loads into one ring slot
   // then do not make the compiler wait before reads of another).
@@ -950,7 +950,7 @@ hipError_t run(const BwdArgs& a, int stage) {
   constexpr int RPB = 256 / (D / 8);
   const long long g1 = (rows + RPB - 1) / RPB;
   const int n_kblk = (a.N + KV<D>::BNK - 1) / KV<D>::BNK;
-  const int n_qblk = (a.N + QG<D>::BM - 1) / QG<D>::BM;
+  int n_qblk = (a.N + QG<D>::BM - 1) / QG<D>::BM;
   long long g2 = (long long)items_per_head(n_kblk, CAUSAL) * (a.BH / a.G);
   long long g3 = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -960,6 +960,13 @@ hipError_t run(const BwdArgs& a, int stage) {
   hipError_t de = hipGetDevice(&dev);
   if (de == hipSuccess) de = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (de != hipSuccess) return de;
+  // dQ items that would fill at most half the CUs: 128-query items on four
+  // waves, one per SIMD, so that twice the CUs work
+  const bool dq4 = QG<D>::NW == 8 && 2 * g3 <= cus;
+  if (dq4) {
+    n_qblk = (a.N + QG<D, 4>::BM - 1) / QG<D, 4>::BM;
+    g3 = (long long)items_per_head(n_qblk, CAUSAL) * a.BH;
+  }
   if (g2 > cus) g2 = cus;
   if (g3 > cus) g3 = cus;
   const float qk_scale = fabsf(a.scale) * kLog2eHost;
@@ -985,8 +992,12 @@ hipError_t run(const BwdArgs& a, int stage) {
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 3) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g3), dim3(QG<D>::NT), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, a.G, qk_scale, a.scale, qsign);
+    if (dq4)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, 4>), dim3((unsigned)g3), dim3(QG<D, 4>::NT), 0, a.stream, q, k,
+                         v, dout, a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, a.G, qk_scale, a.scale, qsign);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, QG<D>::NW>), dim3((unsigned)g3), dim3(QG<D>::NT), 0, a.stream, q,
+                         k, v, dout, a.lse, a.delta, a.dq, a.N, n_qblk, a.BH, a.G, qk_scale, a.scale, qsign);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
