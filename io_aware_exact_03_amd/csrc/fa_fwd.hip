@@ -76,7 +76,8 @@ struct Fwd16 {
 
 // A sub-block's weights p = exp2(S q - m) are accepted when this lane's sum
 // of its 16 weights stays at or below 2^8 (so every weight does); otherwise
-// the reference max is raised to the true row max and the weights are redone.
+// the reference max is raised to the true row max (plus the lift below) and
+// the weights are redone.
 constexpr float kSumLimit = 256.f;
 // A raised reference sits this far (log2 units) above the row max it was
 // raised to, so later, larger scores stay under the limit longer.  bf16
@@ -1188,9 +1189,9 @@ hipError_t launch16(const FwdArgs& a) {
                        a.qk_scale, a.neg ? 0x80008000u : 0u);
     return hipGetLastError();
   }
-  // Fewer 256-query items than CUs: 128-query items on four waves fill
-  // twice the CUs; a CU then runs one wave per SIMD, slower per query than
-  // two, but every CU works.
+  // At most half as many 256-query items as CUs: 128-query items on four
+  // waves fill twice the CUs; a CU then runs one wave per SIMD, slower per
+  // query than two, but twice the CUs work.
   if (C::NW == 8 && 2 * items <= cus) return launch16_nw<T, D, CAUSAL, 4>(a, cus, qshift, koff);
   return launch16_nw<T, D, CAUSAL, C::NW>(a, cus, qshift, koff);
 }
