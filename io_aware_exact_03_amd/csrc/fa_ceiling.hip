@@ -56,35 +56,51 @@ __global__ __launch_bounds__(512) void ceiling_mfma_kernel(float* __restrict__ s
   }
 }
 
-// Streaming copy, 16 bytes per lane per access, grid-stride, four accesses
-// in flight per lane.
-__global__ __launch_bounds__(256) void ceiling_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                           size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
-    dst[i] = x0;
-    dst[i + stride] = x1;
-    dst[i + 2 * stride] = x2;
-    dst[i + 3 * stride] = x3;
-  }
-  for (; i < n; i += stride) dst[i] = src[i];
+// The streaming kernels give each workgroup one contiguous chunk of the
+// buffer (a grid-stride walk, where neighbouring workgroups touch addresses
+// a grid apart, sustains about 12% less on this chip) and keep U 16-byte
+// accesses per lane in flight.
+__device__ __forceinline__ void stream_chunk(size_t n, size_t* lo, size_t* hi) {
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  *lo = min(n, (size_t)blockIdx.x * per);
+  *hi = min(n, *lo + per);
 }
 
-// Streaming read: every 16-byte chunk is loaded once and folded into an XOR
-// per lane, written to sink (one word per lane) so no load is dead.
+// Streaming copy, 8 loads then 8 stores per lane per round.
+__global__ __launch_bounds__(256) void ceiling_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           size_t n) {
+  constexpr int U = 8;
+  size_t lo, hi;
+  stream_chunk(n, &lo, &hi);
+  size_t i = lo + threadIdx.x;
+  for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[i + u * 256] = x[u];
+  }
+  for (; i < hi; i += 256) dst[i] = src[i];
+}
+
+// Streaming read, 16 loads per lane per round: every 16-byte chunk is loaded
+// once and folded into an XOR per lane, written to sink (one word per lane)
+// so no load is dead.
 __global__ __launch_bounds__(256) void ceiling_read_kernel(const uint4* __restrict__ src, size_t n,
                                                            uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int U = 16;
+  size_t lo, hi;
+  stream_chunk(n, &lo, &hi);
+  size_t i = lo + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
-    acc ^= (x0.x ^ x0.y ^ x0.z ^ x0.w) ^ (x1.x ^ x1.y ^ x1.z ^ x1.w) ^ (x2.x ^ x2.y ^ x2.z ^ x2.w) ^
-           (x3.x ^ x3.y ^ x3.z ^ x3.w);
+  for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
   }
-  for (; i < n; i += stride) acc ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
+  for (; i < hi; i += 256) acc ^= src[i].x ^ src[i].y ^ src[i].z ^ src[i].w;
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 

@@ -50,6 +50,13 @@
 namespace fa {
 namespace {
 
+// V sub-tiles each wave keeps in its LDS ring (K fragments run one fewer
+// ahead, in registers); a build may define 3 to time the shallower stream.
+#ifndef FA_DEC_SLOTS
+#define FA_DEC_SLOTS 4
+#endif
+static_assert(FA_DEC_SLOTS == 3 || FA_DEC_SLOTS == 4, "decode ring slots");
+
 template <int D, int NW_, int NSLOT_>
 struct Dec {
   static constexpr int NW = NW_, NT = 64 * NW, NSLOT = NSLOT_;
@@ -69,90 +76,68 @@ __device__ __forceinline__ int decode_len(const int* kv_lens, int b, int Nkv) {
   return l < 0 ? 0 : (l > Nkv ? Nkv : l);
 }
 
-// Block-wide sums of tiles over all batches (T) and over batches < blim
-// (P), with all NT threads; `red` holds 2 NT ints.  Block-uniform.
-template <int NT>
-__device__ __forceinline__ void decode_block_sums(const int* kv_lens, int B, int Nkv, int UB, int blim, int* red,
-                                                  int* T_out, int* P_out) {
-  const int tid = threadIdx.x;
+// Wave-wide sum and inclusive prefix sum of an int over the 64 lanes.
+__device__ __forceinline__ int wave_total(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// Sums of tiles over all batches (T) and over batches < blim (P), computed
+// by each wave on its own: no LDS and no barrier, so the first loads of a
+// workgroup wait only for the lengths.  Wave-uniform.
+__device__ __forceinline__ void decode_wave_sums(const int* kv_lens, int B, int Nkv, int UB, int blim, int* T_out,
+                                                 int* P_out) {
+  const int lane = threadIdx.x & 63;
   int sT = 0, sP = 0;
-  for (int b = tid; b < B; b += NT) {
+  for (int b = lane; b < B; b += 64) {
     const int v = decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
     sT += v;
     sP += b < blim ? v : 0;
   }
-  red[tid] = sT;
-  red[NT + tid] = sP;
-  __syncthreads();
-  for (int st = NT / 2; st > 0; st >>= 1) {
-    if (tid < st) {
-      red[tid] += red[tid + st];
-      red[NT + tid] += red[NT + tid + st];
-    }
-    __syncthreads();
-  }
-  *T_out = red[0];
-  *P_out = red[NT];
-  __syncthreads();
+  *T_out = __builtin_amdgcn_readfirstlane(wave_total(sT));
+  *P_out = __builtin_amdgcn_readfirstlane(wave_total(sP));
 }
 
-// The partition, computed by every workgroup of the split kernel with all
-// its threads: the total tile count T, and the batch b holding tile
-// `target` with the first tile P_b of that batch.  Batches go NT at a time
-// through an inclusive scan in LDS (`red`, NT + 2 ints).  Block-uniform.
-template <int NT>
-__device__ __forceinline__ void decode_block_plan(const int* kv_lens, int B, int Nkv, int UB, int parts_total,
-                                                  int part, int* red, int* T_out, int* per_out, int* b_out,
-                                                  int* Pb_out) {
-  const int tid = threadIdx.x;
-  // pass 1: T
+// The partition, computed by each wave on its own: the total tile count T,
+// the tiles per part, and the batch b holding tile part * per with the
+// first tile P_b of that batch (b = B, P_b = T when the part is empty).
+// Batches go 64 at a time through a wave-wide prefix sum.  Wave-uniform.
+__device__ __forceinline__ void decode_wave_plan(const int* kv_lens, int B, int Nkv, int UB, int parts_total,
+                                                 int part, int* T_out, int* per_out, int* b_out, int* Pb_out) {
+  const int lane = threadIdx.x & 63;
   int sum = 0;
-  for (int b = tid; b < B; b += NT) sum += decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
-  red[tid] = sum;
-  __syncthreads();
-  for (int st = NT / 2; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  const int T = red[0];
+  for (int b = lane; b < B; b += 64) sum += decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
+  const int T = __builtin_amdgcn_readfirstlane(wave_total(sum));
   const int per = (T + parts_total - 1) / parts_total;
   const int target = part * per;
-  __syncthreads();
   *T_out = T;
   *per_out = per;
   *b_out = B;
   *Pb_out = T;
   if (target >= T) return;
-  // pass 2: the batch holding `target`
-  if (tid == 0) red[NT] = -1;  // published by the first barrier below
   int base = 0;
-  for (int c0 = 0; c0 < B; c0 += NT) {
-    const int b = c0 + tid;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int b = c0 + lane;
     const int v = b < B ? decode_tiles(decode_len(kv_lens, b, Nkv)) * UB : 0;
-    red[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-      const int x = tid >= off ? red[tid - off] : 0;
-      __syncthreads();
-      red[tid] += x;
-      __syncthreads();
-    }
-    const int incl = base + red[tid];
-    const int chunk_total = red[NT - 1];
-    __syncthreads();
-    if (v > 0 && incl - v <= target && target < incl) {
-      red[NT] = b;
-      red[NT + 1] = incl - v;
-    }
-    __syncthreads();
-    if (red[NT] >= 0) {
-      *b_out = red[NT];
-      *Pb_out = red[NT + 1];
-      __syncthreads();
+    const int incl = base + wave_incl_scan(v);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(v > 0 && incl - v <= target && target < incl);
+    if (hit != 0) {
+      const int src = __builtin_ctzll(hit);
+      *b_out = c0 + src;
+      *Pb_out = __builtin_amdgcn_readlane(incl - v, src);
       return;
     }
-    base += chunk_total;
-    __syncthreads();
+    base = __builtin_amdgcn_readlane(incl, 63);
   }
 }
 
@@ -165,19 +150,24 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
   constexpr int DS = C::DS, DB = C::DB;
   // Each wave's V ring: NSLOT sub-tiles of 32 swizzled rows.
   __shared__ __attribute__((aligned(16))) uint16_t ring[NW][NSLOT][32 * D];
-  __shared__ int plan[C::NT + 2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
   const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB;
 
-  // Batches with no valid key: O = 0, LSE = -inf (no part owns them).
+  // Batches with no valid key: O = 0, LSE = -inf (no part owns them).  The
+  // lengths are read 64 at a time, one per lane; every wave finds the same
+  // batches and the workgroup writes each.
   if (blockIdx.x == 0) {
-    for (int b = 0; b < B; ++b) {
-      if (decode_len(kv_lens, b, Nkv) != 0) continue;
-      for (int i = threadIdx.x; i < H * D; i += C::NT) og[((size_t)b * H) * D + i] = 0;
-      for (int i = threadIdx.x; i < H; i += C::NT) lseg[(size_t)b * H + i] = kNegInf;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+      uint64_t zero = __builtin_amdgcn_ballot_w64(c0 + lane < B && decode_len(kv_lens, c0 + lane, Nkv) == 0);
+      while (zero != 0) {
+        const int bz = c0 + __builtin_ctzll(zero);
+        zero &= zero - 1;
+        for (int i = threadIdx.x; i < H * D; i += C::NT) og[((size_t)bz * H) * D + i] = 0;
+        for (int i = threadIdx.x; i < H; i += C::NT) lseg[(size_t)bz * H + i] = kNegInf;
+      }
     }
   }
 
@@ -185,7 +175,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
   // which the query blocks of one K/V head read in turn.
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   int Ttot, per, b, P_b;
-  decode_block_plan<C::NT>(kv_lens, B, Nkv, UB, (int)gridDim.x, w, plan, &Ttot, &per, &b, &P_b);
+  decode_wave_plan(kv_lens, B, Nkv, UB, (int)gridDim.x, w, &Ttot, &per, &b, &P_b);
   int t = w * per;
   const int t_end = min(t + per, Ttot);
   if (t >= t_end) return;
@@ -226,7 +216,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     // Loads of the wave's i-th sub-tile: K fragments into a register set
     // (lane (n, g): key n, elements 16 k + 8 g .. + 8) and V rows into a
     // ring slot (row r, stored chunk c holds global chunk c ^ swz_chunk(r)).
-    uint4 kf[2][DS];
+    uint4 kf[NSLOT - 1][DS];
     auto issue_k = [&](int i, uint4 (&kd)[DS]) __attribute__((always_inline)) {
       const int key0 = k0 + 32 * (wave + NW * i);
 #pragma unroll
@@ -281,8 +271,17 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
       if (__builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0) m_run = fmaxf(m_run, row_max());
       float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) psum += fast_exp2(x[r] - m_run);
+      for (int r = 0; r < 16; ++r) {
+        x[r] = fast_exp2(x[r] - m_run);
+        psum += x[r];
+      }
       if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
+        // the scores again (the weights overwrote them), then the new reference
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
+          x[r] = key < k1 ? sc[r] * qk_scale : kNegInf;
+        }
         const float m_new = fmaxf(m_run, row_max());
         const float alpha = fast_exp2(m_run - m_new);
         l_run *= alpha;
@@ -293,11 +292,12 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
         m_run = m_new;
         psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) psum += fast_exp2(x[r] - m_run);
+        for (int r = 0; r < 16; ++r) {
+          x[r] = fast_exp2(x[r] - m_run);
+          psum += x[r];
+        }
       }
       l_run += psum;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - m_run);
       // P^T as the B operand of O^T += V^T P^T: registers 8 h .. 8 h + 7
       // are the keys of 16-key step h in the order read_tr delivers V^T's rows.
 #pragma unroll
@@ -311,38 +311,44 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     };
 
     // The wave's stream: the K fragments of sub-tile i go into register set
-    // i % 2 one sub-tile ahead, its V rows into ring slot i % NSLOT two
-    // sub-tiles ahead; step i issues K(i+1) and then V(i+2), so waiting until
-    // only the DS + 2 VL loads issued after K(i) are outstanding (in-order
-    // counter) means K(i) and V(i) have arrived while V(i+1), K(i+1) and
-    // V(i+2) stay in flight.  Only this wave reads its slots, so no barrier.
-    // The loop is unrolled over six steps so every register set and LDS
-    // offset is fixed; the slots go in as distinct __restrict__ pointers
-    // (loads into one do not alias reads of another, so the compiler does
-    // not wait for them).
-    static_assert(NSLOT == 3, "two V sub-tiles ahead");
+    // i % (KA + 1), KA = NSLOT - 2 sub-tiles ahead, its V rows into ring slot
+    // i % NSLOT, VA = NSLOT - 1 ahead.  The first KA K and VA V sub-tiles go
+    // out as K(0) V(0) K(1) V(1) ... V(VA - 1); step i then issues K(i + KA)
+    // and V(i + VA).  In that order the last of K(i) and V(i) is followed
+    // by the loads of the next min(KA, r) K and min(VA, r) V sub-tiles
+    // (r = sub-tiles after i), so waiting until only those are outstanding
+    // (in-order counter) means K(i) and V(i) have arrived.  Only this wave
+    // reads its slots, so no barrier.  The loop is unrolled over
+    // (KA + 1) NSLOT steps so every register set and LDS offset is fixed;
+    // the slots go in as distinct __restrict__ pointers (loads into one do
+    // not alias reads of another, so the compiler does not wait for them).
+    constexpr int KA = NSLOT - 2, VA = NSLOT - 1, UNR = (KA + 1) * NSLOT;
+    static_assert(KA >= 1 && VA * C::VL + KA * DS < 64, "vmcnt range");
     uint16_t* const myring = ring[wave][0];
-    if (n_mine > 0) {
-      issue_k(0, kf[0]);
-      issue_v(0, myring);
+#pragma unroll
+    for (int s0 = 0; s0 < VA; ++s0) {
+      if (s0 < KA && s0 < n_mine) issue_k(s0, kf[s0]);
+      if (s0 < n_mine) issue_v(s0, myring + s0 * 32 * D);
     }
-    if (n_mine > 1) issue_v(1, myring + 32 * D);
     auto step = [&](int i, const uint4 (&kd)[DS], uint4 (&kn)[DS], const uint16_t* __restrict__ vt,
-                    uint16_t* __restrict__ vn2) __attribute__((always_inline)) {
-      if (i + 1 < n_mine) issue_k(i + 1, kn);
-      if (i + 2 < n_mine) issue_v(i + 2, vn2);
-      const int later = (i + 1 < n_mine ? C::VL + DS : 0) + (i + 2 < n_mine ? C::VL : 0);
-      if (later == C::VL + DS + C::VL) vm_wait<2 * C::VL + DS>();
-      else if (later == C::VL + DS) vm_wait<C::VL + DS>();
+                    uint16_t* __restrict__ vn) __attribute__((always_inline)) {
+      if (i + KA < n_mine) issue_k(i + KA, kn);
+      if (i + VA < n_mine) issue_v(i + VA, vn);
+      const int r = n_mine - 1 - i;
+      if (r >= VA) vm_wait<VA * C::VL + KA * DS>();
+      else if (r >= 2) vm_wait<2 * (C::VL + DS)>();  // VA = 3: r = 2 = KA
+      else if (r == 1) vm_wait<C::VL + DS>();
       else vm_wait<0>();
       sub_block(kd, vt, k0 + 32 * (wave + NW * i));
     };
-    for (int i0 = 0; i0 < n_mine; i0 += 6) {
+    static_assert(VA <= 3, "wait cases");
+    for (int i0 = 0; i0 < n_mine; i0 += UNR) {
 #pragma unroll
-      for (int jj = 0; jj < 6; ++jj) {
+      for (int jj = 0; jj < UNR; ++jj) {
         const int i = i0 + jj;
         if (i < n_mine)
-          step(i, kf[jj % 2], kf[(jj + 1) % 2], myring + (jj % 3) * 32 * D, myring + ((jj + 2) % 3) * 32 * D);
+          step(i, kf[jj % (KA + 1)], kf[(jj + KA) % (KA + 1)], myring + (jj % NSLOT) * 32 * D,
+               myring + ((jj + VA) % NSLOT) * 32 * D);
       }
     }
 
@@ -445,7 +451,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   constexpr int U = 4;        // pieces per group in flight
   __shared__ float red[8][D];
   __shared__ float rs[2][8];
-  __shared__ int sums[512];
   const int Hkv = H / G, QB = decode_query_blocks(G), UB = Hkv * QB, CPU = min(32, G);
   const int u = blockIdx.x / CPU, col = blockIdx.x % CPU;
   const int b = u / UB, ui = u % UB, qb = ui % QB;
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     Ttot = B * UB * nb;
     P_b = b * UB * nb;
   } else {
-    decode_block_sums<256>(kv_lens, B, Nkv, UB, b, sums, &Ttot, &P_b);
+    decode_wave_sums(kv_lens, B, Nkv, UB, b, &Ttot, &P_b);
   }
   const int per = (Ttot + n_parts - 1) / n_parts;
   const int P_u = P_b + ui * nb;
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 template <typename T, int D>
 hipError_t run(const DecodeArgs& a) {
-  constexpr int NW = 4, NSLOT = 3;
+  constexpr int NW = 4, NSLOT = FA_DEC_SLOTS;
   using C = Dec<D, NW, NSLOT>;
   const float qk_scale = a.scale * kLog2eHost;
   hipLaunchKernelGGL((decode_split_kernel<T, D, NW, NSLOT>), dim3((unsigned)a.parts), dim3(C::NT), 0, a.stream,

@@ -143,6 +143,21 @@ def test_lengths_edge_cases(n_parts):
     assert bool((o[0] == 0).all()) and bool((o[6] == 0).all())
 
 
+@pytest.mark.parametrize("n_parts", [1, 7, 200])
+def test_many_batches(n_parts):
+    """More batches than a wave has lanes: the workgroups locate their
+    ranges 64 batches at a time, so empty batches and ranges that start or
+    end on either side of a 64-batch boundary must all come out right."""
+    g = torch.Generator().manual_seed(9975)
+    lens = torch.randint(1, 301, (150,), generator=g, dtype=torch.int32)
+    for b in (0, 63, 64, 65, 127, 128, 149):
+        lens[b] = 0
+    lens[62] = 300
+    lens[129] = 1
+    res = _run(150, 2, 1, 300, 64, "bf16", 9976, n_parts, lens=lens)
+    _check(*res[:7], "bf16", f"B150 parts={n_parts}")
+
+
 @pytest.mark.parametrize("n_parts", [1, 3])
 def test_rows_past_the_length_are_never_read(n_parts):
     """Cache rows at and beyond each length hold NaN; the result is finite and
