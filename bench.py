@@ -9,9 +9,11 @@ credited attention TFLOP/s of that step: forward 4*B*H*N^2*d and backward
 
 The same run also times, as separate legs reported under "legs": the causal
 prefill forward (B2 H32 N8192 d128 bf16), the long causal forward and the
-naive three-kernel baseline (B1 H16 N16384 d64 bf16), the non-causal fp16
-sweep N=512..4096 (fused vs naive, with the byte models), and the fp32
-single-head forward.  The sweep and the single-head legs are short calls:
+naive three-kernel baseline (B1 H16 N16384 d64 bf16), the non-causal bf16
+d128 forwards (B2 H32 N8192 and B1 H32 N16384), the FP8, grouped-query,
+chunked-prefill and decode workloads, the FA1 loop order, the non-causal
+fp16 sweep N=512..4096 (fused vs naive, with the byte models), and the
+fp32 single-head forward.  The sweep and the single-head legs are short calls:
 their times come from back-to-back calls replayed from a HIP graph (host
 launch cost excluded), with the single eager call's time beside them.
 `cpu_baseline` times the fp64 oracle on a sample of the step's heads on the
@@ -1110,8 +1112,9 @@ def read_traffic_legs(digest: str):
 def run_legs(torch, fa, fa_synth, dev):
     legs = {}
 
-    # causal prefill forward and long causal forward (bf16)
-    for w in (fa_synth.CAUSAL_PREFILL, fa_synth.LONG_CAUSAL):
+    # causal prefill forward and long causal forward (bf16), and the
+    # non-causal d = 128 forwards beside them
+    for w in (fa_synth.CAUSAL_PREFILL, fa_synth.LONG_CAUSAL, fa_synth.NONCAUSAL_PREFILL, fa_synth.NONCAUSAL_LONG):
         q, k, v = (t.to(dev) for t in fa_synth.workload_inputs(w, with_dout=False))
         o, lse = fa.fwd(q, k, v, w.scale, w.causal)
         fn = lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)

@@ -63,6 +63,13 @@ CAUSAL_PREFILL = Workload("causal_prefill_fwd_B2_H32_N8192_d128_bf16", 2, 32, 81
 # Long causal sequence with wide logits, naive baseline beside it.
 LONG_CAUSAL = Workload("long_causal_fwd_B1_H16_N16384_d64_bf16", 1, 16, 16384, 64, "bf16", True, 1 / 8,
                        1004, sigma_qk=2.0, naive=True)
+# The causal prefill's shape without the mask, and a longer non-causal
+# sequence at d = 128: the forward's rate where no block is cut by the
+# diagonal.
+NONCAUSAL_PREFILL = Workload("noncausal_prefill_fwd_B2_H32_N8192_d128_bf16", 2, 32, 8192, 128, "bf16", False,
+                             1 / math.sqrt(128), 1011)
+NONCAUSAL_LONG = Workload("noncausal_fwd_B1_H32_N16384_d128_bf16", 1, 32, 16384, 128, "bf16", False,
+                          1 / math.sqrt(128), 1012)
 # Causal training step: forward and backward.
 TRAIN_STEP = Workload("causal_train_step_B4_H16_N4096_d128_bf16", 4, 16, 4096, 128, "bf16", True,
                       1 / math.sqrt(128), 1005, passes=("fwd", "bwd"))

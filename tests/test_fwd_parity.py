@@ -147,7 +147,8 @@ def test_single_head_f32_full():
 
 
 @pytest.mark.parametrize("w", fa_synth.NONCAUSAL_SWEEP + (fa_synth.CAUSAL_PREFILL, fa_synth.LONG_CAUSAL,
-                                                          fa_synth.TRAIN_STEP), ids=lambda w: w.name)
+                                                          fa_synth.TRAIN_STEP, fa_synth.NONCAUSAL_PREFILL,
+                                                          fa_synth.NONCAUSAL_LONG), ids=lambda w: w.name)
 def test_full_size_sampled(w):
     """Full-size workloads in the launch configuration the bench times:
     sampled heads and rows against the oracle, and every output finite."""
