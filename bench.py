@@ -755,6 +755,12 @@ def measure_ceilings(torch, fa, dev):
     sink = fa.ceiling_read(src)
     ms, _ = time_reps(lambda: fa.ceiling_read(src, sink), 10, torch)
     out["read_gbs"] = nbytes / (ms * 1e-3) / 1e9
+    # the same read over 128 MiB, about a decode step's cache (one launch
+    # then carries its ramp and tail, as the decode kernels do)
+    small = src[: (128 << 20) // 4]
+    fa.ceiling_read(small, sink)
+    ms, _ = time_reps(lambda: fa.ceiling_read(small, sink), 20, torch)
+    out["read_gbs_128mib"] = (128 << 20) / (ms * 1e-3) / 1e9
     del src, dst, sink
     torch.cuda.empty_cache()
     # vector issue cost of the softmax's instructions, one wave (shader-clock
@@ -777,7 +783,7 @@ def measure_ceilings(torch, fa, dev):
     out["fwd_step_mix"] = mix
     out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
     out["how"] = ("fa_ceiling_mfma: 256 workgroups x 8 waves x 4000 x 8 products; fa_ceiling_copy / "
-                  "fa_ceiling_read over 2 GiB; medians of HIP-event timings; fa_ceiling_valu: one wave, "
+                  "fa_ceiling_read over 2 GiB (and 128 MiB); medians of HIP-event timings; fa_ceiling_valu: one wave, "
                   "20000 iterations of 32 exp + 32 mul / 96 fma / both; fa_ceiling_mix: 256 workgroups x 8 "
                   "waves x 2000 forward steps of 16 products and 16 weights")
     return out
