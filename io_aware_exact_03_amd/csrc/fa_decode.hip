@@ -50,22 +50,16 @@
 namespace fa {
 namespace {
 
-// V sub-tiles each wave keeps in its LDS ring (K fragments run one fewer
-// ahead, in registers); a build may define 3 to time the shallower stream.
-#ifndef FA_DEC_SLOTS
-#define FA_DEC_SLOTS 4
-#endif
-static_assert(FA_DEC_SLOTS == 3 || FA_DEC_SLOTS == 4, "decode ring slots");
-
 template <int D, int NW_, int NSLOT_>
 struct Dec {
   static constexpr int NW = NW_, NT = 64 * NW, NSLOT = NSLOT_;
   static constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   static constexpr int RPP = 64 / CPR;          // sub-tile rows per 1 KB wave load
-  static constexpr int VL = 32 / RPP;           // 1 KB loads per 32-key V sub-tile
+  static constexpr int VL = 32 / RPP;           // 1 KB loads per 32-key K or V sub-tile
+  static constexpr int KSLOT = NSLOT - 1;       // K ring slots (K runs one fewer sub-tile ahead)
   static constexpr int EPT = D / (2 * NW);      // output elements per thread in the combine
   static constexpr int OROW = D + 1;            // padded fp32 row of a wave's O in LDS
-  static_assert(2 * VL + DS < 64, "vmcnt range");
+  static_assert((NSLOT + KSLOT) * NW * 32 * D * 2 <= 160 * 1024, "rings fit in LDS");
   static_assert(EPT % 8 == 0, "combine vector width");
   static_assert(NW * 32 * (OROW + 2) * 4 <= NW * NSLOT * 32 * D * 2, "combine fits in the ring");
 };
@@ -148,8 +142,9 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     float* __restrict__ opart, float* __restrict__ lpart, int B, int H, int G, int Nkv, float qk_scale) {
   using C = Dec<D, NW, NSLOT>;
   constexpr int DS = C::DS, DB = C::DB;
-  // Each wave's V ring: NSLOT sub-tiles of 32 swizzled rows.
+  // Each wave's rings: NSLOT V and NSLOT - 1 K sub-tiles of 32 swizzled rows.
   __shared__ __attribute__((aligned(16))) uint16_t ring[NW][NSLOT][32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kring[NW][C::KSLOT][32 * D];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -213,23 +208,20 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const int n_sub = (k1 - k0 + 31) / 32;
     const int n_mine = n_sub > wave ? (n_sub - 1 - wave) / NW + 1 : 0;
 
-    // Loads of the wave's i-th sub-tile: K fragments into a register set
-    // (lane (n, g): key n, elements 16 k + 8 g .. + 8) and V rows into a
-    // ring slot (row r, stored chunk c holds global chunk c ^ swz_chunk(r)).
-    uint4 kf[NSLOT - 1][DS];
-    auto issue_k = [&](int i, uint4 (&kd)[DS]) __attribute__((always_inline)) {
-      const int key0 = k0 + 32 * (wave + NW * i);
-#pragma unroll
-      for (int k = 0; k < DS; ++k) kd[k] = load16(krs, ((uint32_t)(key0 + n) * D + 16 * k + 8 * g) * 2);
-    };
-    auto issue_v = [&](int i, uint16_t* __restrict__ vd) __attribute__((always_inline)) {
+    // Loads of the wave's i-th sub-tile: its K rows and its V rows each into
+    // a ring slot (row r, stored chunk c holds global chunk c ^
+    // swz_chunk(r)), straight from global memory.  The loads are issued so
+    // that the compiler does not track them (it would otherwise wait for
+    // all of them wherever its view of the stream's branches is unsure);
+    // the stream below waits for them explicitly.
+    auto issue_rows = [&](const rsrc_t& rs, int i, uint16_t* dst) __attribute__((always_inline)) {
       const int key0 = k0 + 32 * (wave + NW * i);
       const int lrow = lane / C::CPR;
 #pragma unroll
       for (int e = 0; e < C::VL; ++e) {
         const int row = e * C::RPP + lrow;
         const int ch = (lane % C::CPR) ^ swz_chunk<D>(row);
-        load_lds16(vrs, vd + e * C::RPP * D, ((uint32_t)(key0 + row) * D + 8 * ch) * 2);
+        load_lds16_untracked(rs, lds_addr(dst + e * C::RPP * D), ((uint32_t)(key0 + row) * D + 8 * ch) * 2);
       }
     };
 
@@ -238,15 +230,28 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     m_run = kNegInf;
     l_run = 0.f;
 
-    // One 32-key sub-tile: K fragments kd, V rows in vt, first key key0.
-    auto sub_block = [&](const uint4 (&kd)[DS], const uint16_t* __restrict__ vt, int key0)
-        __attribute__((always_inline)) {
+    // The operand fragments of one sub-tile, read from its slots into
+    // registers: K fragment k of lane (n, g) is key n, elements 16 k + 8 g ..
+    // + 8 (A operand of S^T = K Q^T); V^T fragment h DB + db covers keys
+    // 16 h .. and d block db (A operand of O^T += V^T P^T).
+    auto read_frags = [&](const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt, uint4 (&kfr)[DS],
+                          uint4 (&vfr)[2 * DB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < DS; ++k) kfr[k] = read_row<D>(kt, n, 16 * k + 8 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vfr[h * DB + db] = read_tr<D>(vt, 16 * h, 32 * db, lane);
+    };
+
+    // One 32-key sub-tile from its fragments; first key key0.
+    auto sub_block = [&](const uint4 (&kfr)[DS], const uint4 (&vfr)[2 * DB], int key0) __attribute__((always_inline)) {
       // two independent product chains (even and odd k), summed
       f32x16 sc = f32x16{}, sc1 = f32x16{};
 #pragma unroll
       for (int k = 0; k < DS; k += 2) {
-        sc = mma16(T{}, kd[k], qf[k], sc);
-        sc1 = mma16(T{}, kd[k + 1], qf[k + 1], sc1);
+        sc = mma16(T{}, kfr[k], qf[k], sc);
+        sc1 = mma16(T{}, kfr[k + 1], qf[k + 1], sc1);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] += sc1[r];
@@ -306,49 +311,63 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
                                     pack2(T{}, x[8 * h + 4], x[8 * h + 5]), pack2(T{}, x[8 * h + 6], x[8 * h + 7]));
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          oacc[db] = mma16(T{}, read_tr<D>(vt, 16 * h, 32 * db, lane), pk, oacc[db]);
+          oacc[db] = mma16(T{}, vfr[h * DB + db], pk, oacc[db]);
       }
     };
 
-    // The wave's stream: the K fragments of sub-tile i go into register set
-    // i % (KA + 1), KA = NSLOT - 2 sub-tiles ahead, its V rows into ring slot
-    // i % NSLOT, VA = NSLOT - 1 ahead.  The first KA K and VA V sub-tiles go
-    // out as K(0) V(0) K(1) V(1) ... V(VA - 1); step i then issues K(i + KA)
-    // and V(i + VA).  In that order the last of K(i) and V(i) is followed
-    // by the loads of the next min(KA, r) K and min(VA, r) V sub-tiles
-    // (r = sub-tiles after i), so waiting until only those are outstanding
-    // (in-order counter) means K(i) and V(i) have arrived.  Only this wave
-    // reads its slots, so no barrier.  The loop is unrolled over
-    // (KA + 1) NSLOT steps so every register set and LDS offset is fixed;
-    // the slots go in as distinct __restrict__ pointers (loads into one do
-    // not alias reads of another, so the compiler does not wait for them).
-    constexpr int KA = NSLOT - 2, VA = NSLOT - 1, UNR = (KA + 1) * NSLOT;
-    static_assert(KA >= 1 && VA * C::VL + KA * DS < 64, "vmcnt range");
+    // The wave's stream: the K rows of sub-tile i go into K slot i % KA, its
+    // V rows into V slot i % VA.  The first KA K and VA V sub-tiles go out
+    // as K(0) V(0) K(1) V(1) ... V(VA - 1).  Step i waits for K(i) and V(i),
+    // reads both into registers, and only then reuses their slots for
+    // K(i + KA) and V(i + VA), so KA K and VA V sub-tiles are in flight
+    // while it computes.  In that order the last of K(i) and V(i) is
+    // followed by the loads of the next min(KA - 1, r) K and min(VA - 1, r)
+    // V sub-tiles (r = sub-tiles after i), so waiting until only those are
+    // outstanding (in-order counter) means K(i) and V(i) are in LDS.  Only
+    // this wave reads its slots, so no barrier.  The loop is unrolled over
+    // KA VA steps so every LDS offset is fixed.
+    constexpr int KA = C::KSLOT, VA = NSLOT, UNR = KA * VA;
+    static_assert(KA == 2 && VA == 3, "wait cases");
     uint16_t* const myring = ring[wave][0];
+    uint16_t* const mykring = kring[wave][0];
 #pragma unroll
     for (int s0 = 0; s0 < VA; ++s0) {
-      if (s0 < KA && s0 < n_mine) issue_k(s0, kf[s0]);
-      if (s0 < n_mine) issue_v(s0, myring + s0 * 32 * D);
+      if (s0 < KA && s0 < n_mine) issue_rows(krs, s0, mykring + s0 * 32 * D);
+      if (s0 < n_mine) issue_rows(vrs, s0, myring + s0 * 32 * D);
     }
-    auto step = [&](int i, const uint4 (&kd)[DS], uint4 (&kn)[DS], const uint16_t* __restrict__ vt,
-                    uint16_t* __restrict__ vn) __attribute__((always_inline)) {
-      if (i + KA < n_mine) issue_k(i + KA, kn);
-      if (i + VA < n_mine) issue_v(i + VA, vn);
-      const int r = n_mine - 1 - i;
-      if (r >= VA) vm_wait<VA * C::VL + KA * DS>();
-      else if (r >= 2) vm_wait<2 * (C::VL + DS)>();  // VA = 3: r = 2 = KA
-      else if (r == 1) vm_wait<C::VL + DS>();
-      else vm_wait<0>();
-      sub_block(kd, vt, k0 + 32 * (wave + NW * i));
+    // Read sub-tile i's fragments, then refill its slots once the reads have
+    // returned (lgkmcnt(0)), then compute.
+    auto step_tail = [&](int i, uint16_t* __restrict__ kt, uint16_t* __restrict__ vt) __attribute__((always_inline)) {
+      uint4 kfr[DS], vfr[2 * DB];
+      read_frags(kt, vt, kfr, vfr);
+      lds_fence();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt free
+      if (i + KA < n_mine) issue_rows(krs, i + KA, kt);
+      if (i + VA < n_mine) issue_rows(vrs, i + VA, vt);
+      sub_block(kfr, vfr, k0 + 32 * (wave + NW * i));
     };
-    static_assert(VA <= 3, "wait cases");
+    // Step 0 waits for everything in flight (the first sub-tiles and the
+    // query fragments): the compiler tracks the query loads but not the
+    // tile loads behind them, so a wait it placed for the fragments would
+    // hold a later step until every tile load issued so far had arrived.
+    // After this wait it has no load to wait for.
+    if (n_mine > 0) {
+      vm_wait<0>();
+      lds_fence();
+      step_tail(0, mykring, myring);
+    }
     for (int i0 = 0; i0 < n_mine; i0 += UNR) {
 #pragma unroll
       for (int jj = 0; jj < UNR; ++jj) {
         const int i = i0 + jj;
-        if (i < n_mine)
-          step(i, kf[jj % (KA + 1)], kf[(jj + KA) % (KA + 1)], myring + (jj % NSLOT) * 32 * D,
-               myring + ((jj + VA) % NSLOT) * 32 * D);
+        if (i >= 1 && i < n_mine) {
+          const int r = n_mine - 1 - i;
+          if (r >= 2) vm_wait<(KA - 1 + VA - 1) * C::VL>();
+          else if (r == 1) vm_wait<2 * C::VL>();
+          else vm_wait<0>();
+          lds_fence();
+          step_tail(i, mykring + (jj % KA) * 32 * D, myring + (jj % VA) * 32 * D);
+        }
       }
     }
 
@@ -549,7 +568,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 template <typename T, int D>
 hipError_t run(const DecodeArgs& a) {
-  constexpr int NW = 4, NSLOT = FA_DEC_SLOTS;
+  constexpr int NW = 4, NSLOT = 3;
   using C = Dec<D, NW, NSLOT>;
   const float qk_scale = a.scale * kLog2eHost;
   hipLaunchKernelGGL((decode_split_kernel<T, D, NW, NSLOT>), dim3((unsigned)a.parts), dim3(C::NT), 0, a.stream,
