@@ -230,64 +230,73 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     m_run = kNegInf;
     l_run = 0.f;
 
-    // The operand fragments of one sub-tile, read from its slots into
-    // registers: K fragment k of lane (n, g) is key n, elements 16 k + 8 g ..
-    // + 8 (A operand of S^T = K Q^T); V^T fragment h DB + db covers keys
-    // 16 h .. and d block db (A operand of O^T += V^T P^T).
-    auto read_frags = [&](const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt, uint4 (&kfr)[DS],
-                          uint4 (&vfr)[2 * DB]) __attribute__((always_inline)) {
+    // Operand fragments, read from a slot into registers: K fragment k of
+    // lane (n, g) is key n, elements 16 k + 8 g .. + 8 (A operand of S^T =
+    // K Q^T); V^T fragment h DB + db covers keys 16 h .. and d block db (A
+    // operand of O^T += V^T P^T).
+    // In the swizzled layout every fragment sits at a per-lane base XOR a
+    // constant plus a row offset (the chunk permutation only touches the
+    // address bits within a row): K fragment k at Rb ^ 32 k bytes, the two
+    // transposing reads of V^T fragment (h, db) at (Tb ^ 64 db) + 32 h D and
+    // (Tb ^ 64 db ^ 32) + (32 h + 16) D.  The bases pass through an empty
+    // asm at each use, so the addresses are formed next to their reads
+    // rather than kept live for every slot of the unrolled loop.
+    const uint32_t Rb = 2u * (uint32_t)swz<D>(n, 8 * g);
+    const uint32_t Tb = 2u * (uint32_t)swz<D>(4 * g + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    auto read_k = [&](const uint16_t* __restrict__ kt, uint4 (&kfr)[DS]) __attribute__((always_inline)) {
+      uint32_t rb = Rb;
+      asm volatile("" : "+v"(rb));
+      const char* base = reinterpret_cast<const char*>(kt);
 #pragma unroll
-      for (int k = 0; k < DS; ++k) kfr[k] = read_row<D>(kt, n, 16 * k + 8 * g);
+      for (int k = 0; k < DS; ++k) kfr[k] = *reinterpret_cast<const uint4*>(base + (rb ^ (32 * k)));
+    };
+    auto read_v = [&](const uint16_t* __restrict__ vt, uint4 (&vfr)[2 * DB]) __attribute__((always_inline)) {
+      uint32_t tb = Tb;
+      asm volatile("" : "+v"(tb));
+      const char* base = reinterpret_cast<const char*>(vt);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vfr[h * DB + db] = read_tr<D>(vt, 16 * h, 32 * db, lane);
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t t = tb ^ (64 * db);
+          const uint2 lo = read_tr_b64(reinterpret_cast<const uint16_t*>(base + t + 32 * h * D));
+          const uint2 hi = read_tr_b64(reinterpret_cast<const uint16_t*>(base + (t ^ 32) + (32 * h + 16) * D));
+          vfr[h * DB + db] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    };
+    // Once this wave's LDS reads have returned, their slots may be refilled.
+    auto reads_done = [&]() __attribute__((always_inline)) {
+      lds_fence();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt free
     };
 
-    // One 32-key sub-tile from its fragments; first key key0.
-    auto sub_block = [&](const uint4 (&kfr)[DS], const uint4 (&vfr)[2 * DB], int key0) __attribute__((always_inline)) {
-      // two independent product chains (even and odd k), summed
-      f32x16 sc = f32x16{}, sc1 = f32x16{};
-#pragma unroll
-      for (int k = 0; k < DS; k += 2) {
-        sc = mma16(T{}, kfr[k], qf[k], sc);
-        sc1 = mma16(T{}, kfr[k + 1], qf[k + 1], sc1);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] += sc1[r];
-      // register r is key key0 + 8 (r / 4) + 4 g + r % 4
-      float x[16];
+    // Scores of a sub-tile: two independent product chains (even and odd
+    // k), summed.  Register r of S^T is key key0 + 8 (r / 4) + 4 g + r % 4.
+    f32x16 scur;  // scores of the sub-tile whose weights the next step computes
+    // Lazy reference max, as in the forward: the wave's first sub-tile sets
+    // the reference to its row max (it holds a valid key); later weights are
+    // accepted while each lane's sum of its 16 weights stays at or below
+    // 2^8, otherwise (rare) the reference is raised to the row max and O, l
+    // rescaled.  Exact: O, l and the LSE share the reference.  Keys past
+    // k1 (only in a segment's last sub-tile) get weight zero.
+    auto row_max = [&](int key0) __attribute__((always_inline)) {
+      float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
-        x[r] = key < k1 ? sc[r] * qk_scale : kNegInf;
+        mx = fmaxf(mx, key < k1 ? scur[r] * qk_scale : kNegInf);
       }
-      // Lazy reference max, as in the forward: the wave's first sub-tile sets
-      // the reference to its row max (some key of it is valid); later
-      // weights are accepted while each lane's sum of its 16 weights stays
-      // at or below 2^8, otherwise (rare) the reference is raised to the row
-      // max and O, l rescaled.  Exact: O, l and the LSE share the reference.
-      auto row_max = [&]() __attribute__((always_inline)) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
-        return halves_max(mx);
-      };
-      if (__builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0) m_run = fmaxf(m_run, row_max());
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = fast_exp2(x[r] - m_run);
-        psum += x[r];
-      }
+      return halves_max(mx);
+    };
+    auto weight = [&](int key0, int r) __attribute__((always_inline)) {
+      const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
+      return key < k1 ? fast_exp2(__builtin_fmaf(scur[r], qk_scale, -m_run)) : 0.f;
+    };
+    // The rare raise, then the row sum joins l and the weights of scur
+    // (x) go into the PV product with V^T fragments vfr.
+    auto finish = [&](int key0, float (&x)[16], float psum, const uint4 (&vfr)[2 * DB]) __attribute__((always_inline)) {
       if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
-        // the scores again (the weights overwrote them), then the new reference
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 8 * (r / 4) + 4 * g + (r % 4);
-          x[r] = key < k1 ? sc[r] * qk_scale : kNegInf;
-        }
-        const float m_new = fmaxf(m_run, row_max());
+        const float m_new = fmaxf(m_run, row_max(key0));
         const float alpha = fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
         psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          x[r] = fast_exp2(x[r] - m_run);
+          x[r] = weight(key0, r);
           psum += x[r];
         }
       }
@@ -310,65 +319,125 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
         const uint4 pk = make_uint4(pack2(T{}, x[8 * h + 0], x[8 * h + 1]), pack2(T{}, x[8 * h + 2], x[8 * h + 3]),
                                     pack2(T{}, x[8 * h + 4], x[8 * h + 5]), pack2(T{}, x[8 * h + 6], x[8 * h + 7]));
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[db] = mma16(T{}, vfr[h * DB + db], pk, oacc[db]);
+        for (int db = 0; db < DB; ++db) oacc[db] = mma16(T{}, vfr[h * DB + db], pk, oacc[db]);
       }
     };
 
-    // The wave's stream: the K rows of sub-tile i go into K slot i % KA, its
-    // V rows into V slot i % VA.  The first KA K and VA V sub-tiles go out
-    // as K(0) V(0) K(1) V(1) ... V(VA - 1).  Step i waits for K(i) and V(i),
-    // reads both into registers, and only then reuses their slots for
-    // K(i + KA) and V(i + VA), so KA K and VA V sub-tiles are in flight
-    // while it computes.  In that order the last of K(i) and V(i) is
-    // followed by the loads of the next min(KA - 1, r) K and min(VA - 1, r)
-    // V sub-tiles (r = sub-tiles after i), so waiting until only those are
-    // outstanding (in-order counter) means K(i) and V(i) are in LDS.  Only
-    // this wave reads its slots, so no barrier.  The loop is unrolled over
-    // KA VA steps so every LDS offset is fixed.
+    // The wave's stream.  K rows of sub-tile j go into K slot j % KA, V rows
+    // into V slot j % VA, straight from global memory with loads the
+    // compiler does not track.  Software pipeline: step i computes the
+    // weights of sub-tile i (scores from step i - 1) while the matrix cores
+    // run the score products of sub-tile i + 1, then the PV product of i.
+    // So step i reads K(i + 1) and V(i), and refills their slots with
+    // K(i + 1 + KA) and V(i + VA) once the reads have returned.  Issue order:
+    // K(0) V(0) K(1) V(1) V(2), then K(2) when K(0) has been read, then
+    // K(i + 3) V(i + 3) in step i.  So in step i >= 2 the last of K(i + 1)
+    // and V(i) is followed by V(i + 1), K(i + 2) and V(i + 2) (those that
+    // exist), in step 1 by K(3) and V(3), and in step 0 only K(2) can be in
+    // flight (the prologue waited for the rest); waiting until only those
+    // are outstanding (in-order counter) means K(i + 1) and V(i) are in LDS.
+    // Only this wave reads its slots, so no barrier.  The loop is unrolled
+    // over KA VA steps so every LDS offset is fixed.
     constexpr int KA = C::KSLOT, VA = NSLOT, UNR = KA * VA;
-    static_assert(KA == 2 && VA == 3, "wait cases");
+    static_assert(KA == 2 && VA == 3, "issue order and waits");
     uint16_t* const myring = ring[wave][0];
     uint16_t* const mykring = kring[wave][0];
+    auto kslot = [&](int j) __attribute__((always_inline)) { return mykring + (j % KA) * 32 * D; };
+    auto vslot = [&](int j) __attribute__((always_inline)) { return myring + (j % VA) * 32 * D; };
 #pragma unroll
     for (int s0 = 0; s0 < VA; ++s0) {
-      if (s0 < KA && s0 < n_mine) issue_rows(krs, s0, mykring + s0 * 32 * D);
-      if (s0 < n_mine) issue_rows(vrs, s0, myring + s0 * 32 * D);
+      if (s0 < KA && s0 < n_mine) issue_rows(krs, s0, kslot(s0));
+      if (s0 < n_mine) issue_rows(vrs, s0, vslot(s0));
     }
-    // Read sub-tile i's fragments, then refill its slots once the reads have
-    // returned (lgkmcnt(0)), then compute.
-    auto step_tail = [&](int i, uint16_t* __restrict__ kt, uint16_t* __restrict__ vt) __attribute__((always_inline)) {
-      uint4 kfr[DS], vfr[2 * DB];
-      read_frags(kt, vt, kfr, vfr);
-      lds_fence();
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt free
-      if (i + KA < n_mine) issue_rows(krs, i + KA, kt);
-      if (i + VA < n_mine) issue_rows(vrs, i + VA, vt);
-      sub_block(kfr, vfr, k0 + 32 * (wave + NW * i));
-    };
-    // Step 0 waits for everything in flight (the first sub-tiles and the
-    // query fragments): the compiler tracks the query loads but not the
-    // tile loads behind them, so a wait it placed for the fragments would
-    // hold a later step until every tile load issued so far had arrived.
-    // After this wait it has no load to wait for.
+    // Prologue: wait for everything in flight (the first sub-tiles and the
+    // query fragments: the compiler tracks the query loads but not the tile
+    // loads behind them, so a wait it placed for the fragments would hold a
+    // later step until every tile load issued so far had arrived; after this
+    // wait it has none to place), the scores of sub-tile 0, the reference.
     if (n_mine > 0) {
       vm_wait<0>();
-      lds_fence();
-      step_tail(0, mykring, myring);
+      uint4 kfr[DS];
+      read_k(kslot(0), kfr);
+      reads_done();
+      if (KA < n_mine) issue_rows(krs, KA, kslot(0));
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int k = 0; k < DS; k += 2) {
+        s0 = mma16(T{}, kfr[k], qf[k], s0);
+        s1 = mma16(T{}, kfr[k + 1], qf[k + 1], s1);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scur[r] = s0[r] + s1[r];
+      m_run = row_max(k0 + 32 * wave);
     }
-    for (int i0 = 0; i0 < n_mine; i0 += UNR) {
+    // Step i < n_mine - 1 (a next sub-tile exists; sub-tile i has no key
+    // past k1).  kt: K slot of i + 1, vt: V slot of i.
+    auto step = [&](int i, uint16_t* __restrict__ kt, uint16_t* __restrict__ vt) __attribute__((always_inline)) {
+      const int key0 = k0 + 32 * (wave + NW * i);
+      uint4 kfr[DS];
+      read_k(kt, kfr);
+      reads_done();
+      if (i + 1 + KA < n_mine) issue_rows(krs, i + 1 + KA, kt);
+      // scores of i + 1 on the matrix cores, weights of i beside them: one
+      // product, then two weights
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      float x[16], psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < DS; ++k) {
+        if (k % 2 == 0) s0 = mma16(T{}, kfr[k], qf[k], s0);
+        else s1 = mma16(T{}, kfr[k], qf[k], s1);
+#pragma unroll
+        for (int e = 0; e < 16 / DS; ++e) {
+          const int r = k * (16 / DS) + e;
+          x[r] = fast_exp2(__builtin_fmaf(scur[r], qk_scale, -m_run));
+          psum += x[r];
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      uint4 vfr[2 * DB];
+      read_v(vt, vfr);
+      finish(key0, x, psum, vfr);
+      reads_done();
+      if (i + VA < n_mine) issue_rows(vrs, i + VA, vt);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scur[r] = s0[r] + s1[r];
+    };
+    // The last step: weights (possibly masked) of the last sub-tile and its
+    // PV product, no next scores.
+    auto last_step = [&](int i) __attribute__((always_inline)) {
+      const int key0 = k0 + 32 * (wave + NW * i);
+      uint4 vfr[2 * DB];
+      read_v(vslot(i), vfr);
+      float x[16], psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = weight(key0, r);
+        psum += x[r];
+      }
+      finish(key0, x, psum, vfr);
+    };
+    for (int i0 = 0; i0 < n_mine - 1; i0 += UNR) {
 #pragma unroll
       for (int jj = 0; jj < UNR; ++jj) {
         const int i = i0 + jj;
-        if (i >= 1 && i < n_mine) {
-          const int r = n_mine - 1 - i;
-          if (r >= 2) vm_wait<(KA - 1 + VA - 1) * C::VL>();
-          else if (r == 1) vm_wait<2 * C::VL>();
+        if (i < n_mine - 1) {
+          // loads issued after the last of K(i + 1) and V(i), see above
+          const int later = i == 0 ? 1 : (i == 1 ? (3 < n_mine ? 2 : 0) : 1 + (i + 2 < n_mine ? 2 : 0));
+          if (later == 3) vm_wait<3 * C::VL>();
+          else if (later == 2) vm_wait<2 * C::VL>();
+          else if (later == 1) vm_wait<C::VL>();
           else vm_wait<0>();
           lds_fence();
-          step_tail(i, mykring + (jj % KA) * 32 * D, myring + (jj % VA) * 32 * D);
+          step(i, kslot(jj + 1), vslot(jj));
         }
       }
+    }
+    if (n_mine > 0) {
+      vm_wait<0>();
+      lds_fence();
+      last_step(n_mine - 1);
     }
 
     // Combine the waves through LDS (the rings are free after this barrier:
