@@ -24,11 +24,13 @@
 // Split kernel, one workgroup per range, walking its range unit by unit:
 //   * a unit's piece is cut into 32-key sub-tiles and wave w takes sub-tiles
 //     w, w + NW, w + 2 NW, ...: every wave streams its own keys, with no
-//     workgroup barrier, and keeps NSLOT - 1 sub-tiles in flight -- K
-//     fragments straight into registers (the A operand of S^T = K Q^T), V
-//     straight into the wave's own NSLOT-slot LDS ring (buffer_load ... lds,
-//     rows swizzled as in the forward) -- so each CU has many loads
-//     outstanding, which a bandwidth-bound stream needs;
+//     workgroup barrier, K and V rows straight into the wave's own LDS rings
+//     (buffer_load ... lds, rows swizzled as in the forward), several
+//     sub-tiles ahead, so each CU has many loads outstanding, which a
+//     bandwidth-bound stream needs;
+//   * per step a wave runs the score products of its next sub-tile on the
+//     matrix cores while its vector units form the current sub-tile's
+//     weights, then the current PV product;
 //   * the buffer range of the head ends at its valid length, so keys past it
 //     read as zeros (never a stale or non-finite cache entry) and are masked;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (lane = query head, registers =
