@@ -88,28 +88,34 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Sums of tiles over all batches (T) and over batches < blim (P), computed
-// by each wave on its own: no LDS and no barrier, so the first loads of a
-// workgroup wait only for the lengths.  Wave-uniform.
+// Sums of tiles over all batches (T) and over batches < blim (P), and the
+// tiles of batch blim itself (nb), computed by each wave on its own from one
+// pass over the lengths: no LDS and no barrier, and no second, dependent
+// read of a length.  Wave-uniform.
 __device__ __forceinline__ void decode_wave_sums(const int* kv_lens, int B, int Nkv, int UB, int blim, int* T_out,
-                                                 int* P_out) {
+                                                 int* P_out, int* nb_out) {
   const int lane = threadIdx.x & 63;
-  int sT = 0, sP = 0;
-  for (int b = lane; b < B; b += 64) {
-    const int v = decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
-    sT += v;
-    sP += b < blim ? v : 0;
+  int sT = 0, sP = 0, nb = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int b = c0 + lane;
+    const int t = b < B ? decode_tiles(decode_len(kv_lens, b, Nkv)) : 0;
+    sT += t * UB;
+    sP += b < blim ? t * UB : 0;
+    if (blim >= c0 && blim < c0 + 64) nb = __builtin_amdgcn_readlane(t, blim - c0);
   }
   *T_out = __builtin_amdgcn_readfirstlane(wave_total(sT));
   *P_out = __builtin_amdgcn_readfirstlane(wave_total(sP));
+  *nb_out = nb;
 }
 
 // The partition, computed by each wave on its own: the total tile count T,
 // the tiles per part, and the batch b holding tile part * per with the
-// first tile P_b of that batch (b = B, P_b = T when the part is empty).
+// first tile P_b of that batch and its own tile count (b = B, P_b = T when
+// the part is empty).
 // Batches go 64 at a time through a wave-wide prefix sum.  Wave-uniform.
 __device__ __forceinline__ void decode_wave_plan(const int* kv_lens, int B, int Nkv, int UB, int parts_total,
-                                                 int part, int* T_out, int* per_out, int* b_out, int* Pb_out) {
+                                                 int part, int* T_out, int* per_out, int* b_out, int* Pb_out,
+                                                 int* nb_out) {
   const int lane = threadIdx.x & 63;
   int sum = 0;
   for (int b = lane; b < B; b += 64) sum += decode_tiles(decode_len(kv_lens, b, Nkv)) * UB;
@@ -120,6 +126,7 @@ __device__ __forceinline__ void decode_wave_plan(const int* kv_lens, int B, int 
   *per_out = per;
   *b_out = B;
   *Pb_out = T;
+  *nb_out = 0;
   if (target >= T) return;
   int base = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
@@ -131,6 +138,7 @@ __device__ __forceinline__ void decode_wave_plan(const int* kv_lens, int B, int 
       const int src = __builtin_ctzll(hit);
       *b_out = c0 + src;
       *Pb_out = __builtin_amdgcn_readlane(incl - v, src);
+      *nb_out = __builtin_amdgcn_readlane(v, src) / UB;
       return;
     }
     base = __builtin_amdgcn_readlane(incl, 63);
@@ -171,14 +179,14 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
   // This part's tile range; consecutive parts share an XCD (and its L2),
   // which the query blocks of one K/V head read in turn.
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  int Ttot, per, b, P_b;
-  decode_wave_plan(kv_lens, B, Nkv, UB, (int)gridDim.x, w, &Ttot, &per, &b, &P_b);
+  int Ttot, per, b, P_b, nb;
+  decode_wave_plan(kv_lens, B, Nkv, UB, (int)gridDim.x, w, &Ttot, &per, &b, &P_b, &nb);
   int t = w * per;
   const int t_end = min(t + per, Ttot);
   if (t >= t_end) return;
 
-  // The unit holding tile t: batch b (first tile P_b), unit ui of the batch.
-  int nb = decode_tiles(decode_len(kv_lens, b, Nkv));
+  // The unit holding tile t: batch b (first tile P_b, nb tiles per unit),
+  // unit ui of the batch.
   int ui = (t - P_b) / nb;
   int P_u = P_b + ui * nb;
 
@@ -545,15 +553,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   const int u = blockIdx.x / CPU, col = blockIdx.x % CPU;
   const int b = u / UB, ui = u % UB, qb = ui % QB;
   if (col >= min(32, G - 32 * qb)) return;  // (block-uniform returns throughout)
-  const int nb = decode_tiles(decode_len(kv_lens, b, Nkv));
-  if (nb == 0) return;
-  int Ttot, P_b;
+  int Ttot, P_b, nb;
   if (kv_lens == nullptr) {
+    nb = decode_tiles(Nkv);
     Ttot = B * UB * nb;
     P_b = b * UB * nb;
   } else {
-    decode_wave_sums(kv_lens, B, Nkv, UB, b, &Ttot, &P_b);
+    decode_wave_sums(kv_lens, B, Nkv, UB, b, &Ttot, &P_b, &nb);
   }
+  if (nb == 0) return;
   const int per = (Ttot + n_parts - 1) / n_parts;
   const int P_u = P_b + ui * nb;
   const int w_first = P_u / per, w_last = (P_u + nb - 1) / per;
