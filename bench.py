@@ -291,6 +291,11 @@ def main():
                          "workload (twice each, after the calibration copy), for counter passes")
     ap.add_argument("--traffic-legs-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_naive_vs_fused.md from the counter passes of --traffic-legs")
+    ap.add_argument("--decode-traffic", action="store_true",
+                    help="run only the two decode workloads (twice each, after the calibration copy), for "
+                         "counter passes")
+    ap.add_argument("--decode-traffic-write", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_decode.md from the counter passes of --decode-traffic")
     ap.add_argument("--stats", metavar="KERNEL_TRACE_CSV",
                     help="write profiles/kernel_stats_<workload>.md from a rocprofv3 kernel trace of the "
                          "default training-step run (--legs 0 --cpu-baseline 0) and exit")
@@ -309,6 +314,9 @@ def main():
     args = ap.parse_args()
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.calib_copy_mib)
+        return
+    if args.decode_traffic_write:
+        write_decode_traffic(args.decode_traffic_write[0], args.decode_traffic_write[1], args.calib_copy_mib)
         return
     if args.traffic_legs_write:
         write_traffic_legs(args.traffic_legs_write[0], args.traffic_legs_write[1], args.calib_copy_mib)
@@ -340,6 +348,9 @@ def main():
     fa._lib.load()
     dev = torch.device("cuda:0")
     digest = source_digest()
+    if args.decode_traffic:
+        run_decode_traffic(torch, fa, fa_synth, dev, args.calib_copy_mib)
+        return
     if args.traffic_legs:
         run_traffic_legs(torch, fa, fa_synth, dev, args.calib_copy_mib)
         return
@@ -1096,6 +1107,106 @@ def write_traffic_legs(fetch_csv: str, write_csv: str, calib_mib: int):
     print(f"wrote {path}")
 
 
+def decode_traffic_workloads():
+    import fa_synth
+    return (fa_synth.GQA_DECODE, fa_synth.GQA_DECODE_RAGGED)
+
+
+def decode_inputs(torch, fa, fa_synth, w, dev):
+    q, k, v, lens = (t.to(dev) for t in fa_synth.make_decode_inputs(
+        w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, ragged="ragged" in w.name))
+    parts = fa.decode_plan(w.B, w.H, w.kv_heads, w.N, w.d)
+    ws = torch.empty(max(1, fa.decode_workspace_bytes(w.B, w.H, w.kv_heads, w.d, parts)), dtype=torch.uint8,
+                     device=dev)
+    return q, k, v, lens, parts, ws
+
+
+def decode_alg_bytes(w, lens_sum: float) -> float:
+    """K and V read once over the valid lengths, q read, O (16-bit) and the
+    fp32 LSE written."""
+    return lens_sum * w.kv_heads * w.d * 2 * 2 + 2 * w.B * w.H * w.d * 2 + 4 * w.B * w.H
+
+
+def run_decode_traffic(torch, fa, fa_synth, dev, calib_mib: int):
+    """Calibration copy, then each decode workload twice (split and merge
+    kernels), in this fixed order."""
+    if calib_mib <= 0:
+        sys.exit("--decode-traffic needs --calib-copy-mib")
+    src = torch.ones(calib_mib * (1 << 18), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    for w in decode_traffic_workloads():
+        q, k, v, lens, parts, ws = decode_inputs(torch, fa, fa_synth, w, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            fa.decode(q, k, v, w.scale, kv_lens=lens, n_parts=parts, out=o, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        log(f"[bench] decode traffic: {w.name} done")
+        del q, k, v, lens, ws, o, lse
+        torch.cuda.empty_cache()
+
+
+def write_decode_traffic(fetch_csv: str, write_csv: str, calib_mib: int):
+    import fa_synth
+    import torch
+    if calib_mib <= 0:
+        sys.exit("--decode-traffic-write needs the --calib-copy-mib the counter runs used")
+    ws = decode_traffic_workloads()
+    rows = {w.name: {"w": w} for w in ws}
+    scales = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = _counter_dispatches(path, counter)
+        calib = [v for _, n, v in ds if "elementwise" in n and "add" in n]
+        if not calib:
+            sys.exit(f"{path}: no calibration copy")
+        scale = calib_mib * 1024.0 / (sum(calib) / len(calib))
+        scales[counter] = scale
+        seq = [(n, v * scale * 1024.0) for _, n, v in ds if "decode_" in n]
+        per = 4  # two calls of split + merge
+        if len(seq) != per * len(ws):
+            sys.exit(f"{path}: {len(seq)} decode dispatches, expected {per * len(ws)}")
+        for wi, w in enumerate(ws):
+            part = seq[wi * per:(wi + 1) * per]
+            for j, (n, _) in enumerate(part):
+                assert ("decode_split" if j % 2 == 0 else "decode_merge") in n, (n, j)
+            rows[w.name][counter] = {"split": (part[0][1] + part[2][1]) / 2, "merge": (part[1][1] + part[3][1]) / 2}
+    digest = digest_of(("fa_decode.hip", "fa_device.hpp", "fa_plan.hpp"))
+    path = os.path.join(PROFILES, "traffic_decode.md")
+    with open(path, "w") as f:
+        f.write("# HBM-side bytes of a decode step (split and merge kernels)\n\n")
+        f.write("Command (repo root on the MI355X box, `TMPDIR=/tmp`), two counter passes of their own:\n\n```\n")
+        for c, d in (("FETCH_SIZE", "dt_fetch"), ("WRITE_SIZE", "dt_write")):
+            f.write(f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/{d} -o run -- \\\n"
+                    f"    python3 bench.py --decode-traffic --calib-copy-mib {calib_mib}\n")
+        f.write(f"python3 bench.py --decode-traffic-write gpurun_out/dt_fetch/run_counter_collection.csv "
+                f"gpurun_out/dt_write/run_counter_collection.csv --calib-copy-mib {calib_mib}\n```\n\n")
+        f.write("Bytes past L2 (HBM or the memory-side cache) per call: FETCH_SIZE and WRITE_SIZE (KiB per "
+                "dispatch) scaled by what the same counters read for an elementwise copy of "
+                f"{calib_mib} MiB in and {calib_mib} MiB out (read scale {scales['FETCH_SIZE']:.3f}, write scale "
+                f"{scales['WRITE_SIZE']:.3f}), averaged over two calls. Algorithmic bytes: K and V read once over "
+                "the valid lengths, q read, O and the LSE written.\n\n")
+        f.write("| workload | split read (MB) | split write (MB) | merge read (MB) | merge write (MB) | "
+                "total (MB) | algorithmic (MB) | total / algorithmic |\n|---|---|---|---|---|---|---|---|\n")
+        machine = []
+        for name, r in rows.items():
+            w = r["w"]
+            lens = fa_synth.make_decode_inputs(w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed,
+                                               ragged="ragged" in w.name)[3]
+            alg = decode_alg_bytes(w, float(lens.sum().item()))
+            fe, wr = r["FETCH_SIZE"], r["WRITE_SIZE"]
+            tot = fe["split"] + wr["split"] + fe["merge"] + wr["merge"]
+            f.write(f"| `{name}` | {fe['split'] / 1e6:.1f} | {wr['split'] / 1e6:.2f} | {fe['merge'] / 1e6:.2f} | "
+                    f"{wr['merge'] / 1e6:.3f} | {tot / 1e6:.1f} | {alg / 1e6:.1f} | {tot / alg:.3f} |\n")
+            machine.append(f"{name}.counter_bytes = {tot:.0f}")
+        f.write("\n```\n" + "\n".join(machine) + f"\nsource_digest = {digest}\n```\n")
+    print(f"wrote {path}")
+
+
 def read_traffic_legs(digest: str):
     path = os.path.join(PROFILES, "traffic_naive_vs_fused.md")
     if not os.path.exists(path):
@@ -1199,19 +1310,14 @@ def run_legs(torch, fa, fa_synth, dev):
 
     # decode steps (one query per head against a K/V cache): HBM-bound, so
     # reported as K/V bytes read per second against the HBM peak
-    for w in (fa_synth.GQA_DECODE, fa_synth.GQA_DECODE_RAGGED):
-        q, k, v, lens = (t.to(dev) for t in fa_synth.make_decode_inputs(
-            w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, ragged="ragged" in w.name))
-        parts = fa.decode_plan(w.B, w.H, w.kv_heads, w.N, w.d)
-        ws = torch.empty(max(1, fa.decode_workspace_bytes(w.B, w.H, w.kv_heads, w.d, parts)), dtype=torch.uint8,
-                         device=dev)
+    for w in decode_traffic_workloads():
+        q, k, v, lens, parts, ws = decode_inputs(torch, fa, fa_synth, w, dev)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
         fn = lambda: fa.decode(q, k, v, w.scale, kv_lens=lens, n_parts=parts, out=o, lse=lse, ws=ws)
         ms_eager, _ = time_reps(fn, 30, torch)
         ms, calls = time_graph(fn, torch, ms_eager)  # a decode step is short: host launch cost excluded
-        kv_bytes = float(lens.sum().item()) * w.kv_heads * w.d * 2 * 2
-        alg = kv_bytes + 2 * w.B * w.H * w.d * 2 + 4 * w.B * w.H  # + q read, o written, lse written
+        alg = decode_alg_bytes(w, float(lens.sum().item()))
         gbs = alg / (ms * 1e-3) / 1e9
         entry = {"decode_us": ms * 1e3, "decode_us_eager_call": ms_eager * 1e3, "graph_calls": calls,
                  "parts": parts, "alg_bytes": alg, "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
