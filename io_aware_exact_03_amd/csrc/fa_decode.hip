@@ -338,8 +338,10 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     // compiler does not track.  Software pipeline: step i computes the
     // weights of sub-tile i (scores from step i - 1) while the matrix cores
     // run the score products of sub-tile i + 1, then the PV product of i.
-    // So step i reads K(i + 1) and V(i), and refills their slots with
-    // K(i + 1 + KA) and V(i + VA) once the reads have returned.  Issue order:
+    // So step i reads K(i + 1) and refills its slot with K(i + 1 + KA) once
+    // the read has returned, and reads V(i) just before the PV product (to
+    // keep its registers free meanwhile) and refills that slot with
+    // V(i + VA) after it.  Issue order:
     // K(0) V(0) K(1) V(1) V(2), then K(2) when K(0) has been read, then
     // K(i + 3) V(i + 3) in step i.  So in step i >= 2 the last of K(i + 1)
     // and V(i) is followed by V(i + 1), K(i + 2) and V(i + 2) (those that
