@@ -60,7 +60,7 @@ struct Dec {
   static constexpr int VL = 32 / RPP;           // 1 KB loads per 32-key K or V sub-tile
   static constexpr int KSLOT = NSLOT - 1;       // K ring slots (K runs one fewer sub-tile ahead)
   static constexpr int EPT = D / (2 * NW);      // output elements per thread in the combine
-  static constexpr int OROW = D + 1;            // padded fp32 row of a wave's O in LDS
+  static constexpr int OROW = D + 4;            // padded fp32 row of a wave's O in LDS (16-byte rows)
   static_assert((NSLOT + KSLOT) * NW * 32 * D * 2 <= 160 * 1024, "rings fit in LDS");
   static_assert(EPT % 8 == 0, "combine vector width");
   static_assert(NW * 32 * (OROW + 2) * 4 <= NW * NSLOT * 32 * D * 2, "combine fits in the ring");
@@ -463,11 +463,13 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
       mrow[wave * 32 + n] = m_run;
       lrow[wave * 32 + n] = l_tot;
     }
+    // registers 4 j .. 4 j + 3 of a d block are four consecutive elements
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        orow[(wave * 32 + n) * C::OROW + 32 * db + 8 * (r / 4) + 4 * g + (r % 4)] = oacc[db][r];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(orow + (wave * 32 + n) * C::OROW + 32 * db + 8 * j + 4 * g) =
+            make_float4(oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]);
     __syncthreads();
 
     const int col = threadIdx.x % 32, e0 = (threadIdx.x / 32) * C::EPT;
@@ -491,7 +493,13 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
       for (int ww = 0; ww < NW; ++ww) {
         const float* src = orow + (ww * 32 + col) * C::OROW + e0;
 #pragma unroll
-        for (int e = 0; e < C::EPT; ++e) o[e] += ew[ww] * src[e];
+        for (int e = 0; e < C::EPT; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src + e);
+          o[e] += ew[ww] * x.x;
+          o[e + 1] += ew[ww] * x.y;
+          o[e + 2] += ew[ww] * x.z;
+          o[e + 3] += ew[ww] * x.w;
+        }
       }
       const float lse = (M + __log2f(Lsum)) * kLn2;
       if (whole) {  // the final result of these query heads
