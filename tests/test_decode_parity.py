@@ -143,6 +143,17 @@ def test_lengths_edge_cases(n_parts):
     assert bool((o[0] == 0).all()) and bool((o[6] == 0).all())
 
 
+@pytest.mark.parametrize("n_parts", [1, 5])
+def test_no_valid_key_anywhere(n_parts):
+    """Every length 0 (or negative): no part has work, the first workgroup
+    writes O = 0 and LSE = -inf for every head."""
+    lens = torch.tensor([0, -3, 0], dtype=torch.int32)
+    res = _run(3, 8, 2, 256, 128, "bf16", 9980, n_parts, lens=lens)
+    o, lse = res[5], res[6]
+    assert bool((o == 0).all())
+    assert bool(torch.isneginf(lse).all())
+
+
 @pytest.mark.parametrize("n_parts", [1, 7, 200])
 def test_many_batches(n_parts):
     """More batches than a wave has lanes: the workgroups locate their
