@@ -165,6 +165,11 @@ __device__ __forceinline__ void load_lds4(rsrc_t r, void* dst, uint32_t byte_off
 // and the caller waits explicitly (vm_wait, then lds_fence) before it reads
 // the destination.  lds_dst is the wave-uniform LDS byte address (through
 // M0); the load has no result registers.  Counted in vmcnt like any load.
+// The asm sets M0 itself and declares it clobbered; the compiler does not
+// preserve M0 around it (it warns so), which is safe only while the kernel
+// keeps no value of its own in M0 across these loads: the kernels that use
+// this form issue no compiler-tracked load into LDS and no indexed register
+// access (their assembly shows no other M0 use).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t)(const_cast<void*>(p));
 }
